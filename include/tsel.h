@@ -1,0 +1,200 @@
+/*
+ * tsel.h -- C ABI of libtsel.so: batched token selection over the logits of
+ * one decode step, and greedy verification of assistant drafts, on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" point to GPU memory; everything else is host.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously on it; results are valid after the
+ *    caller synchronizes the stream.
+ *  - The caller allocates and frees every buffer (logits, history, masks,
+ *    outputs, workspace).  The library keeps no allocation and no mutable
+ *    global state between calls, so independent calls may run concurrently
+ *    on different streams.  (The pages' generation loop likewise frees only
+ *    the tensors it made and never the caller's: "Transmuter.Generation",
+ *    section "Device memory".)
+ *  - Return value: TSEL_OK, or a negative tsel_status that is decided on the
+ *    host before anything is enqueued (invalid or unsupported arguments), or
+ *    TSEL_ERR_LAUNCH when the runtime refuses a launch.  Faults inside a
+ *    kernel surface at the caller's stream synchronization.  No entry point
+ *    prints, throws or exits.
+ *  - Inputs and outputs must not alias.
+ */
+#ifndef TSEL_H
+#define TSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tsel_status;
+#define TSEL_OK 0
+#define TSEL_ERR_INVALID_ARG (-1)  /* an argument is out of its documented range */
+#define TSEL_ERR_UNSUPPORTED (-2)  /* valid, but outside what this build handles */
+#define TSEL_ERR_LAUNCH (-3)       /* the HIP runtime refused a launch */
+#define TSEL_ERR_WORKSPACE (-4)    /* workspace missing or too small */
+
+/* Element type of the logits. */
+#define TSEL_F32 0
+#define TSEL_BF16 1
+
+/* Initial number of draft tokens of assisted generation ("Assisted
+ * Generation: a new direction toward low-latency text generation", section
+ * "Greedy decoding with assisted generation", step 1). */
+#define TSEL_INITIAL_K 5
+
+/* Largest number of eos ids a call carries. */
+#define TSEL_MAX_EOS 8
+
+/*
+ * Generation settings of one call, named as in generation_config.json.  Read
+ * on the host at call time (the struct may be reused or freed after the call
+ * returns).  Section references are to "Transmuter.Generation (transmuter
+ * v2.0.0)": the module doc fixes the processor order, "Lengths" the length
+ * rules, "Processors" the static masks.
+ */
+typedef struct tsel_params {
+  int32_t batch;                /* B >= 0 rows; B == 0 is a no-op */
+  int32_t vocab;                /* V >= 1 */
+  int64_t logits_row_stride;    /* elements between consecutive logits rows */
+  int32_t dtype;                /* TSEL_F32 or TSEL_BF16 */
+  int32_t hist_stride;          /* int32 elements between history rows, >= every len */
+
+  float repetition_penalty;     /* > 0; 1 = off.  Seen id: score < 0 -> score * p,
+                                   else score / p (module doc, first processor) */
+  int32_t no_repeat_ngram_size; /* >= 0; 0 = off ("Lengths") */
+  const uint32_t *bad_words_mask;      /* device bitmask of single-token bad words, or NULL */
+  const uint32_t *suppress_mask;       /* device bitmask of suppress_tokens, or NULL */
+  const uint32_t *begin_suppress_mask; /* device bitmask of begin_suppress_tokens, or NULL */
+  int32_t min_length;           /* >= 0; 0 = off */
+  int32_t min_new_tokens;       /* >= 0; 0 = off; when > 0 it replaces min_length */
+  int32_t n_eos;                /* 0 .. TSEL_MAX_EOS */
+  int32_t eos_ids[TSEL_MAX_EOS];/* the eos set removed by min_length / min_new_tokens */
+  int32_t forced_bos_token_id;  /* < 0 = off */
+  int32_t forced_eos_token_id;  /* < 0 = off */
+
+  int32_t do_sample;            /* 0 = greedy argmax (the warpers below are ignored) */
+  float temperature;            /* > 0 when sampling; 1 = off */
+  int32_t top_k;                /* >= 0; 0 = off */
+  float top_p;                  /* in (0, 1]; 1 = off */
+} tsel_params;
+
+/*
+ * tsel_process_select -- one decode step of token selection for B rows.
+ *
+ * Applies, per row and in this order, the processors of "Transmuter.
+ * Generation" (module doc; "Lengths"): repetition_penalty,
+ * no_repeat_ngram_size, single-token bad words, min_length /
+ * min_new_tokens, forced_bos_token_id, forced_eos_token_id, suppress_tokens,
+ * begin_suppress_tokens; then, when sampling, temperature, top_k and top_p;
+ * then selects the token: the argmax (lowest id among equal scores) when
+ * greedy, else the inverse CDF of uniforms[b] over the kept ids taken in
+ * (score descending, id ascending) order.  Removed ids score -inf; a forced
+ * id scores 0; the penalty acts once per distinct history id; a row whose
+ * every id is removed selects id 0.
+ *
+ *  logits      device, B rows of V elements of params->dtype, row b at
+ *              logits + b * logits_row_stride.  The start of every row must be
+ *              16-byte aligned (so logits_row_stride * element size must be a
+ *              multiple of 16).  Not modified.
+ *  history     device int32 [B, hist_stride]: the prompt then the new tokens
+ *              of each row, oldest first; row b uses its first lens[b] ids.
+ *              Ids outside [0, V) are ignored by every processor.
+ *  lens        device int32 [3 * B]: lens[b] = prompt + new tokens (0 marks a
+ *              padding row: token -1, nothing else computed);
+ *              lens[B + b] = prompt length; lens[2B + b] = max_length
+ *              (prompt length + max_new_tokens).  ("Lengths"; "Batches")
+ *  uniforms    device float [B] in [0, 1), one per row; required iff sampling.
+ *  out_tokens  device int32 [B]: the selected id, or -1 for a padding row.
+ *  out_processed  device float [B, V] or NULL: the final scores the token is
+ *              chosen from (after top_p when sampling).  A debugging and
+ *              parity aid: it costs one extra pass over each row.
+ *  workspace, workspace_bytes  device scratch of at least
+ *              tsel_process_select_workspace_size(params) bytes (NULL/0 when
+ *              that is 0).
+ *
+ * Errors: TSEL_ERR_INVALID_ARG for B < 0, V < 1, a stride below V, a
+ * hist_stride below 0, penalty <= 0, n < 0, min lengths < 0, n_eos outside
+ * [0, TSEL_MAX_EOS], an unknown dtype, temperature <= 0 / top_k < 0 / top_p
+ * outside (0, 1] when sampling, or a NULL required pointer;
+ * TSEL_ERR_UNSUPPORTED for a misaligned row layout or a vocabulary too large
+ * for the on-chip masks (V > 524,288).
+ */
+tsel_status tsel_process_select(const void *logits, const int32_t *history,
+                                const int32_t *lens, const tsel_params *params,
+                                const float *uniforms, int32_t *out_tokens,
+                                float *out_processed, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Workspace bytes tsel_process_select needs for these params (0 if none). */
+size_t tsel_process_select_workspace_size(const tsel_params *params);
+
+/*
+ * tsel_validate_params -- the host-side argument checks of
+ * tsel_process_select on the params alone (no pointers are dereferenced and
+ * no GPU call is made).  Returns what tsel_process_select would return for
+ * them.
+ */
+tsel_status tsel_validate_params(const tsel_params *params, int32_t sampling_uniforms_given);
+
+/*
+ * tsel_mask_build -- the static mask of a list of single token ids ("the
+ * bad words of one token" and suppress_tokens, made once per group of rows:
+ * "Transmuter.Generation", section "Processors").
+ *
+ *  ids       device int32 [n_ids]; ids outside [0, vocab) are ignored.
+ *  out_mask  device uint32 [ceil(vocab / 32)]: bit (v % 32) of word v / 32
+ *            is set iff v is listed.  Fully overwritten.
+ * Errors: TSEL_ERR_INVALID_ARG for vocab < 1, n_ids < 0, NULL out_mask, or
+ * NULL ids with n_ids > 0.
+ */
+tsel_status tsel_mask_build(int32_t vocab, const int32_t *ids, int32_t n_ids,
+                            uint32_t *out_mask, void *stream);
+
+/*
+ * tsel_verify -- greedy verification of k assistant drafts per row
+ * ("Assisted Generation: a new direction toward low-latency text
+ * generation", section "Greedy decoding with assisted generation", steps
+ * 3-6).  For row b and position j = 0..k, next[j] is the argmax of the raw
+ * logits at that position (lowest id among equal maxima).  n_match is the
+ * length of the common prefix of candidates[b] and next (comparison stops at
+ * the first mismatch); the kept tokens are next[0..n_match] (the matches and
+ * the first divergent token, or the extra token when all k match); the next
+ * draft count is k + 2 when all k match, else max(1, k - 1).
+ *
+ *  logits       device [B, k+1, V] of dtype, position (b, j) at
+ *               logits + (b * (k+1) + j) * row_stride; 16-byte aligned rows.
+ *  candidates   device int32 [B, k] (may be NULL when k == 0).
+ *  out_n_match  device int32 [B]
+ *  out_tokens   device int32 [B, k+1]: kept tokens, then -1.
+ *  out_next     device int32 [B]: next[n_match].
+ *  out_k        device int32 [B]: the next draft count.
+ *  workspace    device, >= tsel_verify_workspace_size(B, k, V) bytes.  It
+ *               must hold zeros before its first use (e.g. hipMemset once
+ *               after allocation); every call leaves it that way again.
+ * Errors: TSEL_ERR_INVALID_ARG for B < 0, k < 0, V < 1, a stride below V,
+ * an unknown dtype, or NULL required pointers; TSEL_ERR_WORKSPACE when the
+ * workspace is missing or too small; TSEL_ERR_UNSUPPORTED for misaligned
+ * rows, k > 1023 or B * (k+1) > 65535.
+ */
+tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_t k,
+                        int32_t vocab, int64_t row_stride, const int32_t *candidates,
+                        int32_t *out_n_match, int32_t *out_tokens, int32_t *out_next,
+                        int32_t *out_k, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Workspace bytes tsel_verify needs. */
+size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab);
+
+/* Static text for a status code. */
+const char *tsel_status_string(tsel_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSEL_H */

@@ -1,0 +1,136 @@
+// k_verify.hip -- greedy verification of assistant drafts over the
+// [B, k+1, V] logits of the main model ("Assisted Generation: a new direction
+// toward low-latency text generation", section "Greedy decoding with assisted
+// generation", steps 3-6).
+//
+// Every (position row, vocabulary chunk) pair is one workgroup of 256
+// threads that streams its chunk once (16 bytes per lane per load) and
+// reduces a (score, id) argmax; the partial maxima go to the workspace.  The
+// last workgroup to finish a batch row (an atomic counter per row) merges the
+// partials of its k+1 positions, counts the left-to-right matches, writes the
+// kept tokens and the next draft count, and clears the counter for the next
+// call.  Chunks keep the grid well above the 256 compute units even when
+// B * (k+1) is small.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tsel_device.hpp"
+#include "tsel_internal.hpp"
+
+namespace tsel {
+
+constexpr int VT = 256;   // threads per workgroup
+constexpr int VCH = 8;    // 16-byte chunks per lane per workgroup
+
+template <int DT>
+__global__ __launch_bounds__(VT) void k_verify(const char *logits, int64_t row_bytes, int V,
+                                               int k, int S, const int32_t *cand,
+                                               int32_t *n_match, int32_t *tokens, int32_t *next,
+                                               int32_t *k_out, uint64_t *partials,
+                                               uint32_t *counters) {
+  constexpr int EPC = DT == 1 ? 8 : 4;
+  constexpr int CHUNK = VT * VCH * EPC;  // elements per workgroup
+  __shared__ uint64_t red[VT / kWave];
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int s = blockIdx.x;       // chunk of the row
+  const int r = blockIdx.y;       // position row b * (k+1) + j
+  const int b = r / (k + 1);
+  const char *rowp = logits + (int64_t)r * row_bytes;
+  const int NG = V / EPC;
+  const int e0 = s * CHUNK;
+
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  uint4 c[VCH];
+#pragma unroll
+  for (int q = 0; q < VCH; ++q) {
+    const int g = e0 / EPC + q * VT + tid;
+    if (g < NG) c[q] = *reinterpret_cast<const uint4 *>(rowp + (int64_t)g * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < VCH; ++q) {
+    const int g = e0 / EPC + q * VT + tid;
+    if (g < NG) {
+      const uint32_t w[4] = {c[q].x, c[q].y, c[q].z, c[q].w};
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const float x = DT == 1 ? ((j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]))
+                                : __uint_as_float(w[j]);
+        if (x > bv) { bv = x; bi = g * EPC + j; }   // ids rise within a lane
+      }
+    }
+  }
+  // Row tail that does not fill a 16-byte chunk: the last chunk's workgroup.
+  if (e0 + CHUNK >= V) {
+    for (int v = NG * EPC + tid; v < V; v += VT) {
+      const float x = DT == 1 ? __uint_as_float(
+                                    (uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
+                              : reinterpret_cast<const float *>(rowp)[v];
+      if (x > bv || (x == bv && v < bi)) { bv = x; bi = v; }
+    }
+  }
+  uint64_t key = bi == 0x7FFFFFFF ? 0ull : sel_key(bv, (uint32_t)bi);
+  key = wave_max_u64(key);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = key;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t m = red[0];
+    for (int i = 1; i < VT / kWave; ++i) m = red[i] > m ? red[i] : m;
+    partials[(int64_t)r * S + s] = m;
+    __threadfence();  // publish the partial before counting this workgroup
+    const uint32_t done = atomicAdd(&counters[b], 1u);
+    last = done == (uint32_t)((k + 1) * S - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  // Epilogue for batch row b: merge the partials of each position, then the
+  // left-to-right comparison (it stops at the first mismatch).
+  __shared__ int sel[kMaxVerifyK + 1];
+  __shared__ int nm_s;
+  for (int j = tid; j <= k; j += VT) {
+    uint64_t m = 0ull;
+    const uint64_t *p = partials + ((int64_t)b * (k + 1) + j) * S;
+    for (int q = 0; q < S; ++q) {
+      const uint64_t v = __hip_atomic_load(p + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      m = v > m ? v : m;
+    }
+    sel[j] = (int)key_index(m);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int nm = 0;
+    while (nm < k && cand[(int64_t)b * k + nm] == sel[nm]) ++nm;
+    nm_s = nm;
+    n_match[b] = nm;
+    next[b] = sel[nm];
+    k_out[b] = nm == k ? k + 2 : (k - 1 > 1 ? k - 1 : 1);
+    counters[b] = 0u;  // ready for the next call
+  }
+  __syncthreads();
+  for (int j = tid; j <= k; j += VT) tokens[(int64_t)b * (k + 1) + j] = j <= nm_s ? sel[j] : -1;
+}
+
+int verify_chunks(int32_t V, int32_t dtype) {
+  const int chunk = VT * VCH * (dtype == 1 ? 8 : 4);
+  return (V + chunk - 1) / chunk;
+}
+
+hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
+                         int64_t row_bytes, int32_t chunks, const int32_t *cand,
+                         int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,
+                         uint64_t *partials, uint32_t *counters, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  dim3 grid(chunks, B * (k + 1));
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_verify<1>, grid, dim3(VT), 0, s, (const char *)logits, row_bytes, V, k,
+                       chunks, cand, n_match, tokens, next, k_out, partials, counters);
+  else
+    hipLaunchKernelGGL(k_verify<0>, grid, dim3(VT), 0, s, (const char *)logits, row_bytes, V, k,
+                       chunks, cand, n_match, tokens, next, k_out, partials, counters);
+  return hipGetLastError();
+}
+
+}  // namespace tsel

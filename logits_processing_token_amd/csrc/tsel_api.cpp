@@ -1,0 +1,226 @@
+// tsel_api.cpp -- the C ABI of libtsel.so (declared in include/tsel.h):
+// argument validation on the host, on-chip layout of the selection kernel,
+// and the launches.  No entry point prints, throws or exits.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "tsel.h"
+#include "tsel_internal.hpp"
+
+namespace {
+
+constexpr int32_t kMaxVocab = 524288;   // on-chip kill + seen masks: V / 4 bytes
+constexpr int32_t kMaxList = 8192 + 8;  // sparse list: distinct seen ids + row tail
+
+inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+tsel_status check_params(const tsel_params *p, bool uniforms_given) {
+  if (!p) return TSEL_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->vocab < 1) return TSEL_ERR_INVALID_ARG;
+  if (p->logits_row_stride < p->vocab) return TSEL_ERR_INVALID_ARG;
+  if (p->dtype != TSEL_F32 && p->dtype != TSEL_BF16) return TSEL_ERR_INVALID_ARG;
+  if (p->hist_stride < 0) return TSEL_ERR_INVALID_ARG;
+  if (!(p->repetition_penalty > 0.0f)) return TSEL_ERR_INVALID_ARG;
+  if (p->no_repeat_ngram_size < 0) return TSEL_ERR_INVALID_ARG;
+  if (p->min_length < 0 || p->min_new_tokens < 0) return TSEL_ERR_INVALID_ARG;
+  if (p->n_eos < 0 || p->n_eos > TSEL_MAX_EOS) return TSEL_ERR_INVALID_ARG;
+  if (p->do_sample) {
+    if (!(p->temperature > 0.0f)) return TSEL_ERR_INVALID_ARG;
+    if (p->top_k < 0) return TSEL_ERR_INVALID_ARG;
+    if (!(p->top_p > 0.0f && p->top_p <= 1.0f)) return TSEL_ERR_INVALID_ARG;
+    if (!uniforms_given) return TSEL_ERR_INVALID_ARG;
+  }
+  if (p->vocab > kMaxVocab) return TSEL_ERR_UNSUPPORTED;
+  const int64_t esize = p->dtype == TSEL_BF16 ? 2 : 4;
+  if ((p->logits_row_stride * esize) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
+  return TSEL_OK;
+}
+
+// On-chip layout of one selection workgroup.  Returns false when V does not
+// fit at all.
+bool plan_layout(const tsel_params *p, tsel::SelectArgs *a, size_t *lds_bytes) {
+  const int32_t V = p->vocab;
+  const int32_t mw = (V + 31) / 32;
+  const size_t mask_bytes = align16((size_t)mw * 4);
+  a->mw = mw;
+  a->off_smask = (uint32_t)mask_bytes;
+  const size_t base = 2 * mask_bytes;
+  const size_t radix = 1024;
+  const size_t budget = (size_t)tsel::kSelectMaxDynLds;
+  if (base + radix + 8 * 64 > budget) return false;
+  size_t lcap_need = (size_t)std::min<int64_t>(std::max<int64_t>(p->hist_stride, 0), V) + 8;
+  lcap_need = std::min<size_t>(lcap_need, kMaxList);
+  int32_t nb = 0, ccap = 0, tcap = 0;
+  size_t mode = 0;
+  size_t lcap = lcap_need;
+  if (p->do_sample) {
+    // Largest power-of-two capacities that leave room for the list.
+    nb = 2048;
+    ccap = 2048;
+    tcap = 2048;
+    auto mode_bytes = [&]() {
+      const size_t full = 16 * (size_t)nb + 24 * (size_t)ccap + 8;
+      const size_t topk = 24 * (size_t)tcap;
+      return std::max(full, topk);
+    };
+    while (base + radix + mode_bytes() + 8 * lcap > budget && nb > 256) {
+      nb /= 2;
+      ccap /= 2;
+      tcap /= 2;
+    }
+    mode = mode_bytes();
+  }
+  if (base + radix + mode + 8 * lcap > budget) {
+    // Shrink the list; rows with more distinct seen ids penalize in the stream.
+    const size_t room = budget - base - radix - mode;
+    lcap = room / 8;
+    if (lcap < 64) return false;
+  }
+  lcap &= ~size_t(3);
+  a->lcap = (int32_t)lcap;
+  a->nb = nb;
+  a->ccap = ccap;
+  a->tcap = tcap;
+  a->off_list_id = (uint32_t)base;
+  a->off_list_val = (uint32_t)(base + 4 * lcap);
+  a->off_area = (uint32_t)align16(base + 8 * lcap);
+  *lds_bytes = a->off_area + radix + mode;
+  return *lds_bytes <= budget;
+}
+
+// Registers per lane that hold a whole row when the row goes straight to the
+// full path (sampling without a top_k the candidate buffer can hold); 0 means
+// the full path re-reads the row.
+int resident_chunks(const tsel_params *p, int32_t tcap) {
+  if (!p->do_sample || (p->top_k > 0 && std::min(p->top_k, p->vocab) * 4 <= tcap)) return 0;
+  const int epc = p->dtype == TSEL_BF16 ? 8 : 4;
+  const int64_t chunks = p->vocab / epc;
+  for (int r : {4, 8, 16})
+    if (chunks <= (int64_t)r * tsel::kSelectThreads) return r;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tsel_status_string(tsel_status s) {
+  switch (s) {
+    case TSEL_OK: return "ok";
+    case TSEL_ERR_INVALID_ARG: return "invalid argument";
+    case TSEL_ERR_UNSUPPORTED: return "unsupported argument combination";
+    case TSEL_ERR_LAUNCH: return "kernel launch failed";
+    case TSEL_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+tsel_status tsel_validate_params(const tsel_params *params, int32_t sampling_uniforms_given) {
+  return check_params(params, sampling_uniforms_given != 0);
+}
+
+size_t tsel_process_select_workspace_size(const tsel_params *params) {
+  (void)params;
+  return 0;
+}
+
+tsel_status tsel_process_select(const void *logits, const int32_t *history, const int32_t *lens,
+                                const tsel_params *params, const float *uniforms,
+                                int32_t *out_tokens, float *out_processed, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  tsel_status st = check_params(params, uniforms != nullptr);
+  if (st != TSEL_OK) return st;
+  if (params->batch == 0) return TSEL_OK;
+  if (!logits || !lens || !out_tokens) return TSEL_ERR_INVALID_ARG;
+  if (!history && params->hist_stride > 0) return TSEL_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
+
+  tsel::SelectArgs a{};
+  size_t lds = 0;
+  if (!plan_layout(params, &a, &lds)) return TSEL_ERR_UNSUPPORTED;
+  const int64_t esize = params->dtype == TSEL_BF16 ? 2 : 4;
+  a.logits = static_cast<const char *>(logits);
+  a.row_bytes = params->logits_row_stride * esize;
+  a.V = params->vocab;
+  a.B = params->batch;
+  a.dtype = params->dtype;
+  a.hist = history;
+  a.hist_stride = params->hist_stride;
+  a.lens = lens;
+  a.uniforms = uniforms;
+  a.out_tokens = out_tokens;
+  a.out_processed = out_processed;
+  a.bad_mask = params->bad_words_mask;
+  a.sup_mask = params->suppress_mask;
+  a.begin_mask = params->begin_suppress_mask;
+  a.rep = params->repetition_penalty;
+  a.ngram = params->no_repeat_ngram_size;
+  a.min_length = params->min_length;
+  a.min_new = params->min_new_tokens;
+  a.n_eos = params->n_eos;
+  for (int i = 0; i < TSEL_MAX_EOS; ++i) a.eos[i] = i < params->n_eos ? params->eos_ids[i] : -1;
+  a.forced_bos = params->forced_bos_token_id;
+  a.forced_eos = params->forced_eos_token_id;
+  a.do_sample = params->do_sample ? 1 : 0;
+  a.temperature = params->temperature;
+  a.top_k = params->top_k;
+  a.top_p = params->top_p;
+  if (!a.do_sample) {  // greedy: the warpers do not apply
+    a.temperature = 1.0f;
+    a.top_k = 0;
+    a.top_p = 1.0f;
+  }
+  hipError_t e = tsel::launch_select(a, resident_chunks(params, a.tcap), lds,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
+tsel_status tsel_mask_build(int32_t vocab, const int32_t *ids, int32_t n_ids, uint32_t *out_mask,
+                            void *stream) {
+  if (vocab < 1 || n_ids < 0 || !out_mask || (n_ids > 0 && !ids)) return TSEL_ERR_INVALID_ARG;
+  hipError_t e =
+      tsel::launch_mask_build(vocab, ids, n_ids, out_mask, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
+size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab) {
+  if (batch <= 0 || k < 0 || vocab < 1) return 0;
+  const int S = std::max(tsel::verify_chunks(vocab, TSEL_F32), tsel::verify_chunks(vocab, TSEL_BF16));
+  const size_t partials = (size_t)batch * (size_t)(k + 1) * (size_t)S * 8;
+  return align16(partials) + align16((size_t)batch * 4);
+}
+
+tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_t k,
+                        int32_t vocab, int64_t row_stride, const int32_t *candidates,
+                        int32_t *out_n_match, int32_t *out_tokens, int32_t *out_next,
+                        int32_t *out_k, void *workspace, size_t workspace_bytes, void *stream) {
+  if (batch < 0 || k < 0 || vocab < 1 || row_stride < vocab) return TSEL_ERR_INVALID_ARG;
+  if (dtype != TSEL_F32 && dtype != TSEL_BF16) return TSEL_ERR_INVALID_ARG;
+  if (batch == 0) return TSEL_OK;
+  if (!logits || !out_n_match || !out_tokens || !out_next || !out_k) return TSEL_ERR_INVALID_ARG;
+  if (k > 0 && !candidates) return TSEL_ERR_INVALID_ARG;
+  if (k > tsel::kMaxVerifyK) return TSEL_ERR_UNSUPPORTED;
+  const int64_t esize = dtype == TSEL_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0 || (row_stride * esize) % 16 != 0)
+    return TSEL_ERR_UNSUPPORTED;
+  const size_t need = tsel_verify_workspace_size(batch, k, vocab);
+  if (!workspace || workspace_bytes < need) return TSEL_ERR_WORKSPACE;
+  if ((int64_t)batch * (k + 1) > 65535) return TSEL_ERR_UNSUPPORTED;  // grid y limit
+  const int S = tsel::verify_chunks(vocab, dtype);
+  const int Smax = std::max(tsel::verify_chunks(vocab, TSEL_F32), tsel::verify_chunks(vocab, TSEL_BF16));
+  char *ws = static_cast<char *>(workspace);
+  uint64_t *partials = reinterpret_cast<uint64_t *>(ws);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(
+      ws + align16((size_t)batch * (size_t)(k + 1) * (size_t)Smax * 8));
+  hipError_t e = tsel::launch_verify(logits, dtype, batch, k, vocab, row_stride * esize, S,
+                                     candidates, out_n_match, out_tokens, out_next, out_k,
+                                     partials, counters, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// tsel_device.hpp -- wave64 / workgroup building blocks shared by the tsel
+// kernels (gfx950, CDNA4).  Device code only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsel {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Scores as ordered integer keys.
+//
+// ordered_f32 maps binary32 values to uint32 so that the integer order is the
+// float order for every non-NaN value; -0.0 is first turned into +0.0 so that
+// the two zeros compare equal, as they do as floats.
+__device__ __forceinline__ uint32_t ordered_f32(float x) {
+  uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unordered_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Selection key of (score, id): a larger key is a larger score, and among
+// equal scores the lower id.  0 is below every key of a real element.
+__device__ __forceinline__ uint64_t sel_key(float x, uint32_t idx) {
+  return ((uint64_t)ordered_f32(x) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) {
+  return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu);
+}
+__device__ __forceinline__ float key_score(uint64_t k) {
+  return unordered_f32((uint32_t)(k >> 32));
+}
+
+// bf16 bit patterns -> binary32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Repetition penalty of a seen id, as in Python transformers: a negative
+// score is multiplied by p, any other is divided by p (IEEE, round to
+// nearest even; HIP keeps binary32 division correctly rounded by default).
+__device__ __forceinline__ float penalize(float x, float p) {
+  return x < 0.0f ? x * p : x / p;
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (64 lanes).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int w = __shfl_up(v, o, kWave);
+    if (lane >= o) v += w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    double w = __shfl_up(v, o, kWave);
+    if (lane >= o) v += w;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup reductions.  `scratch` holds at least one slot per wave; every
+// thread of the workgroup must call; the result is returned to all threads.
+template <int NT>
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = wave_max_u64(v);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  v = lane < NW ? scratch[lane] : 0ull;
+  return wave_max_u64(v);
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max_f32(float v, float *scratch) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = wave_max_f32(v);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  v = lane < NW ? scratch[lane] : -INFINITY;
+  return wave_max_f32(v);
+}
+
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, double *scratch) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = wave_sum_f64(v);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  v = lane < NW ? scratch[lane] : 0.0;
+  return wave_sum_f64(v);
+}
+
+template <int NT>
+__device__ __forceinline__ int block_sum_i32(int v, int *scratch) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = wave_sum_i32(v);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  v = lane < NW ? scratch[lane] : 0;
+  return wave_sum_i32(v);
+}
+
+// Exclusive prefix sum over the workgroup in thread order; *total gets the
+// sum of all values.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan_i32(int v, int *scratch, int *total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  int incl = wave_incl_scan_i32(v);
+  __syncthreads();
+  if (lane == kWave - 1) scratch[wid] = incl;
+  __syncthreads();
+  int wsum = lane < NW ? scratch[lane] : 0;
+  int wincl = wave_incl_scan_i32(wsum);
+  int wbase = __shfl(wincl - wsum, wid, kWave);
+  *total = __shfl(wincl, NW - 1, kWave);
+  return wbase + incl - v;
+}
+
+}  // namespace tsel

@@ -1,0 +1,58 @@
+// tsel_internal.hpp -- launch descriptors shared by the C-ABI layer
+// (tsel_api.cpp) and the kernels.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tsel {
+
+constexpr int kSelectThreads = 1024;        // one workgroup (16 wave64s) per row
+constexpr int kLdsBytes = 160 * 1024;       // LDS of one gfx950 compute unit
+constexpr int kSelectStaticLds = 1024;      // upper bound of the kernel's static LDS
+constexpr int kSelectMaxDynLds = kLdsBytes - kSelectStaticLds;
+constexpr int kMaxVerifyK = 1023;           // drafts per row a verify call accepts
+
+// Arguments of the selection kernel (passed by value).
+struct SelectArgs {
+  const char *logits;
+  int64_t row_bytes;        // bytes between rows
+  int32_t V, B, dtype;
+  const int32_t *hist;
+  int32_t hist_stride;
+  const int32_t *lens;      // [3][B]
+  const float *uniforms;
+  int32_t *out_tokens;
+  float *out_processed;
+  const uint32_t *bad_mask, *sup_mask, *begin_mask;
+  float rep;
+  int32_t ngram;
+  int32_t min_length, min_new;
+  int32_t n_eos;
+  int32_t eos[8];
+  int32_t forced_bos, forced_eos;
+  int32_t do_sample;
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  // on-chip layout: kill mask at byte 0, then the others; capacities
+  int32_t mw;               // mask words: ceil(V / 32)
+  int32_t lcap;             // sparse list capacity
+  int32_t nb, ccap;         // full path: histogram bins, collect capacity
+  int32_t tcap;             // top_k candidate capacity
+  uint32_t off_smask, off_list_id, off_list_val, off_area;
+};
+
+hipError_t launch_select(const SelectArgs &a, int res, size_t lds, hipStream_t s);
+
+hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
+                         int64_t row_bytes, int32_t chunks, const int32_t *cand,
+                         int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,
+                         uint64_t *partials, uint32_t *counters, hipStream_t s);
+int verify_chunks(int32_t V, int32_t dtype);
+
+hipError_t launch_mask_build(int32_t V, const int32_t *ids, int32_t n, uint32_t *mask,
+                             hipStream_t s);
+
+}  // namespace tsel

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+include/tsel.h declares, and its host-side checks return the documented
+status codes before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from logits_processing_token_amd import tsel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "tsel.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsel_\w+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert _declared() == sorted(tsel.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tsel.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _params(**kw):
+    d = dict(batch=2, vocab=1000, row_stride=1000, dtype=tsel.TSEL_F32, hist_stride=16)
+    d.update({k: kw.pop(k) for k in list(kw) if k in d})
+    return tsel.make_params(d["batch"], d["vocab"], d["row_stride"], d["dtype"],
+                            d["hist_stride"], kw)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), tsel.TSEL_OK),
+    (dict(batch=-1), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(vocab=0, row_stride=0), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(row_stride=999), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(dtype=7), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(hist_stride=-1), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(repetition_penalty=0.0), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(repetition_penalty=float("nan")), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(no_repeat_ngram_size=-2), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(min_length=-1), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(min_new_tokens=-1), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(do_sample=True, temperature=0.0), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(do_sample=True, temperature=-1.0), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(do_sample=True, top_k=-1), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(do_sample=True, top_p=0.0), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(do_sample=True, top_p=1.5), tsel.TSEL_ERR_INVALID_ARG),
+    (dict(do_sample=True, top_p=1.0, top_k=5, temperature=0.5), tsel.TSEL_OK),
+    (dict(temperature=0.0), tsel.TSEL_OK),           # greedy ignores the warpers
+    (dict(vocab=1001, row_stride=1001), tsel.TSEL_ERR_UNSUPPORTED),  # 4004-byte rows
+    (dict(vocab=1001, row_stride=1004), tsel.TSEL_OK),
+    (dict(vocab=600000, row_stride=600000), tsel.TSEL_ERR_UNSUPPORTED),
+    (dict(dtype=tsel.TSEL_BF16, vocab=1004, row_stride=1004), tsel.TSEL_ERR_UNSUPPORTED),
+    (dict(dtype=tsel.TSEL_BF16, vocab=1004, row_stride=1008), tsel.TSEL_OK),
+])
+def test_validate(kw, status):
+    assert tsel.validate(_params(**kw)) == status
+
+
+def test_eos_count_checked():
+    p = _params()
+    p.n_eos = 9
+    assert tsel.validate(p) == tsel.TSEL_ERR_INVALID_ARG
+    p.n_eos = -1
+    assert tsel.validate(p) == tsel.TSEL_ERR_INVALID_ARG
+
+
+def test_sampling_needs_uniforms():
+    p = _params(do_sample=True)
+    assert tsel.validate(p, uniforms_given=False) == tsel.TSEL_ERR_INVALID_ARG
+    assert tsel.validate(p, uniforms_given=True) == tsel.TSEL_OK
+
+
+def test_entry_points_reject_before_any_gpu_call():
+    """Invalid or empty calls return from the host checks; no pointer is
+    dereferenced (the fake addresses would fault) and nothing is launched."""
+    lib = tsel.load()
+    fake = C.c_void_p(0x1000)
+    p = _params(batch=0)
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, None, 0,
+                                   None) == tsel.TSEL_OK
+    p = _params()
+    assert lib.tsel_process_select(None, fake, fake, C.byref(p), None, fake, None, None, 0,
+                                   None) == tsel.TSEL_ERR_INVALID_ARG
+    p = _params(do_sample=True)
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, None, 0,
+                                   None) == tsel.TSEL_ERR_INVALID_ARG
+    p = _params()
+    assert lib.tsel_process_select(C.c_void_p(0x1004), fake, fake, C.byref(p), None, fake, None,
+                                   None, 0, None) == tsel.TSEL_ERR_UNSUPPORTED
+    assert lib.tsel_mask_build(0, fake, 1, fake, None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_mask_build(10, None, 3, fake, None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_mask_build(10, fake, -1, fake, None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_mask_build(10, fake, 1, None, None) == tsel.TSEL_ERR_INVALID_ARG
+    ws = C.c_void_p(0x2000)
+    # verify: empty batch, bad sizes, missing/small workspace, misalignment
+    assert lib.tsel_verify(fake, 1, 0, 5, 100, 104, fake, fake, fake, fake, fake, None, 0,
+                           None) == tsel.TSEL_OK
+    assert lib.tsel_verify(fake, 1, 2, -1, 100, 104, fake, fake, fake, fake, fake, ws, 1 << 20,
+                           None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_verify(fake, 1, 2, 5, 100, 99, fake, fake, fake, fake, fake, ws, 1 << 20,
+                           None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_verify(fake, 3, 2, 5, 100, 104, fake, fake, fake, fake, fake, ws, 1 << 20,
+                           None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_verify(fake, 1, 2, 5, 100, 104, None, fake, fake, fake, fake, ws, 1 << 20,
+                           None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_verify(fake, 1, 2, 5, 100, 104, fake, fake, fake, fake, fake, None, 0,
+                           None) == tsel.TSEL_ERR_WORKSPACE
+    need = lib.tsel_verify_workspace_size(2, 5, 100)
+    assert need > 0
+    assert lib.tsel_verify(fake, 1, 2, 5, 100, 104, fake, fake, fake, fake, fake, ws, need - 1,
+                           None) == tsel.TSEL_ERR_WORKSPACE
+    assert lib.tsel_verify(fake, 1, 2, 5, 100, 100, fake, fake, fake, fake, fake, ws, need,
+                           None) == tsel.TSEL_ERR_UNSUPPORTED
+    assert lib.tsel_verify(fake, 1, 2, 2000, 100, 104, fake, fake, fake, fake, fake, ws, 1 << 30,
+                           None) == tsel.TSEL_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 17):
+        assert isinstance(tsel.status_string(s), str)
