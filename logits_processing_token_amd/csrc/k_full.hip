@@ -1,0 +1,691 @@
+// k_full.hip -- sampling without top_k (or with a top_k the candidate buffer
+// of k_topk cannot hold) for gfx950.
+//
+// One 1024-thread workgroup per row.  The row stays in registers when it
+// fits (16 chunks of 16 bytes per lane: 131072 bf16 or 65536 binary32 ids);
+// its loads are issued first and fly while the history is staged.  Then:
+//
+//  1. Mass histogram.  Every score y gets the mass e = 2^((y - r) log2 e)
+//     relative to a reference r just above the first chunk's maximum.  The
+//     binary32 bits of e name a bin (exponent and top mantissa bits), and one
+//     64-bit LDS add per element accumulates (count << 40) + (the mantissa
+//     bits below the bin's top bits).  Each bin's mass then follows exactly:
+//     every element of the bin shares the exponent and top bits, so the sum
+//     of their e is (count * (2^23 + top bits) + low-bit sum) * 2^(E-150).
+//     The order of the adds does not matter and nothing is rounded.
+//  2. The bin of the top_p boundary and the bins that can hold the sample
+//     (a short range) follow from the cumulative bin masses.
+//  3. The elements of those bins are collected (a bin edge maps back to a
+//     score threshold because the hardware exp2 is monotone, which a GPU test
+//     checks exhaustively), ordered by (score desc, id asc) and walked with
+//     binary64 prefix sums: the last kept id of top_p, the kept mass W' and
+//     the id whose cumulative mass first exceeds u * W'.
+//
+// A reference too far below the row maximum moves to the maximum (a second
+// histogram pass); bins too large to collect, and rows whose history needs
+// the in-stream penalty, use a bisection over selection keys that re-reads
+// the row.  Sources: "Transmuter.Generation (transmuter v2.0.0)", module doc
+// (temperature, top_k, top_p are the sampling warpers, in that order), and
+// the inverse-CDF draw of a caller uniform in (score desc, id asc) order.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "k_select_common.hpp"
+
+namespace tsel {
+
+// Histogram bin of a mass e >= 0 (its binary32 bits): the exponent and the
+// top mantissa bits, offset so that bin 1 starts kBinBelow binades below the
+// reference; bin 0 holds e == 0 and everything smaller, the last bin
+// everything larger.
+__device__ __forceinline__ int mass_bin(uint32_t bits, int shift, int base, int nb) {
+  return min(max((int)(bits >> shift), base), base + nb - 1) - base;  // one v_med3_i32
+}
+
+// Exact sum of the masses of bin b from its (count, low-bit sum) word.  Bin
+// 0 (removed ids and masses below the covered range) counts as 0.
+__device__ __forceinline__ double bin_mass(uint64_t acc, int b, int shift, int base) {
+  const uint64_t cnt = acc >> 40;
+  if (b == 0 || cnt == 0) return 0.0;
+  const uint64_t low = acc & ((1ull << 40) - 1);
+  // The bin's smallest mass e_lo has the bin's top bits and zero low bits;
+  // every member is e_lo + (its low bits) * ulp, ulp = 2^(exponent - 150).
+  const uint32_t lo_bits = (uint32_t)(b + base) << shift;
+  const double e_lo = (double)__uint_as_float(lo_bits);
+  const int expo = (int)(lo_bits >> 23);  // binary32 exponent field, 1..254
+  const double ulp = __longlong_as_double((long long)(expo - 150 + 1023) << 52);
+  return (double)cnt * e_lo + (double)low * ulp;  // both products exact
+}
+
+// Mass of a final score y relative to the reference (cref = r log2 e); with
+// a top_k, scores below its threshold t_y have none.  exp2(-inf) = 0, so
+// removed ids (-inf) have none either.
+template <bool TOPK = true>
+__device__ __forceinline__ float mass_of(float y, float t_y, float cref) {
+  const float e = __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -cref));
+  return TOPK ? ((y >= t_y) ? e : 0.0f) : e;
+}
+
+// ---------------------------------------------------------------------------
+// Slow, general pieces: they re-read the row from memory.
+
+// Exact k-th largest final score of the row (radix select over the stream).
+template <int DT>
+__device__ __forceinline__ float topk_threshold_stream(const SelectArgs &a, int row, const Lds &s,
+                                                    RowShared &sh, int k_eff) {
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  const float T = a.temperature;
+  const int n_list = sh.n_list;
+  const bool dense_pen = sh.dense_pen != 0;
+  const uint32_t tk = radix_kth_largest(
+      [&](auto &&f) {
+        stream_row<DT>(a, rowp, s, dense_pen, [&](int, float x) {
+          const float y = (T != 1.0f) ? x / T : x;
+          if (y > -INFINITY) f(ordered_f32(y));
+        });
+        for (int i = threadIdx.x; i < n_list; i += NT) {
+          const float y = (T != 1.0f) ? s.list_val[i] / T : s.list_val[i];
+          f(ordered_f32(y));
+        }
+      },
+      k_eff, s.rhist, sh);
+  return tk == 0u ? -INFINITY : unordered_f32(tk);
+}
+
+// Mass of the elements (score >= t_y) whose selection key is >= q.
+template <int DT>
+__device__ __forceinline__ double mass_key_ge(const SelectArgs &a, int row, const Lds &s,
+                                          RowShared &sh, float t_y, float cref, uint64_t q) {
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  const float T = a.temperature;
+  const int n_list = sh.n_list;
+  double m = 0.0;
+  stream_row<DT>(a, rowp, s, sh.dense_pen != 0, [&](int v, float x) {
+    const float y = (T != 1.0f) ? x / T : x;
+    if (y > -INFINITY && y >= t_y && sel_key(y, (uint32_t)v) >= q) m += (double)mass_of(y, t_y, cref);
+  });
+  for (int i = threadIdx.x; i < n_list; i += NT) {
+    const float y = (T != 1.0f) ? s.list_val[i] / T : s.list_val[i];
+    if (y >= t_y && sel_key(y, (uint32_t)s.list_id[i]) >= q) m += (double)mass_of(y, t_y, cref);
+  }
+  return block_sum_f64<NT>(m, sh.red_f64);
+}
+
+// Top_p cut and inverse-CDF draw by bisection over 64-bit selection keys.
+// Returns the token; *kcut_out = smallest kept key.
+template <int DT>
+__device__ __forceinline__ int bisect_select(const SelectArgs &a, int row, const Lds &s,
+                                          RowShared &sh, float t_y, float cref,
+                                          uint64_t *kcut_out) {
+  const double W = mass_key_ge<DT>(a, row, s, sh, t_y, cref, 1ull);
+  const double pw = (double)a.top_p * W;
+  uint64_t kcut = 0ull;
+  double Wp = W;
+  if (a.top_p < 1.0f && pw <= W) {
+    // kept iff the mass of larger keys is < pW: kcut is the smallest q with
+    // mass(key > q) = mass(key >= q + 1) < pW.  No element has key ~0.
+    uint64_t lo = 0ull, hi = ~0ull - 1ull;
+    while (hi - lo > 1ull) {
+      const uint64_t mid = lo + (hi - lo) / 2;
+      if (mass_key_ge<DT>(a, row, s, sh, t_y, cref, mid + 1) < pw) hi = mid; else lo = mid;
+    }
+    kcut = hi;
+    Wp = mass_key_ge<DT>(a, row, s, sh, t_y, cref, kcut);
+  }
+  const double target = (double)a.uniforms[row] * Wp;
+  // the token's key is max{q >= kcut : mass(key >= q) > target}
+  uint64_t lo = kcut, hi = ~0ull;
+  if (mass_key_ge<DT>(a, row, s, sh, t_y, cref, lo) > target) {
+    while (hi - lo > 1ull) {
+      const uint64_t mid = lo + (hi - lo) / 2;
+      if (mass_key_ge<DT>(a, row, s, sh, t_y, cref, mid) > target) lo = mid; else hi = mid;
+    }
+  } else {
+    // rounding at the very end: the smallest kept key
+    const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+    const float T = a.temperature;
+    uint64_t best = 0ull;
+    stream_row<DT>(a, rowp, s, sh.dense_pen != 0, [&](int v, float x) {
+      const float y = (T != 1.0f) ? x / T : x;
+      if (y > -INFINITY && y >= t_y) {
+        const uint64_t kk = sel_key(y, (uint32_t)v);
+        if (kk >= kcut) best = max(best, ~kk);
+      }
+    });
+    for (int i = threadIdx.x; i < sh.n_list; i += NT) {
+      const float y = (T != 1.0f) ? s.list_val[i] / T : s.list_val[i];
+      const uint64_t kk = sel_key(y, (uint32_t)s.list_id[i]);
+      if (y >= t_y && kk >= kcut) best = max(best, ~kk);
+    }
+    best = block_max_u64<NT>(best, sh.red_u64);
+    lo = ~best;
+  }
+  *kcut_out = kcut;
+  return (int)key_index(lo);
+}
+
+// ---------------------------------------------------------------------------
+// Histogram, bins, collect and walk for one row.  visit(f) calls f(id, y)
+// once for every element of the row (dense stream and list), y the final
+// score before top_k / top_p (killed ids as -inf).  Returns the token, or -1
+// when the bisection must decide; *kcut / *t_out describe the kept set.
+template <bool TOPK, class Visit>
+__device__ __forceinline__ int full_core(const SelectArgs &a, int row, const Lds &s,
+                                         RowShared &sh, float t_y, float m0, Visit &&visit,
+                                         uint64_t *kcut_out, float *t_out, float *cref_out) {
+  const int tid = threadIdx.x;
+  const int nb = a.nb;
+  const int shift = 23 - a.bin_mant;
+  const int base = (127 - kBinBelow) << a.bin_mant;
+  const uint32_t lowmask = (1u << shift) - 1u;
+  uint64_t *hist = reinterpret_cast<uint64_t *>(s.area);
+  uint64_t *ckey = reinterpret_cast<uint64_t *>(s.area + 8 * (size_t)nb);
+  float *cval = reinterpret_cast<float *>(s.area + 8 * (size_t)nb + 8 * (size_t)a.ccap);
+
+  // ---- 1. mass histogram (a second pass when the maximum outruns r) ----
+  float ref = m0 == -INFINITY ? 0.0f : m0 + kRefSlack;
+  float mx = -INFINITY;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const float c = ref * kLog2e;
+    for (int i = tid; i < nb; i += NT) hist[i] = 0ull;
+    __syncthreads();
+    float lmx = -INFINITY;
+    visit([&](int, float y) {
+      lmx = fmaxf(lmx, y);
+      const uint32_t bits = __float_as_uint(mass_of<TOPK>(y, t_y, c));
+      atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
+    });
+    mx = block_max_f32<NT>(lmx, sh.red_f32);
+    // Masses below 2^(kBinAbove - 1) stay under the top bin.
+    if (mx == -INFINITY || (mx - ref) * kLog2e < (float)(kBinAbove - 1)) break;
+    ref = mx;
+  }
+  const float cref = ref * kLog2e;
+  *cref_out = cref;
+  *t_out = t_y;
+  *kcut_out = 0ull;
+  if (mx == -INFINITY || mx < t_y) {  // every id removed: id 0
+    *kcut_out = ~0ull;
+    *t_out = INFINITY;
+    return 0;
+  }
+  // ---- 2. cumulative masses from the top bin down ------------------------
+  // Thread t owns bins [t*bpt, t*bpt + bpt); C(b) = mass of bins >= b.
+  const int bpt = (nb + NT - 1) / NT;
+  double part = 0.0;
+  for (int q = 0; q < bpt; ++q) {
+    const int b = tid * bpt + q;
+    if (b < nb) part += bin_mass(hist[b], b, shift, base);
+  }
+  double incl;  // mass of bins owned by threads >= tid
+  {
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    double v = part;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double t = __shfl_down(v, o, kWave);
+      if (lane + o < kWave) v += t;
+    }
+    __syncthreads();
+    if (lane == 0) sh.red_f64[wid] = v;
+    __syncthreads();
+    double after = 0.0;
+    for (int q = wid + 1; q < NW; ++q) after += sh.red_f64[q];
+    incl = v + after;
+  }
+  const double above_me = incl - part;
+  if (tid == 0) {
+    sh.wprime = incl;
+    sh.bin_p = -1;
+    sh.bin_hi = -1;
+  }
+  __syncthreads();
+  const double W = sh.wprime;
+  const bool use_top_p = a.top_p < 1.0f;
+  const double pw = (double)a.top_p * W;
+  const double u = (double)a.uniforms[row];
+  // top_p boundary bin bp: C(bp + 1) < pW <= C(bp)
+  {
+    double C = above_me;
+    for (int q = bpt - 1; q >= 0; --q) {
+      const int b = tid * bpt + q;
+      if (b >= nb) continue;
+      const double Cb1 = C;
+      C += bin_mass(hist[b], b, shift, base);
+      if (use_top_p && Cb1 < pw && C >= pw) { sh.bin_p = b; sh.sbase = Cb1; }
+    }
+  }
+  __syncthreads();
+  const int bp = sh.bin_p;
+  const double C_bp1 = bp >= 0 ? sh.sbase : 0.0;  // C(bp + 1): mass above the boundary bin
+  // W' lies in [C(bp + 1), C(bp)], so the target u W' lies in [t_lo, t_hi];
+  // the sample's bin is between the bins holding t_hi and t_lo.
+  const double t_lo = bp < 0 ? u * W : u * C_bp1;
+  const double t_hi = bp < 0 ? u * W : u * (C_bp1 + bin_mass(hist[bp], bp, shift, base));
+  if (tid == 0) {
+    sh.bin_hi = -1;
+    sh.found = -1;
+  }
+  __syncthreads();
+  {
+    double C = above_me;
+    for (int q = bpt - 1; q >= 0; --q) {
+      const int b = tid * bpt + q;
+      if (b >= nb) continue;
+      const double Cb1 = C;
+      C += bin_mass(hist[b], b, shift, base);
+      if (Cb1 <= t_lo && t_lo < C) { sh.bin_hi = b; sh.sbase = Cb1; }
+      if (Cb1 <= t_hi && t_hi < C) sh.found = b;
+    }
+  }
+  __syncthreads();
+  const int shi = sh.bin_hi;                    // highest bin that can hold the sample
+  const double S_top = shi >= 0 ? sh.sbase : 0.0;  // C(shi + 1)
+  int slo = sh.found;                           // lowest bin that can hold the sample
+  if (slo < 0 || (bp >= 0 && slo < bp)) slo = bp >= 0 ? bp : shi;
+  uint32_t ncount = 0;
+  if (shi >= 0)
+    for (int b = slo; b <= shi; ++b) ncount += (uint32_t)(hist[b] >> 40);
+  if (bp >= 0 && bp < slo) ncount += (uint32_t)(hist[bp] >> 40);
+  if (!(shi >= 1 && slo >= 1 && slo <= shi && ncount <= (uint32_t)a.ccap)) return -1;
+
+  // ---- 3. collect bin bp and bins [slo, shi] ----------------------------
+  // Bins are score intervals: Y(b) = smallest ordered score key of bin >= b,
+  // four bisections run on four lanes.
+  __shared__ uint32_t ylim[4];
+  if (tid < 4) {
+    const int bsel = tid == 0 ? slo : tid == 1 ? shi + 1 : tid == 2 ? bp : bp + 1;
+    uint32_t r = 0u;
+    if (tid < 2 || bp >= 0) {
+      if (bsel >= nb) {
+        r = 0xFFFFFFFFu;
+      } else {
+        uint32_t lo = ordered_f32(-INFINITY), hi = ordered_f32(INFINITY);
+        while (hi - lo > 1) {
+          const uint32_t mid = lo + (hi - lo) / 2;
+          if (mass_bin(__float_as_uint(mass_of<TOPK>(unordered_f32(mid), t_y, cref)), shift, base,
+                       nb) >= bsel)
+            hi = mid;
+          else
+            lo = mid;
+        }
+        r = hi;
+      }
+    }
+    ylim[tid] = r;
+  }
+  if (tid == 0) sh.n_coll = 0;
+  __syncthreads();
+  const uint32_t s_lo = ylim[0], s_hi = ylim[1], p_lo = ylim[2], p_hi = ylim[3];
+  visit([&](int v, float y) {
+    const uint32_t ky = ordered_f32(y);
+    if ((ky >= s_lo && ky < s_hi) || (ky >= p_lo && ky < p_hi)) {
+      const int slot = atomicAdd(&sh.n_coll, 1);
+      if (slot < a.ccap) {
+        ckey[slot] = sel_key(y, (uint32_t)v);
+        cval[slot] = mass_of<TOPK>(y, t_y, cref);
+      }
+    }
+  });
+  __syncthreads();
+  const int nc = min(sh.n_coll, a.ccap);
+
+  // ---- 4. exact order inside one bin --------------------------------------
+  // Among the collected elements of level-1 bin bsel with key >= kmin,
+  // starting from the mass `start` of everything before them: a
+  // sub-histogram over the next 8 mass bits (exact masses, as for the bins)
+  // finds the sub-bin where the running mass crosses `goal`; only that
+  // sub-bin is ordered by key.  cut: the first element whose mass before it
+  // is >= goal is removed (returns the last kept index, *acc = mass through
+  // it).  draw: the first element whose mass through it is > goal.
+  // Returns the selected key, or 0 when the sub-bin is too large to order.
+  __shared__ uint64_t subh[256];
+  __shared__ uint64_t gkey[kGatherCap];
+  __shared__ float gval[kGatherCap];
+  __shared__ double sub_start;
+  __shared__ int sub_sel, n_g;
+  __shared__ uint32_t g_emin, g_emax;
+  const int sshift = shift - 8;
+  const uint32_t slowmask = (1u << sshift) - 1u;
+  auto resolve = [&](int bsel, uint64_t kmin, double start, double goal, bool cut,
+                     double *acc) -> uint64_t {
+    for (int i = tid; i < 256; i += NT) subh[i] = 0ull;
+    if (tid == 0) { n_g = 0; sub_sel = -1; }
+    __syncthreads();
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t bits = __float_as_uint(cval[i]);
+      if (mass_bin(bits, shift, base, nb) == bsel && ckey[i] >= kmin)
+        atomicAdd(&subh[(bits >> sshift) & 255u], (1ull << 40) | (bits & slowmask));
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l holds sub-bins 255 - 4l .. 252 - 4l (descending mass)
+      double m[4], lane_sum = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int sb = 255 - 4 * tid - q;
+        const uint64_t acc_w = subh[sb];
+        const uint64_t cnt = acc_w >> 40;
+        const uint32_t lo_bits = ((uint32_t)(bsel + base) << shift) | ((uint32_t)sb << sshift);
+        const int expo = (int)(lo_bits >> 23);
+        const double ulp = __longlong_as_double((long long)(expo - 150 + 1023) << 52);
+        m[q] = cnt ? (double)cnt * (double)__uint_as_float(lo_bits) +
+                         (double)(acc_w & ((1ull << 40) - 1)) * ulp
+                   : 0.0;
+        lane_sum += m[q];
+      }
+      const double incl = wave_incl_scan_f64(lane_sum);
+      double before = start + (incl - lane_sum);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double after = before + m[q];
+        const bool hit = cut ? (before < goal && goal <= after) : (before <= goal && goal < after);
+        if (hit && m[q] > 0.0) { sub_sel = 255 - 4 * tid - q; sub_start = before; }
+        before = after;
+      }
+      // Nothing crossed inside this bin (rounding at its end): take the
+      // lowest non-empty sub-bin.
+      if (tid == kWave - 1) {
+        // (written only if no lane hit; checked after the barrier)
+      }
+    }
+    __syncthreads();
+    if (sub_sel < 0) {
+      if (tid < kWave) {
+        int lowest = -1;
+        for (int sb = tid; sb < 256; sb += kWave)
+          if ((subh[sb] >> 40) != 0) lowest = lowest < 0 ? sb : min(lowest, sb);
+        // wave min over lanes of `lowest` (ignoring -1)
+        int v = lowest < 0 ? 0x7FFFFFFF : lowest;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+        if (tid == 0 && v != 0x7FFFFFFF) {
+          double before = start;
+          for (int sb = 255; sb > v; --sb) {
+            const uint64_t acc_w = subh[sb];
+            const uint64_t cnt = acc_w >> 40;
+            if (!cnt) continue;
+            const uint32_t lo_bits = ((uint32_t)(bsel + base) << shift) | ((uint32_t)sb << sshift);
+            const int expo = (int)(lo_bits >> 23);
+            const double ulp = __longlong_as_double((long long)(expo - 150 + 1023) << 52);
+            before += (double)cnt * (double)__uint_as_float(lo_bits) +
+                      (double)(acc_w & ((1ull << 40) - 1)) * ulp;
+          }
+          sub_sel = v;
+          sub_start = before;
+        }
+      }
+      __syncthreads();
+    }
+    const int ss = sub_sel;
+    if (ss < 0) return 0ull;
+    if (tid == 0) { g_emin = 0xFFFFFFFFu; g_emax = 0u; }
+    __syncthreads();
+    auto in_group = [&](int i) {
+      const uint32_t bits = __float_as_uint(cval[i]);
+      return mass_bin(bits, shift, base, nb) == bsel && ckey[i] >= kmin &&
+             (int)((bits >> sshift) & 255u) == ss;
+    };
+    for (int i = tid; i < nc; i += NT) {
+      if (in_group(i)) {
+        const int slot = atomicAdd(&n_g, 1);
+        if (slot < kGatherCap) { gkey[slot] = ckey[i]; gval[slot] = cval[i]; }
+        atomicMin(&g_emin, __float_as_uint(cval[i]));  // masses are >= 0: bits order
+        atomicMax(&g_emax, __float_as_uint(cval[i]));
+      }
+    }
+    __syncthreads();
+    const int ng = n_g;
+    if (ng > kGatherCap) {
+      // A large group of equal masses (tied scores, typically): the mass
+      // before its j-th member in key order is sub_start + j e, so the member's
+      // rank follows by arithmetic and a radix select over the 64-bit keys
+      // names it.  Unequal masses: the caller bisects.
+      if (g_emin != g_emax) return 0ull;
+      const double e = (double)__uint_as_float(g_emin);
+      long long r;  // rank (0 = largest key) of the selected member
+      double through;
+      {
+        const double q = (goal - sub_start) / e;
+        if (cut) {  // first removed: smallest j with sub_start + j e >= goal
+          long long j = (long long)ceil(q);
+          if (j < 0) j = 0;
+          while (j > 0 && sub_start + (double)(j - 1) * e >= goal) --j;
+          while (j < ng && sub_start + (double)j * e < goal) ++j;
+          r = (j < ng ? j : ng) - 1;  // last kept
+          if (r < 0) r = 0;
+        } else {    // smallest j with sub_start + (j + 1) e > goal
+          long long j = (long long)floor(q);
+          if (j < 0) j = 0;
+          while (j > 0 && sub_start + (double)j * e > goal) --j;
+          while (j < ng - 1 && sub_start + (double)(j + 1) * e <= goal) ++j;
+          r = j < ng ? j : ng - 1;
+        }
+        through = sub_start + (double)(r + 1) * e;
+      }
+      const int k = (int)r + 1;
+      // k-th largest key of the group: high words first, then low words.
+      const uint32_t hiw = radix_kth_largest(
+          [&](auto &&f) {
+            for (int i = tid; i < nc; i += NT)
+              if (in_group(i)) f((uint32_t)(ckey[i] >> 32));
+          },
+          k, s.rhist, sh);
+      int above = 0;
+      for (int i = tid; i < nc; i += NT)
+        if (in_group(i) && (uint32_t)(ckey[i] >> 32) > hiw) ++above;
+      above = block_sum_i32<NT>(above, sh.red_i32);
+      const uint32_t low = radix_kth_largest(
+          [&](auto &&f) {
+            for (int i = tid; i < nc; i += NT)
+              if (in_group(i) && (uint32_t)(ckey[i] >> 32) == hiw) f((uint32_t)ckey[i]);
+          },
+          k - above, s.rhist, sh);
+      *acc = through;
+      return ((uint64_t)hiw << 32) | low;
+    }
+    // rank order (keys are distinct), into the collect buffer's head
+    // ordered copy: the scratch after the collect buffer
+    uint64_t *okey = reinterpret_cast<uint64_t *>(s.area + 8 * (size_t)nb + 12 * (size_t)a.ccap);
+    float *oval = reinterpret_cast<float *>(okey + kGatherCap);
+    for (int i = tid; i < ng; i += NT) {
+      const uint64_t ki = gkey[i];
+      int r = 0;
+      for (int j = 0; j < ng; ++j) r += gkey[j] > ki;
+      okey[r] = ki;
+      oval[r] = gval[i];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double A = sub_start;
+      int sel = -1;
+      if (cut) {
+        for (int j = 0; j < ng; ++j) {
+          if (A >= goal) break;
+          A += (double)oval[j];
+          sel = j;
+        }
+      } else {
+        for (int j = 0; j < ng; ++j) {
+          A += (double)oval[j];
+          sel = j;
+          if (A > goal) break;
+        }
+      }
+      sh.kcut = sel >= 0 ? okey[sel] : 0ull;
+      sh.wprime = A;
+    }
+    __syncthreads();
+    *acc = sh.wprime;
+    return sh.kcut;
+  };
+
+  uint64_t kc = 0ull;
+  double Wp = W;
+  if (bp >= 0) {
+    kc = resolve(bp, 0ull, C_bp1, pw, true, &Wp);
+    if (kc == 0ull) return -1;
+  }
+  // The sample's bin: walk bins from shi down (their masses; bp counts only
+  // its kept part).
+  const double target = u * Wp;
+  if (tid == 0) {
+    double C = S_top;
+    int bs = -1;
+    double before = S_top;
+    for (int b = shi; b >= slo && b >= 1; --b) {
+      const double mb = (bp >= 0 && b == bp) ? (Wp - C) : bin_mass(hist[b], b, shift, base);
+      if (mb > 0.0 && C <= target && target < C + mb) { bs = b; before = C; break; }
+      C += mb;
+    }
+    if (bs < 0) { bs = bp >= 0 ? bp : slo; before = -1.0; }
+    sh.bin_hi = bs;
+    sh.sbase = before;
+  }
+  __syncthreads();
+  const int bs = sh.bin_hi;
+  const double bs_start = sh.sbase;
+  if (bs_start < 0.0) return -1;  // rounding left the target outside: bisect
+  double dummy;
+  const uint64_t tk = resolve(bs, bs == bp ? kc : 0ull, bs_start, target, false, &dummy);
+  if (tk == 0ull || tk < kc) return -1;
+  *kcut_out = kc;
+  return (int)key_index(tk);
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int RES, bool SIMPLE>
+__global__ __launch_bounds__(NT, 1) void k_full(SelectArgs a, int pending_only) {
+  using E = Elem<DT>;
+  constexpr int EPC = E::EPC;
+  constexpr int R = RES > 0 ? RES : 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ RowShared sh;
+  const Lds s = carve(a, smem);
+  const int tid = threadIdx.x, row = blockIdx.x, V = a.V;
+  if (pending_only && a.out_tokens[row] != kPending) return;
+  const int NG = V / EPC;
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  const float T = SIMPLE ? 1.0f : a.temperature;  // SIMPLE: no temperature, no top_k
+  const int k_eff = (!SIMPLE && a.top_k > 0) ? min(a.top_k, V) : 0;
+  // Rows without top_k keep the row in registers when it fits; the loads fly
+  // while the history is staged.
+  const bool want_res = SIMPLE && RES > 0 && NG <= RES * NT;
+  uint4 reg[R];
+  if (want_res) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int g = tid + i * NT;
+      if (g < NG) reg[i] = load16(rowp + (int64_t)g * 16);
+    }
+  }
+  RowInfo ri;
+  if (row_prologue(a, row, ri)) return;
+  stage_row<DT>(a, row, ri, s, sh);
+  const bool dense_pen = sh.dense_pen != 0;
+  const int n_list = sh.n_list;
+  uint64_t kcut = 0ull;
+  float t_out = -INFINITY, cref = 0.0f;
+  int token;
+  float t_y = -INFINITY;
+  if (want_res && !dense_pen) {
+    // ---- resident row ----
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int g = tid + i * NT;
+      if (g < NG) reg[i] = kill_chunk<DT>(reg[i], g, s);
+    }
+    float m0 = -INFINITY;  // reference: the first chunk of every lane and the list
+    if (tid < NG)
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const float x = E::get(reg[0], j);
+        m0 = fmaxf(m0, (T != 1.0f) ? x / T : x);
+      }
+    for (int i = tid; i < n_list; i += NT) {
+      const float x = s.list_val[i];
+      m0 = fmaxf(m0, (T != 1.0f) ? x / T : x);
+    }
+    m0 = block_max_f32<NT>(m0, sh.red_f32);
+    token = full_core<!SIMPLE>(a, row, s, sh, t_y, m0,
+                      [&](auto &&f) {
+                        // Each pass unpacks the resident words afresh: without
+                        // this the compiler keeps the unpacked binary32 values
+                        // of one pass for the next and spills them.
+#pragma unroll
+                        for (int i = 0; i < R; ++i)
+                          asm volatile("" : "+v"(reg[i].x), "+v"(reg[i].y), "+v"(reg[i].z),
+                                       "+v"(reg[i].w));
+#pragma unroll
+                        for (int i = 0; i < R; ++i) {
+                          const int g = tid + i * NT;
+                          if (g < NG)
+#pragma unroll
+                            for (int j = 0; j < EPC; ++j) {
+                              const float x = E::get(reg[i], j);
+                              f(g * EPC + j, (T != 1.0f) ? x / T : x);
+                            }
+                        }
+                        for (int i = tid; i < n_list; i += NT) {
+                          const float x = s.list_val[i];
+                          f(s.list_id[i], (T != 1.0f) ? x / T : x);
+                        }
+                      },
+                      &kcut, &t_out, &cref);
+  } else {
+    // ---- streamed row ----
+    if (k_eff > 0) t_y = topk_threshold_stream<DT>(a, row, s, sh, k_eff);
+    auto visit = [&](auto &&f) {
+      stream_row<DT>(a, rowp, s, dense_pen,
+                     [&](int v, float x) { f(v, (T != 1.0f) ? x / T : x); });
+      for (int i = tid; i < n_list; i += NT) {
+        const float x = s.list_val[i];
+        f(s.list_id[i], (T != 1.0f) ? x / T : x);
+      }
+    };
+    float m0 = -INFINITY;
+    visit([&](int, float y) {
+      if (y >= t_y) m0 = fmaxf(m0, y);
+    });
+    m0 = block_max_f32<NT>(m0, sh.red_f32);
+    token = full_core<!SIMPLE>(a, row, s, sh, t_y, m0, visit, &kcut, &t_out, &cref);
+  }
+  if (token < 0) token = bisect_select<DT>(a, row, s, sh, t_y, cref, &kcut);
+  if (tid == 0) a.out_tokens[row] = token;
+  if (a.out_processed) write_processed<DT>(a, row, s, sh, t_out, kcut);
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int RES, bool SIMPLE>
+static hipError_t launch_full_t(const SelectArgs &a, size_t lds, hipStream_t st, int pending) {
+  static bool attr = false;  // benign race: every writer stores the same value
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_full<DT, RES, SIMPLE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kSelectMaxDynLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_full<DT, RES, SIMPLE>), dim3(a.B), dim3(NT), lds, st, a, pending);
+  return hipGetLastError();
+}
+
+// simple: temperature 1 and no top_k (the row may stay in registers).
+template <int DT>
+static hipError_t launch_full_dt(const SelectArgs &a, int res, size_t lds, hipStream_t st,
+                                 int pending, bool simple) {
+  if (!simple) return launch_full_t<DT, 0, false>(a, lds, st, pending);
+  if (res == 16) return launch_full_t<DT, 16, true>(a, lds, st, pending);
+  if (res == 8) return launch_full_t<DT, 8, true>(a, lds, st, pending);
+  if (res == 4) return launch_full_t<DT, 4, true>(a, lds, st, pending);
+  return launch_full_t<DT, 0, true>(a, lds, st, pending);
+}
+
+hipError_t launch_full(const SelectArgs &a, int res, size_t lds, hipStream_t st, int pending) {
+  const bool simple = a.temperature == 1.0f && a.top_k <= 0;
+  return a.dtype == 1 ? launch_full_dt<1>(a, res, lds, st, pending, simple)
+                      : launch_full_dt<0>(a, res, lds, st, pending, simple);
+}
+
+}  // namespace tsel

@@ -1,0 +1,396 @@
+// k_select_common.hpp -- pieces shared by the selection kernels (k_greedy,
+// k_topk, k_full): element access, on-chip layout, the row prologue, the
+// staging of the history and masks, the row stream and the radix select.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tsel_device.hpp"
+#include "tsel_internal.hpp"
+
+namespace tsel {
+
+constexpr int NT = kSelectThreads;
+constexpr int NW = NT / kWave;
+constexpr int U = 8;                 // 16-byte chunks in flight per lane when streaming
+constexpr uint32_t kNoDigit = 0xFFFFFFFFu;
+constexpr int kPending = -2;         // token marker: row left for k_full
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<0> {  // binary32
+  static constexpr int EPC = 4;
+  static constexpr uint32_t kNegInf = 0xFF800000u;
+  __device__ static __forceinline__ float get(const uint4 &c, int j) {
+    return __uint_as_float(j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w);
+  }
+  __device__ static __forceinline__ float load1(const char *row, int v) {
+    return reinterpret_cast<const float *>(row)[v];
+  }
+};
+template <>
+struct Elem<1> {  // bf16
+  static constexpr int EPC = 8;
+  static constexpr uint32_t kNegInf = 0xFF80FF80u;
+  __device__ static __forceinline__ float get(const uint4 &c, int j) {
+    uint32_t w = (j >> 1) == 0 ? c.x : (j >> 1) == 1 ? c.y : (j >> 1) == 2 ? c.z : c.w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+  __device__ static __forceinline__ float load1(const char *row, int v) {
+    uint32_t h = reinterpret_cast<const uint16_t *>(row)[v];
+    return __uint_as_float(h << 16);
+  }
+};
+
+struct RowShared {
+  uint64_t red_u64[NW];
+  double red_f64[NW];
+  float red_f32[NW];
+  int red_i32[NW];
+  int n_list;
+  int dense_pen;
+  int count;
+  int overflow;
+  uint32_t digit;
+  int krem;
+  float tau_x;
+  int token;
+  uint64_t kcut;
+  float t_y;
+  int bin_p, bin_hi;
+  int n_coll;
+  double wprime;
+  double sbase;
+  float ylo, yhi;
+  int found;
+};
+
+// On-chip regions of one workgroup (offsets from SelectArgs).
+struct Lds {
+  uint32_t *kmask, *smask;
+  int32_t *list_id;
+  float *list_val;
+  uint4 *lut;
+  uint32_t *rhist;
+  unsigned char *area;
+};
+
+__device__ __forceinline__ Lds carve(const SelectArgs &a, unsigned char *smem) {
+  Lds s;
+  s.kmask = reinterpret_cast<uint32_t *>(smem);
+  s.smask = reinterpret_cast<uint32_t *>(smem + a.off_smask);
+  s.list_id = reinterpret_cast<int32_t *>(smem + a.off_list_id);
+  s.list_val = reinterpret_cast<float *>(smem + a.off_list_val);
+  s.lut = reinterpret_cast<uint4 *>(smem + a.off_lut);
+  s.rhist = reinterpret_cast<uint32_t *>(smem + a.off_rhist);
+  s.area = smem + a.off_area;
+  return s;
+}
+
+__device__ __forceinline__ uint4 load16(const char *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+
+// Mask bits of chunk g: bit j covers element g * EPC + j.
+template <int DT>
+__device__ __forceinline__ uint32_t chunk_bits(const uint32_t *m, int g) {
+  const uint8_t *b = reinterpret_cast<const uint8_t *>(m);
+  if (DT == 1) return b[g];
+  return (b[g >> 1] >> ((g & 1) * 4)) & 0xFu;
+}
+
+__device__ __forceinline__ bool bit_of(const uint32_t *m, int v) {
+  return (m[v >> 5] >> (v & 31)) & 1u;
+}
+
+// Killed elements of a chunk become -inf in place: the kill bits index a
+// table of 16-byte masks, one bit-field insert per 32-bit word.
+template <int DT>
+__device__ __forceinline__ uint4 kill_chunk(uint4 c, int g, const Lds &s) {
+  const uint4 m = s.lut[chunk_bits<DT>(s.kmask, g)];
+  const uint32_t ninf = Elem<DT>::kNegInf;
+  c.x = (m.x & ninf) | (~m.x & c.x);
+  c.y = (m.y & ninf) | (~m.y & c.y);
+  c.z = (m.z & ninf) | (~m.z & c.z);
+  c.w = (m.w & ninf) | (~m.w & c.w);
+  return c;
+}
+
+// Smallest binary32 x with RN(x / T) >= RN(tau / T): the pre-temperature
+// threshold admitting every score the temperature maps onto tau's value
+// (division by T > 0 is monotone but can merge neighbours).
+__device__ inline float pre_temperature_floor(float tau, float T) {
+  if (T == 1.0f || tau == -INFINITY) return tau;
+  const float t = tau / T;
+  uint32_t hi = ordered_f32(tau), lo = 0;
+  while (hi - lo > 1) {
+    const uint32_t mid = lo + (hi - lo) / 2;
+    if (unordered_f32(mid) / T >= t) hi = mid; else lo = mid;
+  }
+  return unordered_f32(hi);
+}
+
+// k-th largest of a multiset of ordered keys by an LDS radix select over four
+// 8-bit digits; visit(f) calls f(key) once per element (all threads
+// together).  Returns 0 when there are fewer than k elements.
+template <class Visit>
+__device__ __forceinline__ uint32_t radix_kth_largest(Visit &&visit, int k, uint32_t *hist, RowShared &sh) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int krem = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
+    visit([&](uint32_t ok) {
+      if ((ok & pmask) == prefix) atomicAdd(&hist[(ok >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    if (tid < kWave) {
+      const int l = tid;
+      const uint32_t c0 = hist[255 - 4 * l], c1 = hist[254 - 4 * l], c2 = hist[253 - 4 * l],
+                     c3 = hist[252 - 4 * l];
+      const int s = (int)(c0 + c1 + c2 + c3);
+      const int incl = wave_incl_scan_i32(s);
+      const int excl = incl - s;
+      if (excl < krem && krem <= incl) {
+        int r = krem - excl;
+        uint32_t d;
+        if ((int)c0 >= r) d = 255 - 4 * l;
+        else if ((int)(c0 + c1) >= r) { d = 254 - 4 * l; r -= (int)c0; }
+        else if ((int)(c0 + c1 + c2) >= r) { d = 253 - 4 * l; r -= (int)(c0 + c1); }
+        else { d = 252 - 4 * l; r -= (int)(c0 + c1 + c2); }
+        sh.digit = d;
+        sh.krem = r;
+      }
+      if (l == kWave - 1 && incl < krem) sh.digit = kNoDigit;
+    }
+    __syncthreads();
+    const uint32_t d = sh.digit;
+    if (d == kNoDigit) return 0u;
+    prefix |= d << shift;
+    pmask |= 0xFFu << shift;
+    krem = sh.krem;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// ---------------------------------------------------------------------------
+// Row prologue: padding rows (no token) and forced rows (forced_bos at one
+// token, forced_eos at max_length - 1; the later processor wins; a forced id
+// that suppress / begin-suppress then removes leaves an all-removed row, id
+// 0).  Returns true when the row is finished.
+struct RowInfo {
+  int L, P, M, new_tokens;
+  bool begin_active;
+};
+
+__device__ __forceinline__ bool row_prologue(const SelectArgs &a, int row, RowInfo &ri) {
+  const int tid = threadIdx.x;
+  const int V = a.V;
+  ri.L = a.lens[row];
+  ri.P = a.lens[a.B + row];
+  ri.M = a.lens[2 * a.B + row];
+  ri.new_tokens = ri.L - ri.P;
+  ri.begin_active =
+      a.begin_mask != nullptr && ri.new_tokens == ((a.forced_bos >= 0 && ri.P == 1) ? 1 : 0);
+  float *outp = a.out_processed ? a.out_processed + (int64_t)row * V : nullptr;
+  if (ri.L <= 0) {
+    if (tid == 0) a.out_tokens[row] = -1;
+    if (outp)
+      for (int v = tid; v < V; v += NT) outp[v] = -INFINITY;
+    return true;
+  }
+  int forced = -1;
+  if (a.forced_bos >= 0 && ri.L == 1) forced = a.forced_bos;
+  if (a.forced_eos >= 0 && ri.L == ri.M - 1) forced = a.forced_eos;
+  if (forced >= 0) {
+    bool alive = forced < V;
+    if (alive && a.sup_mask && bit_of(a.sup_mask, forced)) alive = false;
+    if (alive && ri.begin_active && bit_of(a.begin_mask, forced)) alive = false;
+    if (tid == 0) a.out_tokens[row] = alive ? forced : 0;
+    if (outp)
+      for (int v = tid; v < V; v += NT) outp[v] = (alive && v == forced) ? 0.0f : -INFINITY;
+    return true;
+  }
+  return false;
+}
+
+// Staging of one row (see the file comment).  Leaves in LDS: the kill mask
+// (seen ids included unless dense_pen), the seen mask, the list of
+// (id, penalized logit) and the kill-mask table.
+template <int DT>
+__device__ __forceinline__ void stage_row(const SelectArgs &a, int row, const RowInfo &ri, const Lds &s,
+                          RowShared &sh) {
+  using E = Elem<DT>;
+  constexpr int EPC = E::EPC;
+  const int tid = threadIdx.x;
+  const int V = a.V;
+  const int NG = V / EPC;
+  const int Vvec = NG * EPC;
+  const int L = ri.L;
+  const int mw = a.mw;
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  for (int w = tid; w < mw; w += NT) {
+    s.kmask[w] = 0u;
+    s.smask[w] = 0u;
+  }
+  // table: kill bits of a chunk -> per-word masks of its killed elements
+  if (DT == 1) {
+    if (tid < 256) {
+      const uint32_t v = (uint32_t)tid;
+      uint32_t m[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        m[j] = (((v >> (2 * j)) & 1u) ? 0x0000FFFFu : 0u) |
+               (((v >> (2 * j + 1)) & 1u) ? 0xFFFF0000u : 0u);
+      s.lut[tid] = make_uint4(m[0], m[1], m[2], m[3]);
+    }
+  } else {
+    if (tid < 16) {
+      const uint32_t v = (uint32_t)tid;
+      s.lut[tid] = make_uint4((v & 1u) ? ~0u : 0u, (v & 2u) ? ~0u : 0u, (v & 4u) ? ~0u : 0u,
+                              (v & 8u) ? ~0u : 0u);
+    }
+  }
+  __syncthreads();
+  const int32_t *h = a.hist + (int64_t)row * a.hist_stride;
+  for (int i = tid; i < L; i += NT) {
+    const int v = h[i];
+    if (v >= 0 && v < V) atomicOr(&s.smask[v >> 5], 1u << (v & 31));
+  }
+  const int n = a.ngram;
+  if (n > 0 && L >= n) {
+    // Window i bans its last id when its first n-1 ids equal the last n-1
+    // ids of the history ("Lengths", no_repeat_ngram_size).
+    const int32_t *tail = h + (L - n + 1);
+    for (int i = tid; i + n <= L; i += NT) {
+      bool match = true;
+      for (int j = 0; j < n - 1; ++j)
+        if (h[i + j] != tail[j]) { match = false; break; }
+      const int t = h[i + n - 1];
+      if (match && t >= 0 && t < V) atomicOr(&s.kmask[t >> 5], 1u << (t & 31));
+    }
+  }
+  const bool minlen_active = a.min_new > 0 ? (ri.new_tokens < a.min_new)
+                                           : (a.min_length > 0 && L < a.min_length);
+  if (minlen_active && tid < a.n_eos) {
+    const int e = a.eos[tid];
+    if (e >= 0 && e < V) atomicOr(&s.kmask[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  // Fold the static masks in; count the seen ids that stay alive.
+  const int wpt = (mw + NT - 1) / NT;  // contiguous words per thread
+  int my_cnt = 0;
+  for (int q = 0; q < wpt; ++q) {
+    const int w = tid * wpt + q;
+    if (w < mw) {
+      uint32_t k = s.kmask[w];
+      if (a.bad_mask) k |= a.bad_mask[w];
+      if (a.sup_mask) k |= a.sup_mask[w];
+      if (ri.begin_active) k |= a.begin_mask[w];
+      s.kmask[w] = k;
+      my_cnt += __popc(s.smask[w] & ~k);
+    }
+  }
+  int n_seen = 0;
+  const int my_off = block_excl_scan_i32<NT>(my_cnt, sh.red_i32, &n_seen);
+  const bool dense_pen = n_seen > a.lcap - 8;
+  if (!dense_pen) {
+    int o = my_off;
+    for (int q = 0; q < wpt; ++q) {
+      const int w = tid * wpt + q;
+      if (w < mw) {
+        uint32_t bits = s.smask[w] & ~s.kmask[w];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          s.list_id[o++] = w * 32 + b;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = dense_pen ? 0 : n_seen;
+    for (int v = Vvec; v < V; ++v) {
+      const bool killed = bit_of(s.kmask, v) || (!dense_pen && bit_of(s.smask, v));
+      if (!killed) s.list_id[o++] = v;
+    }
+    sh.n_list = o;
+    sh.dense_pen = dense_pen ? 1 : 0;
+  }
+  __syncthreads();
+  if (!dense_pen)  // the stream kills seen ids; the list carries them
+    for (int w = tid; w < mw; w += NT) s.kmask[w] |= s.smask[w];
+  const int n_list = sh.n_list;
+  for (int i = tid; i < n_list; i += NT) {
+    const int v = s.list_id[i];
+    float x = E::load1(rowp, v);
+    if (bit_of(s.smask, v)) x = penalize(x, a.rep);
+    s.list_val[i] = x;
+  }
+  __syncthreads();
+}
+
+// Visit the dense elements of this lane in increasing id order, streaming
+// from global memory: f(id, x) with x after kill (-inf) and, in dense_pen
+// mode, after the penalty.
+template <int DT, class F>
+__device__ __forceinline__ void stream_row(const SelectArgs &a, const char *rowp, const Lds &s,
+                                           bool dense_pen, F &&f) {
+  using E = Elem<DT>;
+  constexpr int EPC = E::EPC;
+  const int NG = a.V / EPC;
+  for (int g0 = threadIdx.x; g0 < NG; g0 += NT * U) {
+    uint4 c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u * NT;
+      if (g < NG) c[u] = load16(rowp + (int64_t)g * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u * NT;
+      if (g < NG) {
+        const uint4 ck = kill_chunk<DT>(c[u], g, s);
+        const uint32_t sb = dense_pen ? chunk_bits<DT>(s.smask, g) : 0u;
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) {
+          float x = E::get(ck, j);
+          if ((sb >> j) & 1u) x = penalize(x, a.rep);
+          f(g * EPC + j, x);
+        }
+      }
+    }
+  }
+}
+
+// Final processed scores of a sampled row: the score after temperature when
+// kept (>= the top_k threshold t_y and selection key >= kcut), else -inf.
+template <int DT>
+__device__ __forceinline__ void write_processed(const SelectArgs &a, int row, const Lds &s, RowShared &sh,
+                                float t_y, uint64_t kcut) {
+  constexpr int EPC = Elem<DT>::EPC;
+  const int tid = threadIdx.x, V = a.V;
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  float *outp = a.out_processed + (int64_t)row * V;
+  const float T = a.temperature;
+  stream_row<DT>(a, rowp, s, sh.dense_pen != 0, [&](int v, float x) {
+    const float y = (T != 1.0f) ? x / T : x;
+    outp[v] = (y > -INFINITY && y >= t_y && sel_key(y, (uint32_t)v) >= kcut) ? y : -INFINITY;
+  });
+  for (int v = (V / EPC) * EPC + tid; v < V; v += NT) outp[v] = -INFINITY;
+  __syncthreads();
+  const int n_list = sh.n_list;
+  for (int i = tid; i < n_list; i += NT) {
+    const float y = (T != 1.0f) ? s.list_val[i] / T : s.list_val[i];
+    outp[s.list_id[i]] =
+        (y >= t_y && sel_key(y, (uint32_t)s.list_id[i]) >= kcut) ? y : -INFINITY;
+  }
+}
+
+}  // namespace tsel

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 
 #include "tsel.h"
 #include "tsel_internal.hpp"
@@ -39,63 +40,68 @@ tsel_status check_params(const tsel_params *p, bool uniforms_given) {
   return TSEL_OK;
 }
 
-// On-chip layout of one selection workgroup.  Returns false when V does not
-// fit at all.
-bool plan_layout(const tsel_params *p, tsel::SelectArgs *a, size_t *lds_bytes) {
+// On-chip layout of one selection workgroup for kernel `kind`.  Returns
+// false when V does not fit at all.
+enum class SelectKernel { kGreedy, kTopK, kFull };
+
+bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
+                 size_t *lds_bytes) {
   const int32_t V = p->vocab;
   const int32_t mw = (V + 31) / 32;
   const size_t mask_bytes = align16((size_t)mw * 4);
-  a->mw = mw;
-  a->off_smask = (uint32_t)mask_bytes;
   const size_t base = 2 * mask_bytes;
+  const size_t lut = (p->dtype == TSEL_BF16 ? 256 : 16) * 16;
   const size_t radix = 1024;
   const size_t budget = (size_t)tsel::kSelectMaxDynLds;
-  if (base + radix + 8 * 64 > budget) return false;
-  size_t lcap_need = (size_t)std::min<int64_t>(std::max<int64_t>(p->hist_stride, 0), V) + 8;
-  lcap_need = std::min<size_t>(lcap_need, kMaxList);
-  int32_t nb = 0, ccap = 0, tcap = 0;
-  size_t mode = 0;
-  size_t lcap = lcap_need;
-  if (p->do_sample) {
-    // Largest power-of-two capacities that leave room for the list.
-    nb = 2048;
-    ccap = 2048;
+  const size_t fixed = base + lut + radix;
+  const size_t min_list = 8 * 64;
+  if (fixed + min_list > budget) return false;
+  // every distinct history id plus the row's tail elements; a multiple of 4
+  // so that the value array stays 16-byte aligned
+  size_t lcap = (size_t)std::min<int64_t>(std::max<int64_t>(p->hist_stride, 0), V) + 8;
+  lcap = std::min<size_t>((lcap + 3) & ~size_t(3), kMaxList);
+  int32_t nb = 0, ccap = 0, mant = 0, tcap = 0;
+  size_t area = 0;
+  if (kind == SelectKernel::kTopK) {
     tcap = 2048;
-    auto mode_bytes = [&]() {
-      const size_t full = 16 * (size_t)nb + 24 * (size_t)ccap + 8;
-      const size_t topk = 24 * (size_t)tcap;
-      return std::max(full, topk);
+    while (tcap > 256 && fixed + 24 * (size_t)tcap + 8 * lcap > budget) tcap /= 2;
+    area = 24 * (size_t)tcap;
+  } else if (kind == SelectKernel::kFull) {
+    mant = 6;
+    ccap = 4096;
+    auto need = [&]() {
+      nb = (tsel::kBinBelow + tsel::kBinAbove) << mant;
+      // collected (key, mass) pairs, then room to order one sub-bin
+      return 8 * (size_t)nb + 12 * (size_t)ccap + 12 * (size_t)tsel::kGatherCap;
     };
-    while (base + radix + mode_bytes() + 8 * lcap > budget && nb > 256) {
-      nb /= 2;
-      ccap /= 2;
-      tcap /= 2;
+    area = need();
+    while ((mant > 3 || ccap > 256) && fixed + area + 8 * lcap > budget) {
+      if (mant > 3) --mant; else ccap /= 2;
+      area = need();
     }
-    mode = mode_bytes();
   }
-  if (base + radix + mode + 8 * lcap > budget) {
-    // Shrink the list; rows with more distinct seen ids penalize in the stream.
-    const size_t room = budget - base - radix - mode;
-    lcap = room / 8;
-    if (lcap < 64) return false;
-  }
-  lcap &= ~size_t(3);
+  if (fixed + area + min_list > budget) return false;
+  if (fixed + area + 8 * lcap > budget)  // rows that overflow apply penalties densely
+    lcap = ((budget - fixed - area) / 8) & ~size_t(3);
+  a->mw = mw;
   a->lcap = (int32_t)lcap;
   a->nb = nb;
   a->ccap = ccap;
+  a->bin_mant = mant;
   a->tcap = tcap;
+  a->off_smask = (uint32_t)mask_bytes;
   a->off_list_id = (uint32_t)base;
   a->off_list_val = (uint32_t)(base + 4 * lcap);
-  a->off_area = (uint32_t)align16(base + 8 * lcap);
-  *lds_bytes = a->off_area + radix + mode;
+  a->off_lut = (uint32_t)align16(base + 8 * lcap);
+  a->off_rhist = (uint32_t)(a->off_lut + lut);
+  a->off_area = (uint32_t)(a->off_rhist + radix);
+  *lds_bytes = a->off_area + area;
   return *lds_bytes <= budget;
 }
 
-// Registers per lane that hold a whole row when the row goes straight to the
-// full path (sampling without a top_k the candidate buffer can hold); 0 means
-// the full path re-reads the row.
-int resident_chunks(const tsel_params *p, int32_t tcap) {
-  if (!p->do_sample || (p->top_k > 0 && std::min(p->top_k, p->vocab) * 4 <= tcap)) return 0;
+// Chunks of 16 bytes per lane that hold a whole row in registers on the full
+// path (0: the row is re-read from memory on each pass).
+int resident_chunks(const tsel_params *p) {
   const int epc = p->dtype == TSEL_BF16 ? 8 : 4;
   const int64_t chunks = p->vocab / epc;
   for (int r : {4, 8, 16})
@@ -141,8 +147,6 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
   if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
 
   tsel::SelectArgs a{};
-  size_t lds = 0;
-  if (!plan_layout(params, &a, &lds)) return TSEL_ERR_UNSUPPORTED;
   const int64_t esize = params->dtype == TSEL_BF16 ? 2 : 4;
   a.logits = static_cast<const char *>(logits);
   a.row_bytes = params->logits_row_stride * esize;
@@ -170,13 +174,31 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
   a.temperature = params->temperature;
   a.top_k = params->top_k;
   a.top_p = params->top_p;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t lds = 0;
+  hipError_t e = hipSuccess;
   if (!a.do_sample) {  // greedy: the warpers do not apply
     a.temperature = 1.0f;
     a.top_k = 0;
     a.top_p = 1.0f;
+    if (!plan_layout(params, SelectKernel::kGreedy, &a, &lds)) return TSEL_ERR_UNSUPPORTED;
+    e = tsel::launch_greedy(a, lds, s);
+  } else {
+    tsel::SelectArgs t = a;
+    size_t tlds = 0;
+    const bool topk = a.top_k > 0 && plan_layout(params, SelectKernel::kTopK, &t, &tlds) &&
+                      std::min(a.top_k, a.V) * 4 <= t.tcap;
+    if (!plan_layout(params, SelectKernel::kFull, &a, &lds))
+      return TSEL_ERR_UNSUPPORTED;
+    if (topk) {
+      // Candidate-buffer pass; rows whose ties overflow it are marked and
+      // finished by the full path right after, on the same stream.
+      e = tsel::launch_topk(t, tlds, s);
+      if (e == hipSuccess) e = tsel::launch_full(a, resident_chunks(params), lds, s, 1);
+    } else {
+      e = tsel::launch_full(a, resident_chunks(params), lds, s, 0);
+    }
   }
-  hipError_t e = tsel::launch_select(a, resident_chunks(params, a.tcap), lds,
-                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 
@@ -185,6 +207,20 @@ tsel_status tsel_mask_build(int32_t vocab, const int32_t *ids, int32_t n_ids, ui
   if (vocab < 1 || n_ids < 0 || !out_mask || (n_ids > 0 && !ids)) return TSEL_ERR_INVALID_ARG;
   hipError_t e =
       tsel::launch_mask_build(vocab, ids, n_ids, out_mask, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
+tsel_status tsel_selftest_exp2_monotone(float lo, float hi, unsigned long long *violations,
+                                        void *stream) {
+  if (!violations || !(lo <= hi)) return TSEL_ERR_INVALID_ARG;
+  auto ordered = [](float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (u == 0x80000000u) u = 0u;  // -0 and +0 are one point
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  };
+  hipError_t e = tsel::launch_exp2_monotone(ordered(lo), ordered(hi), violations,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 

@@ -10,11 +10,19 @@ namespace tsel {
 
 constexpr int kSelectThreads = 1024;        // one workgroup (16 wave64s) per row
 constexpr int kLdsBytes = 160 * 1024;       // LDS of one gfx950 compute unit
-constexpr int kSelectStaticLds = 1024;      // upper bound of the kernel's static LDS
+constexpr int kSelectStaticLds = 12288;     // upper bound of the kernels' static LDS
 constexpr int kSelectMaxDynLds = kLdsBytes - kSelectStaticLds;
 constexpr int kMaxVerifyK = 1023;           // drafts per row a verify call accepts
 
-// Arguments of the selection kernel (passed by value).
+// Mass histogram of the full path: bins cover masses from 2^-kBinBelow to
+// 2^kBinAbove relative to the reference, 2^bin_mant bins per binade.
+constexpr int kBinBelow = 50;
+constexpr int kBinAbove = 16;
+constexpr int kGatherCap = 256;           // elements of one mass sub-bin ordered on chip
+constexpr float kRefSlack = 2.0f;           // reference = first-chunk max + this (nats)
+
+
+// Arguments of the selection kernels (passed by value).
 struct SelectArgs {
   const char *logits;
   int64_t row_bytes;        // bytes between rows
@@ -36,21 +44,28 @@ struct SelectArgs {
   float temperature;
   int32_t top_k;
   float top_p;
-  // on-chip layout: kill mask at byte 0, then the others; capacities
+  // on-chip layout (kill mask at byte 0) and capacities
   int32_t mw;               // mask words: ceil(V / 32)
   int32_t lcap;             // sparse list capacity
   int32_t nb, ccap;         // full path: histogram bins, collect capacity
+  int32_t bin_mant;         // full path: mantissa bits per bin
   int32_t tcap;             // top_k candidate capacity
-  uint32_t off_smask, off_list_id, off_list_val, off_area;
+  uint32_t off_smask, off_list_id, off_list_val, off_lut, off_rhist, off_area;
 };
 
-hipError_t launch_select(const SelectArgs &a, int res, size_t lds, hipStream_t s);
+hipError_t launch_greedy(const SelectArgs &a, size_t lds, hipStream_t s);
+hipError_t launch_topk(const SelectArgs &a, size_t lds, hipStream_t s);
+// pending != 0: only rows whose token k_topk left as pending
+hipError_t launch_full(const SelectArgs &a, int res, size_t lds, hipStream_t s, int pending);
 
 hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
                          int64_t row_bytes, int32_t chunks, const int32_t *cand,
                          int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,
                          uint64_t *partials, uint32_t *counters, hipStream_t s);
 int verify_chunks(int32_t V, int32_t dtype);
+
+hipError_t launch_exp2_monotone(uint32_t k0, uint32_t k1, unsigned long long *violations,
+                                hipStream_t s);
 
 hipError_t launch_mask_build(int32_t V, const int32_t *ids, int32_t n, uint32_t *mask,
                              hipStream_t s);

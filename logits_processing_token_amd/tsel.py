@@ -28,6 +28,7 @@ TSEL_MAX_EOS = 8
 EXPORTS = (
     "tsel_process_select", "tsel_process_select_workspace_size", "tsel_validate_params",
     "tsel_mask_build", "tsel_verify", "tsel_verify_workspace_size", "tsel_status_string",
+    "tsel_selftest_exp2_monotone",
 )
 
 
@@ -80,6 +81,8 @@ def load() -> C.CDLL:
     lib.tsel_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.tsel_status_string.restype = C.c_char_p
     lib.tsel_status_string.argtypes = [i32]
+    lib.tsel_selftest_exp2_monotone.restype = i32
+    lib.tsel_selftest_exp2_monotone.argtypes = [C.c_float, C.c_float, vp, vp]
     _lib = lib
     return lib
 
@@ -162,6 +165,15 @@ def mask_build(vocab: int, ids, out_mask=None, stream=None):
     st = lib.tsel_mask_build(vocab, _ptr(ids), int(ids.numel()), _ptr(out_mask), _stream(stream))
     _check(st, "tsel_mask_build")
     return out_mask
+
+
+def selftest_exp2_monotone(lo: float, hi: float, stream=None) -> int:
+    """Number of inputs in [lo, hi] where the device exp2 decreases."""
+    import torch
+    out = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _check(load().tsel_selftest_exp2_monotone(lo, hi, _ptr(out), _stream(stream)),
+           "tsel_selftest_exp2_monotone")
+    return int(out.item())
 
 
 def verify_workspace_size(batch: int, k: int, vocab: int) -> int:
