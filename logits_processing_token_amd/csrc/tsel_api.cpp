@@ -42,7 +42,7 @@ tsel_status check_params(const tsel_params *p, bool uniforms_given) {
 
 // On-chip layout of one selection workgroup for kernel `kind`.  Returns
 // false when V does not fit at all.
-enum class SelectKernel { kGreedy, kTopK, kFull };
+enum class SelectKernel { kGreedy, kTopK, kFull, kRes };
 
 bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
                  size_t *lds_bytes) {
@@ -52,8 +52,9 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   const size_t base = 2 * mask_bytes;
   const size_t lut = (p->dtype == TSEL_BF16 ? 256 : 16) * 16;
   const size_t radix = 1024;
+  const size_t woff = kind == SelectKernel::kRes ? 4 * (size_t)tsel::kSelectThreads : 0;
   const size_t budget = (size_t)tsel::kSelectMaxDynLds;
-  const size_t fixed = base + lut + radix;
+  const size_t fixed = base + lut + radix + woff;
   const size_t min_list = 8 * 64;
   if (fixed + min_list > budget) return false;
   // every distinct history id plus the row's tail elements; a multiple of 4
@@ -66,7 +67,7 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
     tcap = 2048;
     while (tcap > 256 && fixed + 24 * (size_t)tcap + 8 * lcap > budget) tcap /= 2;
     area = 24 * (size_t)tcap;
-  } else if (kind == SelectKernel::kFull) {
+  } else if (kind == SelectKernel::kFull || kind == SelectKernel::kRes) {
     mant = 6;
     ccap = 4096;
     auto need = [&]() {
@@ -94,7 +95,8 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   a->off_list_val = (uint32_t)(base + 4 * lcap);
   a->off_lut = (uint32_t)align16(base + 8 * lcap);
   a->off_rhist = (uint32_t)(a->off_lut + lut);
-  a->off_area = (uint32_t)(a->off_rhist + radix);
+  a->off_woff = (uint32_t)(a->off_rhist + radix);
+  a->off_area = (uint32_t)(a->off_woff + woff);
   *lds_bytes = a->off_area + area;
   return *lds_bytes <= budget;
 }
@@ -103,7 +105,7 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
 // path (0: the row is re-read from memory on each pass).
 int resident_chunks(const tsel_params *p) {
   const int epc = p->dtype == TSEL_BF16 ? 8 : 4;
-  const int64_t chunks = p->vocab / epc;
+  const int64_t chunks = (p->vocab + epc - 1) / epc;
   for (int r : {4, 8, 16})
     if (chunks <= (int64_t)r * tsel::kSelectThreads) return r;
   return 0;
@@ -190,7 +192,19 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
                       std::min(a.top_k, a.V) * 4 <= t.tcap;
     if (!plan_layout(params, SelectKernel::kFull, &a, &lds))
       return TSEL_ERR_UNSUPPORTED;
-    if (topk) {
+    const int res = resident_chunks(params);
+    const int epc = params->dtype == TSEL_BF16 ? 8 : 4;
+    tsel::SelectArgs r = a;
+    size_t rlds = 0;
+    if (a.top_k <= 0 && a.temperature == 1.0f && res > 0 && a.V >= epc &&
+        plan_layout(params, SelectKernel::kRes, &r, &rlds)) {
+      // Row held in registers.  A row with more distinct seen ids than the
+      // on-chip list holds is left pending for the streamed path.
+      e = tsel::launch_res(r, res, rlds, s);
+      const int64_t most_seen = std::min<int64_t>(std::max(params->hist_stride, 0), a.V);
+      if (e == hipSuccess && r.lcap < most_seen)
+        e = tsel::launch_full(a, res, lds, s, 1);
+    } else if (topk) {
       // Candidate-buffer pass; rows whose ties overflow it are marked and
       // finished by the full path right after, on the same stream.
       e = tsel::launch_topk(t, tlds, s);

@@ -49,6 +49,25 @@ __device__ __forceinline__ float penalize(float x, float p) {
 }
 
 // ---------------------------------------------------------------------------
+// Values every lane of the wave holds alike (read from LDS, say) moved into
+// scalar registers, which frees the vector registers they would occupy.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uni(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ float uni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ __forceinline__ uint64_t uni(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double uni(double v) {
+  return __longlong_as_double((long long)uni((uint64_t)__double_as_longlong(v)));
+}
+
+// ---------------------------------------------------------------------------
 // Wave reductions (64 lanes).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
@@ -105,6 +124,28 @@ __device__ __forceinline__ double wave_incl_scan_f64(double v) {
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load the wave has in flight; a kernel that stages
+// data in LDS while its row is still arriving uses this one instead.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max_f32_lds(float v, float *scratch) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = wave_max_f32(v);
+  lds_barrier();
+  if (lane == 0) scratch[wid] = v;
+  lds_barrier();
+  v = lane < NW ? scratch[lane] : -INFINITY;
+  return wave_max_f32(v);
+}
+
+// ---------------------------------------------------------------------------
 // Workgroup reductions.  `scratch` holds at least one slot per wave; every
 // thread of the workgroup must call; the result is returned to all threads.
 template <int NT>
@@ -156,15 +197,15 @@ __device__ __forceinline__ int block_sum_i32(int v, int *scratch) {
 }
 
 // Exclusive prefix sum over the workgroup in thread order; *total gets the
-// sum of all values.
-template <int NT>
+// sum of all values.  LDS_ONLY: barriers that do not wait for global loads.
+template <int NT, bool LDS_ONLY = false>
 __device__ __forceinline__ int block_excl_scan_i32(int v, int *scratch, int *total) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   int incl = wave_incl_scan_i32(v);
-  __syncthreads();
+  if (LDS_ONLY) lds_barrier(); else __syncthreads();
   if (lane == kWave - 1) scratch[wid] = incl;
-  __syncthreads();
+  if (LDS_ONLY) lds_barrier(); else __syncthreads();
   int wsum = lane < NW ? scratch[lane] : 0;
   int wincl = wave_incl_scan_i32(wsum);
   int wbase = __shfl(wincl - wsum, wid, kWave);

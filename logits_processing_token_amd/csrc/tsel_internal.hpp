@@ -51,12 +51,15 @@ struct SelectArgs {
   int32_t bin_mant;         // full path: mantissa bits per bin
   int32_t tcap;             // top_k candidate capacity
   uint32_t off_smask, off_list_id, off_list_val, off_lut, off_rhist, off_area;
+  uint32_t off_woff;        // resident path: list offset of each thread's mask words
 };
 
 hipError_t launch_greedy(const SelectArgs &a, size_t lds, hipStream_t s);
 hipError_t launch_topk(const SelectArgs &a, size_t lds, hipStream_t s);
-// pending != 0: only rows whose token k_topk left as pending
+// pending != 0: only rows whose token an earlier kernel left as pending
 hipError_t launch_full(const SelectArgs &a, int res, size_t lds, hipStream_t s, int pending);
+// sampling without top_k at temperature 1, row held in `res` chunks per lane
+hipError_t launch_res(const SelectArgs &a, int res, size_t lds, hipStream_t s);
 
 hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
                          int64_t row_bytes, int32_t chunks, const int32_t *cand,

@@ -165,6 +165,31 @@ def test_top_k_with_heavy_ties(topk):
     _assert_select(w)
 
 
+@pytest.mark.parametrize("V", [77, 4099, 50273, 131072])
+@pytest.mark.parametrize("q,topp", [(0.25, 0.9), (1.0, 0.3), (0.0625, 1.0), (0.5, 0.999)])
+def test_resident_tie_groups(V, q, topp):
+    """Quantized bf16 logits without top_k at temperature 1 (the resident
+    path): top_p boundaries and draws fall inside tie groups, whose members
+    are named in id order by counting over the registers.  Seen ids with
+    logit 0 keep 0 under the penalty and tie with the unseen zeros; odd V
+    leaves a partial last chunk."""
+    s = dict(repetition_penalty=1.2, do_sample=True, top_p=topp,
+             suppress_tokens=[3, 5, 8], bad_words_ids=[1, V - 1])
+    w = synth.random_select(300 + V, 16, V, 400, dtype="bf16", settings=s, sigma=2.0, quantize=q,
+                            id_range=min(V, 5000))
+    _assert_select(w, max_low_mismatch_frac=0.25)
+
+
+def test_resident_rows_of_one_value():
+    """Every logit equal: one tie group holds the whole row; the boundary and
+    the draw are ranks in id order."""
+    for V, topp in ((40000, 0.3), (1001, 0.77), (131072, 1.0)):
+        w = synth.random_select(7, 4, V, 64, dtype="bf16",
+                                settings=dict(do_sample=True, top_p=topp, repetition_penalty=1.5))
+        w.logits[:] = synth.bf16_bits(np.full((1,), 0.75, np.float32))[0]
+        _assert_select(w)
+
+
 def test_constant_logits_bisection():
     """Every score equal: the top_p boundary and the sample fall inside one
     histogram bin far larger than the collect buffer (bisection path)."""
