@@ -71,7 +71,7 @@ struct ResShared {
   int gid[2];
   int wtot[2][NW][16];
   int n_ind_all;
-  int n_coll2;
+  int ltie;
 };
 
 // Ordered score key of the smallest score whose mass falls in bin >= b.
@@ -180,13 +180,10 @@ __device__ WalkResult single_walk(bool cut, double start, double goal, const Bin
 }
 
 // Slot on the list of seen id v (alive seen ids are listed in id order;
-// woff[t] is the list offset of the kMpt mask words of thread t).
-__device__ __forceinline__ int list_slot(int v, const uint32_t *amask, const int32_t *woff) {
+// woff[w] is the list offset of mask word w).
+__device__ __forceinline__ int list_slot(int v, const uint32_t *amask, const uint16_t *woff) {
   const int w = v >> 5;
-  const int t = w / kMpt;
-  int o = woff[t];
-  for (int q = t * kMpt; q < w; ++q) o += __popc(amask[q]);
-  return o + __popc(amask[w] & ((1u << (v & 31)) - 1u));
+  return (int)woff[w] + __popc(amask[w] & ((1u << (v & 31)) - 1u));
 }
 
 // Hides a chunk's value from the optimizer, so that the elements unpacked
@@ -249,7 +246,7 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   __shared__ RowShared sh;
   __shared__ ResShared rs;
   const Lds s = carve(a, smem);
-  int32_t *woff = reinterpret_cast<int32_t *>(smem + a.off_woff);
+  uint16_t *woff = reinterpret_cast<uint16_t *>(smem + a.off_woff);
   const int tid = threadIdx.x, row = blockIdx.x, V = a.V;
   const int lane = tid & (kWave - 1), wid = tid / kWave;
   const int NG = V / EPC;  // whole chunks (>= 1 on this path)
@@ -374,11 +371,11 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     if (tid == 0) a.out_tokens[row] = kPending;
     return;
   }
-  woff[tid] = my_off;
   {
     int o = my_off;
 #pragma unroll
     for (int q = 0; q < kMpt; ++q) {
+      if (tid * kMpt + q < mw) woff[tid * kMpt + q] = (uint16_t)o;
       uint32_t bits = aq[q];
       while (bits) {
         const int b = __ffs(bits) - 1;
@@ -690,85 +687,121 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     if (tid == 0) sh.n_coll = 0;
     __syncthreads();
   }
-  const uint32_t k0lo = collect ? (uint32_t)gkey[0] : 1u, k0hi = collect ? (uint32_t)gkey[1] : 0u;
-  const uint32_t k1lo = collect ? (uint32_t)gkey[2] : 1u, k1hi = collect ? (uint32_t)gkey[3] : 0u;
-  constexpr int CPW = 32 / EPC;  // chunks per word of match bits
+  // score limits of the collect intervals (a key of ~0 is +inf)
+  float f0lo = INFINITY, f0hi = -INFINITY, f1lo = INFINITY, f1hi = -INFINITY;
+  if (collect) {
+    auto kf = [](uint32_t k) { return k == 0xFFFFFFFFu ? INFINITY : unordered_f32(k); };
+    f0lo = kf(uni((uint32_t)gkey[0]));
+    f0hi = kf(uni((uint32_t)gkey[1]));
+    if (c_hi1 >= c_lo1) {
+      f1lo = kf(uni((uint32_t)gkey[2]));
+      f1hi = kf(uni((uint32_t)gkey[3]));
+    }
+  }
+  constexpr int CPW = 32 / EPC;  // chunks per word of member bits
   uint32_t mk0[R / CPW + 1], mk1[R / CPW + 1];
 #pragma unroll
   for (int q = 0; q <= R / CPW; ++q) mk0[q] = mk1[q] = 0u;
-  if (g0 || g1 || collect) {
+  if (g0 || g1) {
     if (tid == 0) {
       rs.gv[0] = bp_v; rs.gk[0] = g0 ? rs.walk[0].rank + 1 : 0;
       rs.gv[1] = bs_v; rs.gk[1] = g1 ? rs.walk[1].rank + 1 : 0;
       rs.gi[0] = rs.gi[1] = -1;
       rs.gid[0] = rs.gid[1] = -1;
+      rs.ltie = 0;
     }
     __syncthreads();
-    const float v0 = g0 ? rs.gv[0] : NAN, v1 = g1 ? rs.gv[1] : NAN;
+    const float v0 = g0 ? uni(rs.gv[0]) : NAN, v1 = g1 ? uni(rs.gv[1]) : NAN;
+    // list elements equal to a group value join the group (rare): only then
+    // does the count look them up chunk by chunk
+    for (int k = tid; k < n_list; k += NT) {
+      const float y = s.list_val[k];
+      if (y == v0 || y == v1) rs.ltie = 1;
+    }
     __syncthreads();
+    const bool ltie = uni(rs.ltie) != 0;
+    // member bits of every chunk, in registers
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const uint4 c = launder(reg[i]);
       const int g = tid + i * NT;
-      int t0 = 0, t1 = 0;
-      uint32_t b0 = 0u, b1 = 0u;  // group members among this chunk's elements
+      uint32_t b0 = 0u, b1 = 0u;
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
         const float x = E::get(c, j);
         b0 |= (x == v0 ? 1u : 0u) << j;
         b1 |= (x == v1 ? 1u : 0u) << j;
-        t0 += __popcll(__ballot(x == v0));
-        t1 += __popcll(__ballot(x == v1));
-        if (collect) {
-          const uint32_t ky = ordered_f32(x);
-          if (x > -INFINITY && ((ky >= k0lo && ky < k0hi) || (ky >= k1lo && ky < k1hi))) {
-            const int slot = atomicAdd(&sh.n_coll, 1);
-            if (slot < a.ccap) {
-              ckey[slot] = sel_key(x, (uint32_t)(g * EPC + j));
-              cval[slot] = mass_of<false>(x, 0.0f, cref);
-            }
-          }
+      }
+      if (ltie && (g < NG || (g == NG && tail_n > 0))) {
+        uint32_t bits = chunk_bits<DT>(s.smask, g);
+        while (bits) {
+          const int j = __ffs(bits) - 1;
+          bits &= bits - 1;
+          const float y = s.list_val[list_slot(g * EPC + j, s.smask, woff)];
+          b0 |= (y == v0 ? 1u : 0u) << j;
+          b1 |= (y == v1 ? 1u : 0u) << j;
         }
       }
-      if (g0 || g1) {
-        // list elements of this chunk equal to a group value
-        int l0 = 0, l1 = 0;
-        if (g < NG || (g == NG && tail_n > 0)) {
-          uint32_t bits = chunk_bits<DT>(s.smask, g);
-          while (bits) {
-            const int j = __ffs(bits) - 1;
-            bits &= bits - 1;
-            const float y = s.list_val[list_slot(g * EPC + j, s.smask, woff)];
-            l0 += y == v0;
-            l1 += y == v1;
-            b0 |= (y == v0 ? 1u : 0u) << j;
-            b1 |= (y == v1 ? 1u : 0u) << j;
-          }
-        }
-        mk0[i / CPW] |= b0 << (EPC * (i % CPW));
-        mk1[i / CPW] |= b1 << (EPC * (i % CPW));
-        if (__ballot(l0 != 0) != 0ull) t0 += wave_sum_i32(l0);
-        if (__ballot(l1 != 0) != 0ull) t1 += wave_sum_i32(l1);
+      mk0[i / CPW] |= b0 << (EPC * (i % CPW));
+      mk1[i / CPW] |= b1 << (EPC * (i % CPW));
+    }
+    // members per (wave, chunk index): 16-bit fields, two chunks a word
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (!(t == 0 ? g0 : g1)) continue;
+#pragma unroll
+      for (int i = 0; i < R; i += 2) {
+        const uint32_t wa = t == 0 ? mk0[i / CPW] : mk1[i / CPW];
+        const uint32_t wb = t == 0 ? mk0[(i + 1) / CPW] : mk1[(i + 1) / CPW];
+        const uint32_t ca = __popc((wa >> (EPC * (i % CPW))) & ((1u << EPC) - 1u));
+        const uint32_t cb =
+            i + 1 < R ? __popc((wb >> (EPC * ((i + 1) % CPW))) & ((1u << EPC) - 1u)) : 0u;
+        uint32_t pk = ca | (cb << 16);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) pk += (uint32_t)__shfl_xor((int)pk, o, kWave);
         if (lane == 0) {
-          rs.wtot[0][wid][i] = t0;
-          rs.wtot[1][wid][i] = t1;
+          rs.wtot[t][wid][i] = (int)(pk & 0xFFFFu);
+          if (i + 1 < R) rs.wtot[t][wid][i + 1] = (int)(pk >> 16);
         }
       }
     }
-    if (collect) {
-      for (int k = tid; k < n_list; k += NT) {
-        const float y = s.list_val[k];
-        const uint32_t ky = ordered_f32(y);
-        if ((ky >= k0lo && ky < k0hi) || (ky >= k1lo && ky < k1hi)) {
-          const int slot = atomicAdd(&sh.n_coll, 1);
-          if (slot < a.ccap) {
-            ckey[slot] = sel_key(y, (uint32_t)s.list_id[k]);
-            cval[slot] = mass_of<false>(y, 0.0f, cref);
-          }
+  }
+  if (collect) {
+    // elements of the collect intervals, with their keys and masses
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint4 c = launder(reg[i]);
+      const int g = tid + i * NT;
+      uint32_t mb = 0u;
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const float x = E::get(c, j);
+        const bool m = (x >= f0lo && x < f0hi) || (x >= f1lo && x < f1hi);
+        mb |= (m ? 1u : 0u) << j;
+      }
+      while (mb) {
+        const int j = __ffs(mb) - 1;
+        mb &= mb - 1;
+        const float x = E::get(c, j);
+        const int slot = atomicAdd(&sh.n_coll, 1);
+        if (slot < a.ccap) {
+          ckey[slot] = sel_key(x, (uint32_t)(g * EPC + j));
+          cval[slot] = mass_of<false>(x, 0.0f, cref);
         }
       }
     }
-    __syncthreads();
+    for (int k = tid; k < n_list; k += NT) {
+      const float y = s.list_val[k];
+      if ((y >= f0lo && y < f0hi) || (y >= f1lo && y < f1hi)) {
+        const int slot = atomicAdd(&sh.n_coll, 1);
+        if (slot < a.ccap) {
+          ckey[slot] = sel_key(y, (uint32_t)s.list_id[k]);
+          cval[slot] = mass_of<false>(y, 0.0f, cref);
+        }
+      }
+    }
+  }
+  __syncthreads();
     if (g0 || g1) {
       // chunk index and wave of the k-th member in id order (chunk index,
       // then thread, then element)
@@ -825,7 +858,6 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
         __syncthreads();
       }
     }
-  }
   if ((g0 && rs.gid[0] < 0) || (g1 && rs.gid[1] < 0)) fallback = true;
   if (!fallback && g0) kcut = sel_key(bp_v, (uint32_t)rs.gid[0]);
   if (!fallback && draw_kind == kGroup) token = rs.gid[1];

@@ -52,7 +52,7 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   const size_t base = 2 * mask_bytes;
   const size_t lut = (p->dtype == TSEL_BF16 ? 256 : 16) * 16;
   const size_t radix = 1024;
-  const size_t woff = kind == SelectKernel::kRes ? 4 * (size_t)tsel::kSelectThreads : 0;
+  const size_t woff = kind == SelectKernel::kRes ? align16(2 * (size_t)mw) : 0;  // list offset per mask word
   const size_t budget = (size_t)tsel::kSelectMaxDynLds;
   const size_t fixed = base + lut + radix + woff;
   const size_t min_list = 8 * 64;
