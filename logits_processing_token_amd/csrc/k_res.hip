@@ -90,6 +90,48 @@ __device__ __forceinline__ uint32_t bin_floor_key(int b, int nb, int shift, int 
   return hi;
 }
 
+// The same key found by one whole wave: a first guess from the logarithm of
+// the bin's smallest mass, then three 64-way searches that narrow a window
+// of 2^16 keys around it to one key.  The map from score to bin is monotone
+// (the device exp2 is), so the window holds the edge whenever its two ends
+// fall on either side; otherwise one lane bisects the whole key range.
+// Every lane of the wave calls; all get the key.
+__device__ __forceinline__ uint32_t bin_floor_key_wave(int b, int nb, int shift, int base,
+                                                       float cref) {
+  if (b <= 0) return 0u;
+  if (b >= nb) return 0xFFFFFFFFu;
+  const int lane = threadIdx.x & (kWave - 1);
+  auto in_bin = [&](uint32_t k) {
+    return mass_bin(__float_as_uint(mass_of<false>(unordered_f32(k), 0.0f, cref)), shift, base, nb) >= b;
+  };
+  const float e_lo = __uint_as_float((uint32_t)(b + base) << shift);
+  // y with y log2(e) - cref = log2(e_lo)
+  const double y0 = ((double)__log2f(e_lo) + (double)cref) / 1.4426950408889634;
+  const uint32_t k0 = ordered_f32((float)y0);
+  uint32_t lo = k0 > 0x8000u ? k0 - 0x8000u : 1u;          // in_bin(lo) must be false
+  uint32_t hi = k0 < 0xFFFF7FFFu ? k0 + 0x8000u : 0xFFFFFFFEu;  // in_bin(hi) must be true
+  const bool ok = !in_bin(lo) && in_bin(hi);
+  if (ok) {
+    // invariant: !in_bin(lo), in_bin(hi)
+    for (int r = 0; r < 3 && hi - lo > 1; ++r) {
+      const uint64_t step = ((uint64_t)(hi - lo) + 63) / 64;
+      const uint64_t kk = (uint64_t)lo + (uint64_t)(lane + 1) * step;  // no wrap in 64 bits
+      const bool pass = kk >= (uint64_t)hi || in_bin((uint32_t)kk);
+      const uint64_t m = __ballot(pass);  // lanes from the first passing one on pass
+      const int first = __ffsll((long long)m) - 1;  // lane 63 always passes (kk >= hi)
+      const uint32_t new_hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + (uint64_t)(first + 1) * step);
+      const uint32_t new_lo = (uint32_t)((uint64_t)lo + (uint64_t)first * step);
+      lo = new_lo;
+      hi = new_hi;
+    }
+    if (hi - lo <= 1) return hi;
+  }
+  // fall back: one lane bisects the whole range
+  uint32_t r = 0u;
+  if (lane == 0) r = bin_floor_key(b, nb, shift, base, cref);
+  return (uint32_t)__shfl((int)r, 0, kWave);
+}
+
 // The bf16 value set inside scores [klo, khi) (ordered keys): returns the
 // number of bf16 values there, capped at 2, and the first one.
 __device__ __forceinline__ int bf16_values_in(uint32_t klo, uint32_t khi, float *first) {
@@ -397,12 +439,14 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     if (g < NG || (g == NG && tail_n > 0)) {
       const uint32_t kb = chunk_bits<DT>(s.kmask, g), sb = chunk_bits<DT>(s.smask, g);
       if (sb) {
+        // the chunk's seen ids hold consecutive list slots (the list is in
+        // id order); their raw scores go there, the penalty comes later
+        int slot = list_slot(g * EPC + __ffs(sb) - 1, s.smask, woff);
         uint32_t bits = sb;
         while (bits) {
           const int j = __ffs(bits) - 1;
           bits &= bits - 1;
-          const int v = g * EPC + j;
-          s.list_val[list_slot(v, s.smask, woff)] = penalize(E::get(c, j), a.rep);
+          s.list_val[slot++] = E::get(c, j);
         }
       }
       c = kill_bits<DT>(c, kb, s);
@@ -424,9 +468,10 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
     }
   }
-  __syncthreads();  // the row has landed; list values are complete
+  __syncthreads();  // the row has landed; the list holds the raw scores
   for (int k = tid; k < n_list; k += NT) {
-    const float y = s.list_val[k];
+    const float y = penalize(s.list_val[k], a.rep);
+    s.list_val[k] = y;
     lmax = fmaxf(lmax, y);
     const uint32_t bits = __float_as_uint(mass_of<false>(y, 0.0f, cref));
     atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
@@ -546,7 +591,10 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   // ordered by key into okey / oval.  Returns false when the bin has more
   // list elements than fit.
   auto view_bin = [&](int b) -> bool {
-    if (tid < 2) rs.klim[tid] = bin_floor_key(b + tid, nb, shift, base, cref);
+    if (wid < 2) {
+      const uint32_t k = bin_floor_key_wave(b + wid, nb, shift, base, cref);
+      if (lane == 0) rs.klim[wid] = k;
+    }
     if (tid == 0) rs.n_ind_all = 0;
     __syncthreads();
     const uint32_t klo = uni(rs.klim[0]), khi = uni(rs.klim[1]);
@@ -678,11 +726,11 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   }
   const bool collect = !fallback && (cut_kind == kCollect || draw_kind == kCollect);
   if (collect) {
-    if (tid < 4) {
-      const int bsel = tid == 0 ? c_lo0 : tid == 1 ? c_hi0 + 1 : tid == 2 ? c_lo1 : c_hi1 + 1;
+    if (wid < 4) {
+      const int bsel = wid == 0 ? c_lo0 : wid == 1 ? c_hi0 + 1 : wid == 2 ? c_lo1 : c_hi1 + 1;
       uint32_t r = 0u;
-      if (tid < 2 || c_hi1 >= c_lo1) r = bin_floor_key(bsel, nb, shift, base, cref);
-      gkey[tid] = r;
+      if (wid < 2 || c_hi1 >= c_lo1) r = bin_floor_key_wave(bsel, nb, shift, base, cref);
+      if (lane == 0) gkey[wid] = r;
     }
     if (tid == 0) sh.n_coll = 0;
     __syncthreads();
@@ -698,10 +746,7 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       f1hi = kf(uni((uint32_t)gkey[3]));
     }
   }
-  constexpr int CPW = 32 / EPC;  // chunks per word of member bits
-  uint32_t mk0[R / CPW + 1], mk1[R / CPW + 1];
-#pragma unroll
-  for (int q = 0; q <= R / CPW; ++q) mk0[q] = mk1[q] = 0u;
+  bool ltie_all = false;
   if (g0 || g1) {
     if (tid == 0) {
       rs.gv[0] = bp_v; rs.gk[0] = g0 ? rs.walk[0].rank + 1 : 0;
@@ -720,49 +765,37 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     }
     __syncthreads();
     const bool ltie = uni(rs.ltie) != 0;
-    // member bits of every chunk, in registers
+    ltie_all = ltie;
+    // members per (wave, chunk index): wave-wide ballots
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const uint4 c = launder(reg[i]);
       const int g = tid + i * NT;
-      uint32_t b0 = 0u, b1 = 0u;
+      int t0 = 0, t1 = 0;
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
         const float x = E::get(c, j);
-        b0 |= (x == v0 ? 1u : 0u) << j;
-        b1 |= (x == v1 ? 1u : 0u) << j;
+        if (g0) t0 += __popcll(__ballot(x == v0));
+        if (g1) t1 += __popcll(__ballot(x == v1));
       }
-      if (ltie && (g < NG || (g == NG && tail_n > 0))) {
-        uint32_t bits = chunk_bits<DT>(s.smask, g);
-        while (bits) {
-          const int j = __ffs(bits) - 1;
-          bits &= bits - 1;
-          const float y = s.list_val[list_slot(g * EPC + j, s.smask, woff)];
-          b0 |= (y == v0 ? 1u : 0u) << j;
-          b1 |= (y == v1 ? 1u : 0u) << j;
+      if (ltie) {
+        int l0 = 0, l1 = 0;
+        if (g < NG || (g == NG && tail_n > 0)) {
+          uint32_t bits = chunk_bits<DT>(s.smask, g);
+          while (bits) {
+            const int j = __ffs(bits) - 1;
+            bits &= bits - 1;
+            const float y = s.list_val[list_slot(g * EPC + j, s.smask, woff)];
+            l0 += y == v0;
+            l1 += y == v1;
+          }
         }
+        if (__ballot(l0 != 0) != 0ull) t0 += wave_sum_i32(l0);
+        if (__ballot(l1 != 0) != 0ull) t1 += wave_sum_i32(l1);
       }
-      mk0[i / CPW] |= b0 << (EPC * (i % CPW));
-      mk1[i / CPW] |= b1 << (EPC * (i % CPW));
-    }
-    // members per (wave, chunk index): 16-bit fields, two chunks a word
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (!(t == 0 ? g0 : g1)) continue;
-#pragma unroll
-      for (int i = 0; i < R; i += 2) {
-        const uint32_t wa = t == 0 ? mk0[i / CPW] : mk1[i / CPW];
-        const uint32_t wb = t == 0 ? mk0[(i + 1) / CPW] : mk1[(i + 1) / CPW];
-        const uint32_t ca = __popc((wa >> (EPC * (i % CPW))) & ((1u << EPC) - 1u));
-        const uint32_t cb =
-            i + 1 < R ? __popc((wb >> (EPC * ((i + 1) % CPW))) & ((1u << EPC) - 1u)) : 0u;
-        uint32_t pk = ca | (cb << 16);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) pk += (uint32_t)__shfl_xor((int)pk, o, kWave);
-        if (lane == 0) {
-          rs.wtot[t][wid][i] = (int)(pk & 0xFFFFu);
-          if (i + 1 < R) rs.wtot[t][wid][i + 1] = (int)(pk >> 16);
-        }
+      if (lane == 0) {
+        rs.wtot[0][wid][i] = t0;
+        rs.wtot[1][wid][i] = t1;
       }
     }
   }
@@ -835,11 +868,22 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
         if (ii < 0) { fallback = true; continue; }
         if (wid == rs.gw[t]) {
           const int g = tid + ii * NT;
-          uint32_t word = 0u;
+          const float vv = rs.gv[t];
+          uint4 c = reg[0];
 #pragma unroll
-          for (int q = 0; q <= R / CPW; ++q)
-            if (q == ii / CPW) word = t == 0 ? mk0[q] : mk1[q];
-          const uint32_t mbits = (word >> (EPC * (ii % CPW))) & ((1u << EPC) - 1u);
+          for (int i = 1; i < R; ++i)
+            if (i == ii) c = reg[i];
+          uint32_t mbits = 0u;  // members among this lane's elements of chunk ii
+#pragma unroll
+          for (int j = 0; j < EPC; ++j) mbits |= (E::get(c, j) == vv ? 1u : 0u) << j;
+          if (ltie_all && (g < NG || (g == NG && tail_n > 0))) {
+            uint32_t bits = chunk_bits<DT>(s.smask, g);
+            while (bits) {
+              const int j = __ffs(bits) - 1;
+              bits &= bits - 1;
+              if (s.list_val[list_slot(g * EPC + j, s.smask, woff)] == vv) mbits |= 1u << j;
+            }
+          }
           const int cnt = __popc(mbits);
           const int inc = wave_incl_scan_i32(cnt);
           const int rem = rs.gr[t];
