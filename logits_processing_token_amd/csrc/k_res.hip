@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "k_mass.hpp"
 
 namespace tsel {
@@ -36,6 +38,15 @@ namespace {
 constexpr int kPipe = 8;  // 16-byte chunks in flight per lane
 constexpr int kHpt = 4;   // history ids per thread held in registers
 constexpr int kMpt = 4;   // kill-mask words per thread: V <= 32 * kMpt * NT
+// Elements that may share a mass bin with another value are kept on chip
+// as they land, so that such a bin is ordered from that buffer without
+// another pass over the row.  In a bf16 row these are the scores below
+// 2^(7 - bin_mant) in magnitude: with 2^bin_mant bins per binade a bin spans
+// less than 2^-bin_mant in score, and above that magnitude the bf16 spacing
+// is at least as wide, so a bin there holds one value at most.  In a
+// binary32 row, the scores within kHeadDelta nats of the first chunks'
+// maximum.
+constexpr float kHeadDelta = 3.0f;
 
 enum : int { kFail = -1, kInd = 0, kGroup = 1, kCollect = 2, kNone = 3 };
 
@@ -347,6 +358,9 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     s.smask[w] = 0u;
   }
   for (int b = tid; b < nb; b += NT) hist[b] = 0ull;
+  if (tid == 0) sh.n_coll = 0;
+  uint64_t *ckey = reinterpret_cast<uint64_t *>(s.area + 8 * (size_t)nb);
+  float *cval = reinterpret_cast<float *>(s.area + 8 * (size_t)nb + 8 * (size_t)a.ccap);
   if (DT == 1) {
     if (tid < 256) {
       const uint32_t v = (uint32_t)tid;
@@ -429,7 +443,10 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   lds_barrier();
 
   // ---- 2. chunks as they land: kill, list, histogram -------------------------
-  float lmax = -INFINITY, ref = 0.0f, cref = 0.0f;
+  float lmax = -INFINITY, ref = 0.0f, cref = 0.0f, thr = INFINITY;
+  // (captured: |score| < 1.0625 * 2^(7 - bin_mant), which covers every bin
+  // that reaches below 2^(7 - bin_mant), bins being narrower than the margin)
+  const float kMultiZone = 1.0625f * __uint_as_float((uint32_t)(127 + 7 - a.bin_mant) << 23);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     if (i + PIPE < R) reg[i + PIPE] = load16(rowp + (int64_t)min(tid + (i + PIPE) * NT, glast) * 16);
@@ -437,11 +454,17 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     uint4 c = launder(reg[i]);
     if (g == NG && tail_n > 0) c = make_uint4(tw[0], tw[1], tw[2], tw[3]);
     if (g < NG || (g == NG && tail_n > 0)) {
-      const uint32_t kb = chunk_bits<DT>(s.kmask, g), sb = chunk_bits<DT>(s.smask, g);
+      // three independent LDS reads: kill bits, the seen-mask word and the
+      // list offset of that word
+      const int wd = (g * EPC) >> 5, sh5 = (g * EPC) & 31;
+      const uint32_t kb = chunk_bits<DT>(s.kmask, g);
+      const uint32_t sword = s.smask[wd];
+      const int wo = (int)woff[wd];
+      const uint32_t sb = (sword >> sh5) & ((1u << EPC) - 1u);
       if (sb) {
         // the chunk's seen ids hold consecutive list slots (the list is in
         // id order); their raw scores go there, the penalty comes later
-        int slot = list_slot(g * EPC + __ffs(sb) - 1, s.smask, woff);
+        int slot = wo + __popc(sword & ((1u << sh5) - 1u));
         uint32_t bits = sb;
         while (bits) {
           const int j = __ffs(bits) - 1;
@@ -461,6 +484,22 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       const float m0 = block_max_f32_lds<NT>(lmax, sh.red_f32);
       ref = m0 == -INFINITY ? 0.0f : m0 + kRefSlack;
       cref = ref * kLog2e;
+      thr = DT == 1 ? -kMultiZone : m0 - kHeadDelta;
+    }
+    {
+      // the head of the row, as it lands
+      uint32_t hb = 0u;
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const float x = E::get(c, j);
+        hb |= ((DT == 1 ? fabsf(x) < kMultiZone : x >= thr) ? 1u : 0u) << j;
+      }
+      while (hb) {
+        const int j = __ffs(hb) - 1;
+        hb &= hb - 1;
+        const int slot = atomicAdd(&sh.n_coll, 1);
+        if (slot < a.ccap) ckey[slot] = sel_key(E::get(c, j), (uint32_t)(g * EPC + j));
+      }
     }
 #pragma unroll
     for (int j = 0; j < EPC; ++j) {
@@ -473,6 +512,10 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     const float y = penalize(s.list_val[k], a.rep);
     s.list_val[k] = y;
     lmax = fmaxf(lmax, y);
+    if (DT == 1 ? fabsf(y) < kMultiZone : y >= thr) {
+      const int slot = atomicAdd(&sh.n_coll, 1);
+      if (slot < a.ccap) ckey[slot] = sel_key(y, (uint32_t)s.list_id[k]);
+    }
     const uint32_t bits = __float_as_uint(mass_of<false>(y, 0.0f, cref));
     atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
   }
@@ -584,8 +627,6 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   __shared__ float gval[kGatherCap];
   uint64_t *okey = reinterpret_cast<uint64_t *>(s.area + 8 * (size_t)nb + 12 * (size_t)a.ccap);
   float *oval = reinterpret_cast<float *>(okey + kGatherCap);
-  uint64_t *ckey = reinterpret_cast<uint64_t *>(s.area + 8 * (size_t)nb);
-  float *cval = reinterpret_cast<float *>(s.area + 8 * (size_t)nb + 8 * (size_t)a.ccap);
 
   // View of bin b (all threads): single-valued test and its list elements,
   // ordered by key into okey / oval.  Returns false when the bin has more
@@ -664,24 +705,34 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   }
   const float bp_v = uni(rs.view.v);  // the boundary bin's value (single-valued bins)
   double target = u * Wp;
-  // The draw's bin: walk bins from shi down (bp counts only its kept part).
+  // The draw's bin: the bin whose cumulative mass interval holds the target
+  // (bp counts only its kept part); every thread checks its own bins.
   auto find_draw_bin = [&]() {
     if (tid == 0) {
-      double C = S_top;
-      int b_s = -1;
-      double before = -1.0;
-      for (int b = shi; b >= slo && b >= 1; --b) {
-        const double mb = (bp >= 0 && b == bp) ? (Wp - C_bp1) : bin_mass(hist[b], b, shift, base);
-        if (mb > 0.0 && C <= target && target < C + mb) { b_s = b; before = C; break; }
-        C += mb;
+      sh.bin_hi = -1;
+      sh.sbase = -1.0;
+    }
+    __syncthreads();
+    {
+      double C = above_me;
+      for (int q = bpt - 1; q >= 0; --q) {
+        const int b = tid * bpt + q;
+        if (b >= nb || b < 1) continue;
+        const double m = (bp >= 0 && b == bp) ? (Wp - C_bp1) : bin_mass(hist[b], b, shift, base);
+        if (m > 0.0 && C <= target && target < C + m) {
+          sh.bin_hi = b;
+          sh.sbase = C;
+        }
+        C += m;
       }
-      if (b_s < 0) { b_s = bp >= 0 ? bp : slo; before = -1.0; }
-      sh.bin_hi = b_s;
-      sh.sbase = before;
     }
     __syncthreads();
     bs = uni(sh.bin_hi);
     bs_start = uni(sh.sbase);
+    if (bs < 0) {  // rounding left the target outside every bin
+      bs = bp >= 0 ? bp : slo;
+      bs_start = -1.0;
+    }
   };
   if (!fallback && cut_kind != kCollect) {
     find_draw_bin();
@@ -732,7 +783,6 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       if (wid < 2 || c_hi1 >= c_lo1) r = bin_floor_key_wave(bsel, nb, shift, base, cref);
       if (lane == 0) gkey[wid] = r;
     }
-    if (tid == 0) sh.n_coll = 0;
     __syncthreads();
   }
   // score limits of the collect intervals (a key of ~0 is +inf)
@@ -746,7 +796,25 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       f1hi = kf(uni((uint32_t)gkey[3]));
     }
   }
+  // Intervals inside the head: their elements are already on chip.
+  const int n_head = uni(sh.n_coll);
+  // (bf16: the head holds every score in (-2, 2); binary32: every score >= thr)
+  auto in_head = [&](float lo, float hi) {
+    return DT == 1 ? (lo >= -kMultiZone && hi <= kMultiZone) : lo >= thr;
+  };
+  const bool from_head = collect && n_head <= a.ccap && in_head(f0lo, f0hi) &&
+                         (c_hi1 < c_lo1 || in_head(f1lo, f1hi));
+  __syncthreads();  // every wave has read the head count before it may be reset
+  if (from_head) {
+    for (int k = tid; k < n_head; k += NT) cval[k] = mass_of<false>(key_score(ckey[k]), 0.0f, cref);
+  } else if (collect) {
+    if (tid == 0) sh.n_coll = 0;
+  }
+  __syncthreads();
+  const bool col_pass = collect && !from_head;
   bool ltie_all = false;
+  uint32_t tmask = 0u;       // chunks of this thread holding list elements of a group
+  float v0 = NAN, v1 = NAN;  // group values (NaN: idle task, no element equals it)
   if (g0 || g1) {
     if (tid == 0) {
       rs.gv[0] = bp_v; rs.gk[0] = g0 ? rs.walk[0].rank + 1 : 0;
@@ -756,73 +824,88 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       rs.ltie = 0;
     }
     __syncthreads();
-    const float v0 = g0 ? uni(rs.gv[0]) : NAN, v1 = g1 ? uni(rs.gv[1]) : NAN;
+    v0 = g0 ? uni(rs.gv[0]) : NAN;
+    v1 = g1 ? uni(rs.gv[1]) : NAN;
     // list elements equal to a group value join the group (rare): only then
     // does the count look them up chunk by chunk
+    // which chunks of which thread hold such a list element: 16 bits per
+    // thread, two threads a word, in the (now idle) ordered-view buffer
+    uint32_t *tiew = reinterpret_cast<uint32_t *>(okey);
+    for (int q = tid; q < NT / 2; q += NT) tiew[q] = 0u;
+    __syncthreads();
     for (int k = tid; k < n_list; k += NT) {
       const float y = s.list_val[k];
-      if (y == v0 || y == v1) rs.ltie = 1;
+      if (y == v0 || y == v1) {
+        rs.ltie = 1;
+        const int gg = s.list_id[k] / EPC, t = gg % NT, ci = gg / NT;
+        atomicOr(&tiew[t >> 1], 1u << ((t & 1) * 16 + ci));
+      }
     }
     __syncthreads();
-    const bool ltie = uni(rs.ltie) != 0;
-    ltie_all = ltie;
-    // members per (wave, chunk index): wave-wide ballots
+    ltie_all = uni(rs.ltie) != 0;
+    tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
+  }
+  // One pass over the registers: members per (wave, chunk index) of the tie
+  // groups by wave-wide ballots, and the elements of the collect intervals
+  // with their keys and masses.
+  auto pass = [&](auto cnt_tag, auto col_tag) {
+    constexpr bool CNT = decltype(cnt_tag)::value, COL = decltype(col_tag)::value;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const uint4 c = launder(reg[i]);
       const int g = tid + i * NT;
       int t0 = 0, t1 = 0;
-#pragma unroll
-      for (int j = 0; j < EPC; ++j) {
-        const float x = E::get(c, j);
-        if (g0) t0 += __popcll(__ballot(x == v0));
-        if (g1) t1 += __popcll(__ballot(x == v1));
-      }
-      if (ltie) {
-        int l0 = 0, l1 = 0;
-        if (g < NG || (g == NG && tail_n > 0)) {
-          uint32_t bits = chunk_bits<DT>(s.smask, g);
-          while (bits) {
-            const int j = __ffs(bits) - 1;
-            bits &= bits - 1;
-            const float y = s.list_val[list_slot(g * EPC + j, s.smask, woff)];
-            l0 += y == v0;
-            l1 += y == v1;
-          }
-        }
-        if (__ballot(l0 != 0) != 0ull) t0 += wave_sum_i32(l0);
-        if (__ballot(l1 != 0) != 0ull) t1 += wave_sum_i32(l1);
-      }
-      if (lane == 0) {
-        rs.wtot[0][wid][i] = t0;
-        rs.wtot[1][wid][i] = t1;
-      }
-    }
-  }
-  if (collect) {
-    // elements of the collect intervals, with their keys and masses
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const uint4 c = launder(reg[i]);
-      const int g = tid + i * NT;
       uint32_t mb = 0u;
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
         const float x = E::get(c, j);
-        const bool m = (x >= f0lo && x < f0hi) || (x >= f1lo && x < f1hi);
-        mb |= (m ? 1u : 0u) << j;
+        if (CNT) {
+          t0 += __popcll(__ballot(x == v0));
+          t1 += __popcll(__ballot(x == v1));
+        }
+        if (COL) mb |= (((x >= f0lo && x < f0hi) || (x >= f1lo && x < f1hi)) ? 1u : 0u) << j;
       }
-      while (mb) {
-        const int j = __ffs(mb) - 1;
-        mb &= mb - 1;
-        const float x = E::get(c, j);
-        const int slot = atomicAdd(&sh.n_coll, 1);
-        if (slot < a.ccap) {
-          ckey[slot] = sel_key(x, (uint32_t)(g * EPC + j));
-          cval[slot] = mass_of<false>(x, 0.0f, cref);
+      if (CNT) {
+        if (ltie_all) {
+          int l0 = 0, l1 = 0;
+          if ((tmask >> i) & 1u) {
+            uint32_t bits = chunk_bits<DT>(s.smask, g);
+            while (bits) {
+              const int j = __ffs(bits) - 1;
+              bits &= bits - 1;
+              const float y = s.list_val[list_slot(g * EPC + j, s.smask, woff)];
+              l0 += y == v0;
+              l1 += y == v1;
+            }
+          }
+          if (__ballot(l0 != 0) != 0ull) t0 += wave_sum_i32(l0);
+          if (__ballot(l1 != 0) != 0ull) t1 += wave_sum_i32(l1);
+        }
+        if (lane == 0) {
+          rs.wtot[0][wid][i] = t0;
+          rs.wtot[1][wid][i] = t1;
+        }
+      }
+      if (COL) {
+        while (mb) {
+          const int j = __ffs(mb) - 1;
+          mb &= mb - 1;
+          const float x = E::get(c, j);
+          const int slot = atomicAdd(&sh.n_coll, 1);
+          if (slot < a.ccap) {
+            ckey[slot] = sel_key(x, (uint32_t)(g * EPC + j));
+            cval[slot] = mass_of<false>(x, 0.0f, cref);
+          }
         }
       }
     }
+  };
+  using T1 = std::integral_constant<bool, true>;
+  using T0 = std::integral_constant<bool, false>;
+  if ((g0 || g1) && col_pass) pass(T1{}, T1{});
+  else if (g0 || g1) pass(T1{}, T0{});
+  else if (col_pass) pass(T0{}, T1{});
+  if (col_pass) {
     for (int k = tid; k < n_list; k += NT) {
       const float y = s.list_val[k];
       if ((y >= f0lo && y < f0hi) || (y >= f1lo && y < f1hi)) {
@@ -876,7 +959,7 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
           uint32_t mbits = 0u;  // members among this lane's elements of chunk ii
 #pragma unroll
           for (int j = 0; j < EPC; ++j) mbits |= (E::get(c, j) == vv ? 1u : 0u) << j;
-          if (ltie_all && (g < NG || (g == NG && tail_n > 0))) {
+          if (ltie_all && ((tmask >> ii) & 1u)) {
             uint32_t bits = chunk_bits<DT>(s.smask, g);
             while (bits) {
               const int j = __ffs(bits) - 1;

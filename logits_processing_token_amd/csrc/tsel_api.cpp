@@ -76,8 +76,13 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
       return 8 * (size_t)nb + 12 * (size_t)ccap + 12 * (size_t)tsel::kGatherCap;
     };
     area = need();
+    // the resident kernel keeps 64 bins per binade as long as it can (finer
+    // bins hold one bf16 value more often); the streamed kernel keeps its
+    // collect buffer
     while ((mant > 3 || ccap > 256) && fixed + area + 8 * lcap > budget) {
-      if (mant > 3) --mant; else ccap /= 2;
+      if (kind == SelectKernel::kRes && ccap > 1024) ccap /= 2;
+      else if (mant > 3) --mant;
+      else ccap /= 2;
       area = need();
     }
   }
