@@ -257,6 +257,28 @@ __device__ __forceinline__ uint4 kill_bits(uint4 c, uint32_t kb, const Lds &s) {
   return c;
 }
 
+// Killed elements of a chunk become -inf; the per-word masks come from the
+// kill bits by bit-field sign extension (no table read: an LDS read here
+// would wait behind the histogram adds of the chunk before).
+template <int DT>
+__device__ __forceinline__ uint4 kill_alu(uint4 c, uint32_t kb) {
+  uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t ninf = Elem<DT>::kNegInf;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m;
+    if (DT == 1) {
+      const uint32_t lo = (uint32_t)((int32_t)(kb << (31 - 2 * q)) >> 31) & 0x0000FFFFu;
+      const uint32_t hi = (uint32_t)((int32_t)(kb << (30 - 2 * q)) >> 31) & 0xFFFF0000u;
+      m = lo | hi;
+    } else {
+      m = (uint32_t)((int32_t)(kb << (31 - q)) >> 31);
+    }
+    w[q] = (m & ninf) | (~m & w[q]);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Element j of a chunk as its raw word bits, for building the tail chunk.
 template <int DT>
 __device__ __forceinline__ void put_elem(uint32_t *w, int j, uint32_t bits) {
@@ -447,38 +469,33 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   // (captured: |score| < 1.0625 * 2^(7 - bin_mant), which covers every bin
   // that reaches below 2^(7 - bin_mant), bins being narrower than the margin)
   const float kMultiZone = 1.0625f * __uint_as_float((uint32_t)(127 + 7 - a.bin_mant) << 23);
+  // The chunk's kill bits, read one chunk ahead so that the read does not
+  // queue behind the chunk's own histogram adds.  (Seen ids are killed here
+  // too; their scores are gathered onto the list once the row has landed.)
+  auto chunk_kill = [&](int i) {
+    const int g = tid + i * NT;
+    const bool ok = g < NG || (g == NG && tail_n > 0);
+    return chunk_bits<DT>(s.kmask, ok ? g : 0);
+  };
+  uint32_t kb_n = chunk_kill(0);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     if (i + PIPE < R) reg[i + PIPE] = load16(rowp + (int64_t)min(tid + (i + PIPE) * NT, glast) * 16);
     const int g = tid + i * NT;
+    const uint32_t kb = kb_n;
+    if (i + 1 < R) kb_n = chunk_kill(i + 1);
     uint4 c = launder(reg[i]);
     if (g == NG && tail_n > 0) c = make_uint4(tw[0], tw[1], tw[2], tw[3]);
     if (g < NG || (g == NG && tail_n > 0)) {
-      // three independent LDS reads: kill bits, the seen-mask word and the
-      // list offset of that word
-      const int wd = (g * EPC) >> 5, sh5 = (g * EPC) & 31;
-      const uint32_t kb = chunk_bits<DT>(s.kmask, g);
-      const uint32_t sword = s.smask[wd];
-      const int wo = (int)woff[wd];
-      const uint32_t sb = (sword >> sh5) & ((1u << EPC) - 1u);
-      if (sb) {
-        // the chunk's seen ids hold consecutive list slots (the list is in
-        // id order); their raw scores go there, the penalty comes later
-        int slot = wo + __popc(sword & ((1u << sh5) - 1u));
-        uint32_t bits = sb;
-        while (bits) {
-          const int j = __ffs(bits) - 1;
-          bits &= bits - 1;
-          s.list_val[slot++] = E::get(c, j);
-        }
-      }
-      c = kill_bits<DT>(c, kb, s);
+      c = kill_alu<DT>(c, kb);
     } else {
       c = make_uint4(E::kNegInf, E::kNegInf, E::kNegInf, E::kNegInf);
     }
     reg[i] = c;
+    float cmax = E::get(c, 0);
 #pragma unroll
-    for (int j = 0; j < EPC; ++j) lmax = fmaxf(lmax, E::get(c, j));
+    for (int j = 1; j < EPC; ++j) cmax = fmaxf(cmax, E::get(c, j));
+    lmax = fmaxf(lmax, cmax);
     asm volatile("" : "+v"(lmax));  // the running maximum per chunk, not deferred
     if (i == 0) {
       const float m0 = block_max_f32_lds<NT>(lmax, sh.red_f32);
@@ -486,19 +503,22 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       cref = ref * kLog2e;
       thr = DT == 1 ? -kMultiZone : m0 - kHeadDelta;
     }
-    {
-      // the head of the row, as it lands
+    if (DT == 1 ? cmax > -kMultiZone : cmax >= thr) {
+      // the head of the row, as it lands (a chunk whose maximum is below it
+      // holds none)
       uint32_t hb = 0u;
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
         const float x = E::get(c, j);
         hb |= ((DT == 1 ? fabsf(x) < kMultiZone : x >= thr) ? 1u : 0u) << j;
       }
-      while (hb) {
-        const int j = __ffs(hb) - 1;
-        hb &= hb - 1;
-        const int slot = atomicAdd(&sh.n_coll, 1);
-        if (slot < a.ccap) ckey[slot] = sel_key(E::get(c, j), (uint32_t)(g * EPC + j));
+      if (hb) {
+#pragma unroll
+        for (int j = 0; j < EPC; ++j)
+          if ((hb >> j) & 1u) {
+            const int slot = atomicAdd(&sh.n_coll, 1);
+            if (slot < a.ccap) ckey[slot] = sel_key(E::get(c, j), (uint32_t)(g * EPC + j));
+          }
       }
     }
 #pragma unroll
@@ -507,9 +527,9 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
     }
   }
-  __syncthreads();  // the row has landed; the list holds the raw scores
+  __syncthreads();  // the row has landed (in the caches too)
   for (int k = tid; k < n_list; k += NT) {
-    const float y = penalize(s.list_val[k], a.rep);
+    const float y = penalize(E::load1(rowp, s.list_id[k]), a.rep);
     s.list_val[k] = y;
     lmax = fmaxf(lmax, y);
     if (DT == 1 ? fabsf(y) < kMultiZone : y >= thr) {
@@ -887,15 +907,17 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
         }
       }
       if (COL) {
-        while (mb) {
-          const int j = __ffs(mb) - 1;
-          mb &= mb - 1;
-          const float x = E::get(c, j);
-          const int slot = atomicAdd(&sh.n_coll, 1);
-          if (slot < a.ccap) {
-            ckey[slot] = sel_key(x, (uint32_t)(g * EPC + j));
-            cval[slot] = mass_of<false>(x, 0.0f, cref);
-          }
+        if (mb) {
+#pragma unroll
+          for (int j = 0; j < EPC; ++j)
+            if ((mb >> j) & 1u) {
+              const float x = E::get(c, j);
+              const int slot = atomicAdd(&sh.n_coll, 1);
+              if (slot < a.ccap) {
+                ckey[slot] = sel_key(x, (uint32_t)(g * EPC + j));
+                cval[slot] = mass_of<false>(x, 0.0f, cref);
+              }
+            }
         }
       }
     }
@@ -952,13 +974,18 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
         if (wid == rs.gw[t]) {
           const int g = tid + ii * NT;
           const float vv = rs.gv[t];
-          uint4 c = reg[0];
+          // members among this lane's elements of chunk ii (every chunk is
+          // tested with a constant index: selecting reg[ii] would become a
+          // run-time index and send the whole row through scratch memory)
+          uint32_t mbits = 0u;
 #pragma unroll
-          for (int i = 1; i < R; ++i)
-            if (i == ii) c = reg[i];
-          uint32_t mbits = 0u;  // members among this lane's elements of chunk ii
+          for (int i = 0; i < R; ++i) {
+            const uint4 c = launder(reg[i]);
+            uint32_t b = 0u;
 #pragma unroll
-          for (int j = 0; j < EPC; ++j) mbits |= (E::get(c, j) == vv ? 1u : 0u) << j;
+            for (int j = 0; j < EPC; ++j) b |= (E::get(c, j) == vv ? 1u : 0u) << j;
+            mbits = i == ii ? b : mbits;
+          }
           if (ltie_all && ((tmask >> ii) & 1u)) {
             uint32_t bits = chunk_bits<DT>(s.smask, g);
             while (bits) {
