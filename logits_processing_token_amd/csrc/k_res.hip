@@ -47,6 +47,7 @@ constexpr int kMpt = 4;   // kill-mask words per thread: V <= 32 * kMpt * NT
 // binary32 row, the scores within kHeadDelta nats of the first chunks'
 // maximum.
 constexpr float kHeadDelta = 3.0f;
+constexpr int kHeadCap = 512;  // head elements kept on chip
 
 enum : int { kFail = -1, kInd = 0, kGroup = 1, kCollect = 2, kNone = 3 };
 
@@ -246,17 +247,6 @@ __device__ __forceinline__ uint4 launder(uint4 c) {
   return c;
 }
 
-template <int DT>
-__device__ __forceinline__ uint4 kill_bits(uint4 c, uint32_t kb, const Lds &s) {
-  const uint4 m = s.lut[kb];
-  const uint32_t ninf = Elem<DT>::kNegInf;
-  c.x = (m.x & ninf) | (~m.x & c.x);
-  c.y = (m.y & ninf) | (~m.y & c.y);
-  c.z = (m.z & ninf) | (~m.z & c.z);
-  c.w = (m.w & ninf) | (~m.w & c.w);
-  return c;
-}
-
 // Killed elements of a chunk become -inf; the per-word masks come from the
 // kill bits by bit-field sign extension (no table read: an LDS read here
 // would wait behind the histogram adds of the chunk before).
@@ -381,23 +371,19 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   }
   for (int b = tid; b < nb; b += NT) hist[b] = 0ull;
   if (tid == 0) sh.n_coll = 0;
-  uint64_t *ckey = reinterpret_cast<uint64_t *>(s.area + 8 * (size_t)nb);
-  float *cval = reinterpret_cast<float *>(s.area + 8 * (size_t)nb + 8 * (size_t)a.ccap);
-  if (DT == 1) {
-    if (tid < 256) {
-      const uint32_t v = (uint32_t)tid;
-      uint32_t m[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        m[j] = (((v >> (2 * j)) & 1u) ? 0x0000FFFFu : 0u) |
-               (((v >> (2 * j + 1)) & 1u) ? 0xFFFF0000u : 0u);
-      s.lut[tid] = make_uint4(m[0], m[1], m[2], m[3]);
-    }
-  } else if (tid < 16) {
-    const uint32_t v = (uint32_t)tid;
-    s.lut[tid] = make_uint4((v & 1u) ? ~0u : 0u, (v & 2u) ? ~0u : 0u, (v & 4u) ? ~0u : 0u,
-                            (v & 8u) ? ~0u : 0u);
-  }
+  // Two copies of the histogram, lanes of odd index adding to the second
+  // (half the same-address collisions of one instruction); the second copy
+  // starts 8 bytes further on so that the copies of a bin fall on different
+  // banks.  After the row it is folded into the first and its space holds
+  // the collect buffer.  Then the head buffer and the ordered sub-bin.
+  uint64_t *hist2 = hist + nb + 1;
+  uint64_t *hkey = reinterpret_cast<uint64_t *>(s.area + 16 * (size_t)nb + 16);
+  float *hval = reinterpret_cast<float *>(hkey + kHeadCap);
+  uint64_t *okey = reinterpret_cast<uint64_t *>(hval + kHeadCap);
+  float *oval = reinterpret_cast<float *>(okey + kGatherCap);
+  uint64_t *ckey = hist2;
+  float *cval = reinterpret_cast<float *>(hist2 + a.ccap);
+  for (int b = tid; b < nb; b += NT) hist2[b] = 0ull;
   lds_barrier();
 #pragma unroll
   for (int k = 0; k < kHpt; ++k) {
@@ -517,14 +503,15 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
         for (int j = 0; j < EPC; ++j)
           if ((hb >> j) & 1u) {
             const int slot = atomicAdd(&sh.n_coll, 1);
-            if (slot < a.ccap) ckey[slot] = sel_key(E::get(c, j), (uint32_t)(g * EPC + j));
+            if (slot < kHeadCap) hkey[slot] = sel_key(E::get(c, j), (uint32_t)(g * EPC + j));
           }
       }
     }
+    uint64_t *hh = (lane & 1) ? hist2 : hist;
 #pragma unroll
     for (int j = 0; j < EPC; ++j) {
       const uint32_t bits = __float_as_uint(mass_of<false>(E::get(c, j), 0.0f, cref));
-      atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
+      atomicAdd(&hh[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
     }
   }
   __syncthreads();  // the row has landed (in the caches too)
@@ -534,7 +521,7 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     lmax = fmaxf(lmax, y);
     if (DT == 1 ? fabsf(y) < kMultiZone : y >= thr) {
       const int slot = atomicAdd(&sh.n_coll, 1);
-      if (slot < a.ccap) ckey[slot] = sel_key(y, (uint32_t)s.list_id[k]);
+      if (slot < kHeadCap) hkey[slot] = sel_key(y, (uint32_t)s.list_id[k]);
     }
     const uint32_t bits = __float_as_uint(mass_of<false>(y, 0.0f, cref));
     atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
@@ -556,7 +543,7 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     ref = mx;
     cref = ref * kLog2e;
     __syncthreads();
-    for (int b = tid; b < nb; b += NT) hist[b] = 0ull;
+    for (int b = tid; b < nb; b += NT) hist[b] = hist2[b] = 0ull;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -572,6 +559,8 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
       atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
     }
   }
+  __syncthreads();
+  for (int b = tid; b < nb; b += NT) hist[b] += hist2[b];  // fold the second copy in
   __syncthreads();
 
   // ---- 3. cumulative bin masses ------------------------------------------------
@@ -645,8 +634,6 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   // ---- 4. the boundary and the draw ------------------------------------------
   __shared__ uint64_t gkey[kGatherCap];
   __shared__ float gval[kGatherCap];
-  uint64_t *okey = reinterpret_cast<uint64_t *>(s.area + 8 * (size_t)nb + 12 * (size_t)a.ccap);
-  float *oval = reinterpret_cast<float *>(okey + kGatherCap);
 
   // View of bin b (all threads): single-valued test and its list elements,
   // ordered by key into okey / oval.  Returns false when the bin has more
@@ -822,11 +809,13 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   auto in_head = [&](float lo, float hi) {
     return DT == 1 ? (lo >= -kMultiZone && hi <= kMultiZone) : lo >= thr;
   };
-  const bool from_head = collect && n_head <= a.ccap && in_head(f0lo, f0hi) &&
+  const bool from_head = collect && n_head <= kHeadCap && in_head(f0lo, f0hi) &&
                          (c_hi1 < c_lo1 || in_head(f1lo, f1hi));
   __syncthreads();  // every wave has read the head count before it may be reset
   if (from_head) {
-    for (int k = tid; k < n_head; k += NT) cval[k] = mass_of<false>(key_score(ckey[k]), 0.0f, cref);
+    for (int k = tid; k < n_head; k += NT) hval[k] = mass_of<false>(key_score(hkey[k]), 0.0f, cref);
+    ckey = hkey;  // the collected set is the head
+    cval = hval;
   } else if (collect) {
     if (tid == 0) sh.n_coll = 0;
   }

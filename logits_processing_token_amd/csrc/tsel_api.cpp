@@ -50,9 +50,12 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   const int32_t mw = (V + 31) / 32;
   const size_t mask_bytes = align16((size_t)mw * 4);
   const size_t base = 2 * mask_bytes;
-  const size_t lut = (p->dtype == TSEL_BF16 ? 256 : 16) * 16;
+  // the kill table (8 or 4 kill bits -> per-word masks); the resident kernel
+  // builds its masks with ALU operations and keeps a list offset per mask
+  // word instead
+  const size_t lut = kind == SelectKernel::kRes ? 0 : (size_t)(p->dtype == TSEL_BF16 ? 256 : 16) * 16;
   const size_t radix = 1024;
-  const size_t woff = kind == SelectKernel::kRes ? align16(2 * (size_t)mw) : 0;  // list offset per mask word
+  const size_t woff = kind == SelectKernel::kRes ? align16(2 * (size_t)mw) : 0;
   const size_t budget = (size_t)tsel::kSelectMaxDynLds;
   const size_t fixed = base + lut + radix + woff;
   const size_t min_list = 8 * 64;
@@ -67,7 +70,21 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
     tcap = 2048;
     while (tcap > 256 && fixed + 24 * (size_t)tcap + 8 * lcap > budget) tcap /= 2;
     area = 24 * (size_t)tcap;
-  } else if (kind == SelectKernel::kFull || kind == SelectKernel::kRes) {
+  } else if (kind == SelectKernel::kRes) {
+    // two histogram copies (the second, after folding, holds the collect
+    // buffer), the head buffer (512 keys and masses), the ordered sub-bin
+    mant = 6;
+    auto need = [&]() {
+      nb = (tsel::kBinBelow + tsel::kBinAbove) << mant;
+      ccap = (int32_t)std::min<size_t>(4096, (8 * (size_t)nb) / 12);
+      return 16 * (size_t)nb + 16 + 12 * 512 + 12 * (size_t)tsel::kGatherCap;
+    };
+    area = need();
+    while (mant > 3 && fixed + area + 8 * lcap > budget) {
+      --mant;
+      area = need();
+    }
+  } else if (kind == SelectKernel::kFull) {
     mant = 6;
     ccap = 4096;
     auto need = [&]() {
@@ -76,13 +93,8 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
       return 8 * (size_t)nb + 12 * (size_t)ccap + 12 * (size_t)tsel::kGatherCap;
     };
     area = need();
-    // the resident kernel keeps 64 bins per binade as long as it can (finer
-    // bins hold one bf16 value more often); the streamed kernel keeps its
-    // collect buffer
     while ((mant > 3 || ccap > 256) && fixed + area + 8 * lcap > budget) {
-      if (kind == SelectKernel::kRes && ccap > 1024) ccap /= 2;
-      else if (mant > 3) --mant;
-      else ccap /= 2;
+      if (mant > 3) --mant; else ccap /= 2;
       area = need();
     }
   }
