@@ -30,14 +30,12 @@
 
 #include <type_traits>
 
-#include "k_mass.hpp"
+#include "k_res_common.hpp"
 
 namespace tsel {
 namespace {
 
-constexpr int kPipe = 8;  // 16-byte chunks in flight per lane
-constexpr int kHpt = 4;   // history ids per thread held in registers
-constexpr int kMpt = 4;   // kill-mask words per thread: V <= 32 * kMpt * NT
+using namespace res;
 // Elements that may share a mass bin with another value are kept on chip
 // as they land, so that such a bin is ordered from that buffer without
 // another pass over the row.  In a bf16 row these are the scores below
@@ -48,29 +46,6 @@ constexpr int kMpt = 4;   // kill-mask words per thread: V <= 32 * kMpt * NT
 // maximum.
 constexpr float kHeadDelta = 3.0f;
 constexpr int kHeadCap = 512;  // head elements kept on chip
-
-enum : int { kFail = -1, kInd = 0, kGroup = 1, kCollect = 2, kNone = 3 };
-
-// Order of a single-valued bin: list elements above the value, the tie
-// group (dense elements of the value and list elements equal to it, in id
-// order), list elements below the value.  Positions are linear in that
-// order.
-struct BinView {
-  int single;        // the bin's dense elements all hold one value
-  float v;           // that value
-  float e;           // its mass
-  int n_ind;         // list elements of the bin not equal to v (sorted, okey / oval)
-  int n_above;       // of them, above v
-  int n_group;       // members of the tie group
-};
-
-struct WalkResult {
-  int kind;          // kInd, kGroup or kFail
-  uint64_t key;      // kInd: the element's key
-  int rank;          // kGroup: 0-based rank in the group
-  int pos;           // linear position in the bin
-  double acc;        // cut: mass through the last kept element
-};
 
 struct ResShared {
   BinView view;
@@ -161,92 +136,6 @@ __device__ __forceinline__ int bf16_values_in(uint32_t klo, uint32_t khi, float 
   return ordered_f32(v2) >= khi ? 1 : 2;
 }
 
-// Walk of a single-valued bin (thread 0).  cut: the last element kept by
-// top_p (the first element whose mass before it is >= goal and everything
-// after it are removed); draw: the first element whose mass through it
-// exceeds goal, among positions <= pos_lim.
-__device__ WalkResult single_walk(bool cut, double start, double goal, const BinView &bv,
-                                  const uint64_t *okey, const float *oval, int pos_lim) {
-  WalkResult r;
-  r.kind = kFail;
-  r.key = 0ull;
-  r.rank = -1;
-  r.pos = -1;
-  double A = start;
-  const double e = (double)bv.e;
-  const int na = bv.n_above, ni = bv.n_ind, ng = bv.n_group;
-  if (cut) {
-    for (int q = 0; q < na; ++q) {
-      if (A >= goal) { r.acc = A; return r; }
-      A += (double)oval[q];
-      r.kind = kInd; r.key = okey[q]; r.pos = q;
-    }
-    if (ng > 0) {
-      if (A >= goal) { r.acc = A; return r; }
-      // first member j with A + j e >= goal; j >= 1 since A < goal
-      const double q = (goal - A) / e;  // finite and <= ng + a rounding in any bin
-      long long j = q < (double)ng ? (long long)ceil(q) : (long long)ng;
-      if (j < 1) j = 1;
-      while (j > 1 && A + (double)(j - 1) * e >= goal) --j;
-      while (j < ng && A + (double)j * e < goal) ++j;
-      if (j < ng) {
-        r.kind = kGroup; r.rank = (int)j - 1; r.pos = na + (int)j - 1;
-        r.acc = A + (double)j * e;
-        return r;
-      }
-      A += (double)ng * e;
-      r.kind = kGroup; r.rank = ng - 1; r.pos = na + ng - 1;
-    }
-    for (int q = na; q < ni; ++q) {
-      if (A >= goal) { r.acc = A; return r; }
-      A += (double)oval[q];
-      r.kind = kInd; r.key = okey[q]; r.pos = ng + q;
-    }
-    r.acc = A;
-    return r;
-  }
-  // draw
-  WalkResult last;
-  last.kind = kFail;
-  for (int q = 0; q < na && q <= pos_lim; ++q) {
-    A += (double)oval[q];
-    last.kind = kInd; last.key = okey[q]; last.pos = q;
-    if (A > goal) return last;
-  }
-  const int n_eff = pos_lim - na >= ng ? ng : pos_lim - na + 1;  // (no overflow at INT_MAX)
-  if (n_eff > 0) {
-    const double q = (goal - A) / e;
-    long long j = q < (double)n_eff ? (long long)floor(q) : (long long)(n_eff - 1);
-    if (j < 0) j = 0;
-    while (j > 0 && A + (double)j * e > goal) --j;
-    while (j < n_eff - 1 && A + (double)(j + 1) * e <= goal) ++j;
-    last.kind = kGroup; last.rank = (int)j; last.pos = na + (int)j;
-    if (A + (double)(j + 1) * e > goal) return last;
-    A += (double)n_eff * e;
-    last.rank = n_eff - 1; last.pos = na + n_eff - 1;
-  }
-  for (int q = na; q < ni && ng + q <= pos_lim; ++q) {
-    A += (double)oval[q];
-    last.kind = kInd; last.key = okey[q]; last.pos = ng + q;
-    if (A > goal) return last;
-  }
-  return last;  // rounding at the end: the last element within the limit
-}
-
-// Slot on the list of seen id v (alive seen ids are listed in id order;
-// woff[w] is the list offset of mask word w).
-__device__ __forceinline__ int list_slot(int v, const uint32_t *amask, const uint16_t *woff) {
-  const int w = v >> 5;
-  return (int)woff[w] + __popc(amask[w] & ((1u << (v & 31)) - 1u));
-}
-
-// Hides a chunk's value from the optimizer, so that the elements unpacked
-// from it are not computed early and kept live (which spills).
-__device__ __forceinline__ uint4 launder(uint4 c) {
-  asm volatile("" : "+v"(c.x), "+v"(c.y), "+v"(c.z), "+v"(c.w));
-  return c;
-}
-
 // Killed elements of a chunk become -inf; the per-word masks come from the
 // kill bits by bit-field sign extension (no table read: an LDS read here
 // would wait behind the histogram adds of the chunk before).
@@ -269,37 +158,6 @@ __device__ __forceinline__ uint4 kill_alu(uint4 c, uint32_t kb) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Element j of a chunk as its raw word bits, for building the tail chunk.
-template <int DT>
-__device__ __forceinline__ void put_elem(uint32_t *w, int j, uint32_t bits) {
-  if (DT == 1) {
-    const int q = j >> 1;
-    w[q] = (j & 1) ? ((w[q] & 0x0000FFFFu) | (bits << 16)) : ((w[q] & 0xFFFF0000u) | bits);
-  } else {
-    w[j] = bits;
-  }
-}
-
-// Final scores of a sampled row (kept: score >= t_y and key >= kcut, else
-// -inf), one element per thread and step from memory; seen ids take their
-// penalized score from the list.
-template <int DT>
-__device__ __forceinline__ void res_processed(const SelectArgs &a, int row, const Lds &s,
-                                              float t_y, uint64_t kcut, int n_list) {
-  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
-  float *outp = a.out_processed + (int64_t)row * a.V;
-  visit_plain<DT>(a, rowp, s, [&](int v, float y) {
-    outp[v] = (y > -INFINITY && y >= t_y && sel_key(y, (uint32_t)v) >= kcut) ? y : -INFINITY;
-  });
-  for (int v = threadIdx.x; v < a.V; v += NT)
-    if (bit_of(s.kmask, v)) outp[v] = -INFINITY;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n_list; i += NT) {
-    const float y = s.list_val[i];
-    outp[s.list_id[i]] = (y >= t_y && sel_key(y, (uint32_t)s.list_id[i]) >= kcut) ? y : -INFINITY;
-  }
-}
-
 }  // namespace
 
 template <int DT, int R>
@@ -316,48 +174,18 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   const int lane = tid & (kWave - 1), wid = tid / kWave;
   const int NG = V / EPC;  // whole chunks (>= 1 on this path)
   const int glast = NG - 1;
-  const int mw = a.mw;
   const char *rowp = a.logits + (int64_t)row * a.row_bytes;
-  RowInfo ri;
-  if (row_prologue(a, row, ri)) return;
-  const int L = ri.L;
-  const int32_t *h = a.hist + (int64_t)row * a.hist_stride;
-
-  // ---- 0. small loads first, then the row ----------------------------------
-  int hreg[kHpt];
-#pragma unroll
-  for (int k = 0; k < kHpt; ++k) hreg[k] = h[min(tid + k * NT, L - 1)];
-  // (every load here is unconditional and in bounds: an absent mask reads
-  // word 0 of the lengths and discards it, so that no branch splits the
-  // loads and the row's chunks below can be waited for one at a time)
-  const uint32_t *lens_u = reinterpret_cast<const uint32_t *>(a.lens);
-  const uint32_t *m0p = a.bad_mask ? a.bad_mask : lens_u;
-  const uint32_t *m1p = a.sup_mask ? a.sup_mask : lens_u;
-  const uint32_t *m2p = ri.begin_active ? a.begin_mask : lens_u;
-  const uint32_t m0k = a.bad_mask ? ~0u : 0u, m1k = a.sup_mask ? ~0u : 0u;
-  const uint32_t m2k = ri.begin_active ? ~0u : 0u;
-  uint32_t km[kMpt];
-#pragma unroll
-  for (int q = 0; q < kMpt; ++q) {
-    const int w = min(tid * kMpt + q, mw - 1);
-    km[q] = (m0p[m0k ? w : 0] & m0k) | (m1p[m1k ? w : 0] & m1k) | (m2p[m2k ? w : 0] & m2k);
-  }
-  // the tail (V % EPC ids after the last whole chunk) as one more chunk:
-  // every lane loads the same few elements (in bounds, unconditionally, so
-  // that the loads of the row below can be waited for one by one)
+  // ---- 0. small loads first, then the row (none waits for another) -------
+  Early ea;
+  early_loads<DT>(a, row, rowp, ea);
   const int tail_n = V - NG * EPC;
-  uint32_t tw[4] = {E::kNegInf, E::kNegInf, E::kNegInf, E::kNegInf};
-#pragma unroll
-  for (int j = 0; j < EPC - 1; ++j) {
-    const int v = min(NG * EPC + j, V - 1);
-    const uint32_t bits = DT == 1 ? (uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v]
-                                  : reinterpret_cast<const uint32_t *>(rowp)[v];
-    const uint32_t ninf = DT == 1 ? 0xFF80u : 0xFF800000u;
-    put_elem<DT>(tw, j, j < tail_n ? bits : ninf);
-  }
+  const uint32_t *tw = ea.tw;
   uint4 reg[R];
 #pragma unroll
   for (int i = 0; i < PIPE; ++i) reg[i] = load16(rowp + (int64_t)min(tid + i * NT, glast) * 16);
+  RowInfo ri;
+  if (row_prologue(a, row, ri)) return;
+  const int32_t *h = a.hist + (int64_t)row * a.hist_stride;
 
   // ---- 1. staging: masks, list, table (LDS only) ----------------------------
   uint64_t *hist = reinterpret_cast<uint64_t *>(s.area);
@@ -365,12 +193,6 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   const int shift = 23 - a.bin_mant;
   const int base = (127 - kBinBelow) << a.bin_mant;
   const uint32_t lowmask = (1u << shift) - 1u;
-  for (int w = tid; w < mw; w += NT) {
-    s.kmask[w] = 0u;
-    s.smask[w] = 0u;
-  }
-  for (int b = tid; b < nb; b += NT) hist[b] = 0ull;
-  if (tid == 0) sh.n_coll = 0;
   // Two copies of the histogram, lanes of odd index adding to the second
   // (half the same-address collisions of one instruction); the second copy
   // starts 8 bytes further on so that the copies of a bin fall on different
@@ -383,72 +205,11 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   float *oval = reinterpret_cast<float *>(okey + kGatherCap);
   uint64_t *ckey = hist2;
   float *cval = reinterpret_cast<float *>(hist2 + a.ccap);
+  stage_clear(s, sh, a.mw, 4 * a.mw, a.mw);
+  for (int b = tid; b < nb; b += NT) hist[b] = 0ull;
   for (int b = tid; b < nb; b += NT) hist2[b] = 0ull;
-  lds_barrier();
-#pragma unroll
-  for (int k = 0; k < kHpt; ++k) {
-    const int v = hreg[k];
-    if (tid + k * NT < L && v >= 0 && v < V) atomicOr(&s.smask[v >> 5], 1u << (v & 31));
-  }
-  for (int i = kHpt * NT + tid; i < L; i += NT) {  // long histories
-    const int v = h[i];
-    if (v >= 0 && v < V) atomicOr(&s.smask[v >> 5], 1u << (v & 31));
-  }
-  const int n = a.ngram;
-  if (n > 0 && L >= n) {
-    // Window i bans its last id when its first n-1 ids equal the last n-1
-    // ids of the history ("Lengths", no_repeat_ngram_size).
-    const int32_t *tl = h + (L - n + 1);
-    for (int i = tid; i + n <= L; i += NT) {
-      bool match = true;
-      for (int j = 0; j < n - 1; ++j)
-        if (h[i + j] != tl[j]) { match = false; break; }
-      const int t = h[i + n - 1];
-      if (match && t >= 0 && t < V) atomicOr(&s.kmask[t >> 5], 1u << (t & 31));
-    }
-  }
-  const bool minlen_active = a.min_new > 0 ? (ri.new_tokens < a.min_new)
-                                           : (a.min_length > 0 && L < a.min_length);
-  if (minlen_active && tid < a.n_eos) {
-    const int e = a.eos[tid];
-    if (e >= 0 && e < V) atomicOr(&s.kmask[e >> 5], 1u << (e & 31));
-  }
-  lds_barrier();
-  // kmask <- removed from the registers (killed or seen); smask <- alive seen
-  uint32_t aq[kMpt];
-  int my_cnt = 0;
-#pragma unroll
-  for (int q = 0; q < kMpt; ++q) {
-    const int w = tid * kMpt + q;
-    aq[q] = 0u;
-    if (w < mw) {
-      const uint32_t K = s.kmask[w] | km[q], S = s.smask[w];
-      aq[q] = S & ~K;
-      s.kmask[w] = K | S;
-      s.smask[w] = aq[q];
-      my_cnt += __popc(aq[q]);
-    }
-  }
-  int n_list = 0;
-  const int my_off = block_excl_scan_i32<NT, true>(my_cnt, sh.red_i32, &n_list);
-  if (n_list > a.lcap) {  // too many seen ids for the list: the streamed path decides
-    if (tid == 0) a.out_tokens[row] = kPending;
-    return;
-  }
-  {
-    int o = my_off;
-#pragma unroll
-    for (int q = 0; q < kMpt; ++q) {
-      if (tid * kMpt + q < mw) woff[tid * kMpt + q] = (uint16_t)o;
-      uint32_t bits = aq[q];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        s.list_id[o++] = (tid * kMpt + q) * 32 + b;
-      }
-    }
-  }
-  lds_barrier();
+  const int n_list = stage(a, row, ri, s, sh, h, ea, woff);
+  if (n_list < 0) return;
 
   // ---- 2. chunks as they land: kill, list, histogram -------------------------
   float lmax = -INFINITY, ref = 0.0f, cref = 0.0f, thr = INFINITY;

@@ -80,7 +80,7 @@ struct Lds {
 
 __device__ __forceinline__ Lds carve(const SelectArgs &a, unsigned char *smem) {
   Lds s;
-  s.kmask = reinterpret_cast<uint32_t *>(smem);
+  s.kmask = reinterpret_cast<uint32_t *>(smem + a.off_kmask);
   s.smask = reinterpret_cast<uint32_t *>(smem + a.off_smask);
   s.list_id = reinterpret_cast<int32_t *>(smem + a.off_list_id);
   s.list_val = reinterpret_cast<float *>(smem + a.off_list_val);
@@ -188,12 +188,27 @@ struct RowInfo {
   bool begin_active;
 };
 
-__device__ __forceinline__ bool row_prologue(const SelectArgs &a, int row, RowInfo &ri) {
-  const int tid = threadIdx.x;
-  const int V = a.V;
+// The row's lengths (history, prompt, max_length), read on their own so
+// that a kernel can start these loads before any other.
+__device__ __forceinline__ void row_lens(const SelectArgs &a, int row, RowInfo &ri) {
   ri.L = a.lens[row];
   ri.P = a.lens[a.B + row];
   ri.M = a.lens[2 * a.B + row];
+}
+
+// The same through vector loads, which are counted in issue order with the
+// row's own, so that they are not pushed behind them; the values end in
+// scalar registers.
+__device__ __forceinline__ void row_lens_vector(const SelectArgs &a, int row, RowInfo &ri) {
+  ri.L = __builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(a.lens + row));
+  ri.P = __builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(a.lens + a.B + row));
+  ri.M = __builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(a.lens + 2 * a.B + row));
+}
+
+// The prologue once row_lens has run.
+__device__ __forceinline__ bool row_prologue_after_lens(const SelectArgs &a, int row, RowInfo &ri) {
+  const int tid = threadIdx.x;
+  const int V = a.V;
   ri.new_tokens = ri.L - ri.P;
   ri.begin_active =
       a.begin_mask != nullptr && ri.new_tokens == ((a.forced_bos >= 0 && ri.P == 1) ? 1 : 0);
@@ -217,6 +232,11 @@ __device__ __forceinline__ bool row_prologue(const SelectArgs &a, int row, RowIn
     return true;
   }
   return false;
+}
+
+__device__ __forceinline__ bool row_prologue(const SelectArgs &a, int row, RowInfo &ri) {
+  row_lens(a, row, ri);
+  return row_prologue_after_lens(a, row, ri);
 }
 
 // Staging of one row (see the file comment).  Leaves in LDS: the kill mask

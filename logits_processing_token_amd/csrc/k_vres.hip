@@ -1,0 +1,897 @@
+// k_vres.hip -- sampling without top_k at temperature 1 over a bf16 row held
+// in registers, with one histogram bin per bf16 value, for gfx950.
+//
+// One 1024-thread workgroup per row; the row (up to 16 chunks of 16 bytes per
+// lane) arrives with eight chunks in flight per lane while the history and
+// the masks are staged in LDS.  Each landed chunk loses its removed ids
+// (-inf) and is counted into a histogram whose bins are the bf16 values
+// themselves: a score's bin is its ordered 16-bit pattern less an offset,
+// worked out two scores at a time with packed 16-bit integer operations, so
+// that the row costs no exponential and no float arithmetic per element.
+// Lanes add into four copies of the histogram (fewer same-address
+// collisions per instruction), folded once the row has landed.
+//
+//  * Bins start kDropNats below the maximum of every lane's first chunk:
+//    lower scores weigh less than e^-kDropNats of the maximum each and count
+//    for nothing.  Near zero the bf16 values are too dense for a bin each:
+//    the scores of magnitude below 2^-kZoneExp share one bin, whose members
+//    are listed one by one when it is not empty.
+//  * Every other bin holds equal scores: its mass is its count times one
+//    exponential, and its members tie, in id order.
+//  * Individuals -- the seen ids with their penalized scores (any binary32
+//    value) and the listed near-zero members -- each join the bin of the
+//    largest bf16 value not above them and add their own mass there, as an
+//    exact fixed-point sum.
+//
+// Cumulative bin masses then name the bin of the top_p boundary and the bin
+// of the draw.  Inside a bin the order is: individuals above the bin's value
+// (ordered on chip), the tie group (the bin's count plus the individuals
+// equal to the value), individuals below it; a boundary or draw inside the
+// group follows by arithmetic on the equal masses, and one pass over the
+// registers counts the group's members in id order to name the id.  What
+// fits none of this falls back to a bisection over selection keys that
+// re-reads the row.
+//
+// Sources: "Transmuter.Generation (transmuter v2.0.0)", module doc (the
+// processors and warpers, in order; temperature, top_k and top_p are the
+// sampling warpers) and the inverse-CDF draw of a caller uniform over the
+// kept ids in (score desc, id asc) order.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "k_res_common.hpp"
+
+namespace tsel {
+namespace {
+
+using namespace res;
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Scores as 16-bit keys whose integer order is the score order, with every
+// score of magnitude at most 2^-kZoneExp on one of two keys: 0x7FFF (-0 and
+// the negative ones) and 0x8000 (+0 and the positive ones).  From a bf16
+// pattern u: t = max(|u| - Z, 0) with Z the magnitude bits of 2^-kZoneExp,
+// then 0x8000 + t for a positive u and 0x7FFF - t for a negative one.
+constexpr uint32_t kZoneMag = (uint32_t)(127 - kZoneExp) << 7;
+constexpr uint32_t kKeyZoneNeg = 0x7FFFu, kKeyZonePos = 0x8000u;
+constexpr uint32_t kKeyLowFinite = 0x7FFFu - (0x7F7Fu - kZoneMag);  // key of -max finite
+
+__device__ __forceinline__ uint32_t vkey(uint32_t u) {
+  const uint32_t m = u & 0x7FFFu;
+  const uint32_t t = m > kZoneMag ? m - kZoneMag : 0u;
+  return (u & 0x8000u) ? kKeyZoneNeg - t : kKeyZonePos + t;
+}
+// The bf16 value of a key off the two near-zero keys.
+__device__ __forceinline__ float vkey_value(uint32_t k) {
+  const uint32_t u = k > kKeyZonePos ? k - kKeyZonePos + kZoneMag
+                                     : 0x8000u | (kKeyZoneNeg - k + kZoneMag);
+  return __uint_as_float(u << 16);
+}
+// Key of the largest bf16 value not above y (y not NaN; -0 counts as +0).
+__device__ __forceinline__ uint32_t vkey_floor(float y) {
+  uint32_t u = __float_as_uint(y + 0.0f);
+  if ((u & 0x80000000u) && (u & 0xFFFFu)) u += 0x10000u;  // negative: away from zero
+  return vkey(u >> 16);
+}
+
+// The map from key to bin: bin = min(max(k - bk1, 0), top), bk1 = first
+// binned key - 1 (lower keys land in bin 0, which counts for nothing; keys
+// past the last bin pile up there).  zn, zp: the bins of the two near-zero
+// keys, or -1.
+struct VMap {
+  uint32_t bk1, top;
+  int zn, zp;
+};
+
+__device__ __forceinline__ int vbin(uint32_t k, const VMap &m) {
+  return min(max((int)k - (int)m.bk1, 0), (int)m.top);
+}
+// Key of bin b >= 1.
+__device__ __forceinline__ uint32_t vbin_key(int b, const VMap &m) { return (uint32_t)b + m.bk1; }
+
+// Packed form for the two bf16 scores of one word: the LDS byte addresses of
+// their bins in this lane's histogram copy (lb: the copy's address in both
+// halves; bins * 4 + lb stays below 2^16).  Constants sit in scalar
+// registers (a literal cannot be an operand of the three-operand forms).
+struct VMapP {
+  u16x2 bk1, top;
+  uint32_t lb, c7fff, czm, c8000;
+};
+__device__ __forceinline__ u16x2 vkeys2(uint32_t w, const VMapP &m) {
+  const u16x2 u = __builtin_bit_cast(u16x2, w);
+  const u16x2 t = __builtin_elementwise_sub_sat(u & __builtin_bit_cast(u16x2, m.c7fff),
+                                                __builtin_bit_cast(u16x2, m.czm));
+  const i16x2 sx = __builtin_bit_cast(i16x2, u) >> (i16x2)(int16_t)15;
+  uint32_t k;  // t ^ sx ^ 0x8000 in one three-input operation
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96"
+      : "=v"(k)
+      : "v"(__builtin_bit_cast(uint32_t, t)), "v"(__builtin_bit_cast(uint32_t, sx)), "s"(m.c8000));
+  return __builtin_bit_cast(u16x2, k);
+}
+__device__ __forceinline__ uint32_t vaddr2(uint32_t w, const VMapP &m) {
+  const u16x2 idx =
+      __builtin_elementwise_min(__builtin_elementwise_sub_sat(vkeys2(w, m), m.bk1), m.top);
+  uint32_t a;
+  asm("v_pk_mad_u16 %0, %1, 4, %2 op_sel_hi:[1,0,1]"
+      : "=v"(a)
+      : "v"(__builtin_bit_cast(uint32_t, idx)), "v"(m.lb));
+  return a;
+}
+
+// Removed elements of a chunk (kill bit j for element j) become -inf: for
+// word q, bits 2q and 2q + 1 are shifted to the sign bit of each half and
+// spread over it (two packed shifts, written out so that the compiler keeps
+// them rather than a compare and select per half).
+__device__ __forceinline__ uint4 vkill(uint4 c, uint32_t kb, uint32_t ninf) {
+  const uint32_t kbp = (kb & 0xFFu) | ((kb & 0xFEu) << 15);  // bits 2q | bits 2q + 1 << 16
+  uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m;
+    asm("v_pk_lshlrev_b16 %0, %1, %2 op_sel_hi:[0,1]\n\t"
+        "v_pk_ashrrev_i16 %0, 15, %0 op_sel_hi:[0,1]"
+        : "=&v"(m)
+        : "n"(15 - 2 * q), "v"(kbp));
+    w[q] = (m & ninf) | (~m & w[q]);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// A constant in a scalar register (a literal cannot be an operand of the
+// three-operand bit operations).
+__device__ __forceinline__ uint32_t sconst(uint32_t v) {
+  uint32_t r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+  return r;
+}
+
+// LDS address of a pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void lds_add(uint32_t addr, uint32_t v) {
+  __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t *)(uintptr_t)addr, v,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+struct VShared {
+  BinView view;
+  WalkResult walk[2];
+  float gv[2];
+  int gk[2];
+  int gi[2], gw[2], gr[2];
+  int gid[2];
+  int wtot[2][NW][16];
+  int n_ind_b, n_tie_b;
+  int ltie;
+  int nz;
+  uint32_t kmax[NW];
+};
+
+template <int NT_>
+__device__ __forceinline__ uint32_t block_max_u32_lds(uint32_t v, uint32_t *scratch) {
+  constexpr int NW_ = NT_ / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  if (lane == 0) scratch[wid] = v;
+  lds_barrier();
+  v = lane < NW_ ? scratch[lane] : 0u;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+
+// The map for a first binned key bk (>= the smallest finite key).
+__device__ __forceinline__ VMap make_vmap(uint32_t bk) {
+  VMap m;
+  m.bk1 = bk - 1u;
+  m.top = (uint32_t)(kVBins - 1);
+  const int zn = vbin(kKeyZoneNeg, m), zp = vbin(kKeyZonePos, m);
+  m.zn = zn >= 1 && zn < kVBins - 1 ? zn : -1;
+  m.zp = zp >= 1 && zp < kVBins - 1 ? zp : -1;
+  return m;
+}
+__device__ __forceinline__ VMapP pack_vmap(const VMap &m, uint32_t lb) {
+  VMapP p;
+  p.bk1 = (u16x2)(uint16_t)m.bk1;
+  p.top = (u16x2)(uint16_t)m.top;
+  p.lb = lb | (lb << 16);
+  p.c7fff = sconst(0x7FFF7FFFu);
+  p.czm = sconst(kZoneMag | (kZoneMag << 16));
+  p.c8000 = sconst(0x80008000u);
+  return p;
+}
+
+// First binned key for a maximum of key kmax: kDropNats below it.
+__device__ __forceinline__ uint32_t base_key(uint32_t kmax) {
+  if (kmax < kKeyLowFinite) return kKeyLowFinite;  // no finite score: from the lowest
+  if (kmax == kKeyZoneNeg || kmax == kKeyZonePos) kmax = kKeyZonePos + 1u;  // (an upper bound)
+  return max(vkey_floor(vkey_value(kmax) - kDropNats), kKeyLowFinite);
+}
+
+}  // namespace
+
+static_assert(sizeof(RowShared) <= kVRowSharedBytes, "row scalars");
+static_assert(sizeof(VShared) + kVRowSharedBytes <= kVSharedBytes, "kernel scalars");
+
+template <int R>
+__global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
+  using E = Elem<1>;
+  constexpr int EPC = E::EPC;
+  constexpr int PIPE0 = R < 4 ? R : 4;  // chunks asked for before the staging
+  constexpr int PIPE = R < 4 ? R : 4;  // chunks in flight while counting
+  constexpr int NB = kVBins;
+  constexpr int BPT = (NB + NT - 1) / NT;
+  // (no static LDS: the dynamic block starts at address 0, so histogram
+  // offsets are LDS addresses as they stand)
+  extern __shared__ __align__(16) unsigned char smem[];
+  RowShared &sh = *reinterpret_cast<RowShared *>(smem + a.off_sh);
+  VShared &vs = *reinterpret_cast<VShared *>(smem + a.off_sh + kVRowSharedBytes);
+  const Lds s = carve(a, smem);
+  uint16_t *woff = reinterpret_cast<uint16_t *>(smem + a.off_woff);
+  const int tid = threadIdx.x, row = blockIdx.x, V = a.V;
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const int NG = V / EPC;  // whole chunks (>= 1 on this path)
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  // ---- 0. the small loads: lengths, history, masks, tail --------------------
+  RowInfo ri;
+  row_lens_vector(a, row, ri);
+  Early ea;
+  early_loads<1>(a, row, rowp, ea);
+  const int tail_n = V - NG * EPC;
+
+  // ---- 1. staging: masks and list (LDS only) --------------------------------
+  // LDS from byte 0: four histogram copies (u32 counts, kVStride words
+  // apart); after the fold, copy 0 keeps the counts and the space of the
+  // others holds the per-bin masses and the ordered view of one bin.
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(smem);
+  double *bmass = reinterpret_cast<double *>(smem + kVMassOff);
+  uint64_t *lfix = reinterpret_cast<uint64_t *>(smem + kVMassOff);
+  uint64_t *okey = reinterpret_cast<uint64_t *>(smem + kVViewOff);
+  float *oval = reinterpret_cast<float *>(okey + kGatherCap);
+  uint64_t *gkey = reinterpret_cast<uint64_t *>(oval + kGatherCap);
+  float *gval = reinterpret_cast<float *>(gkey + kGatherCap);
+  // While the small loads fly: clear the histogram and the masks.  Both
+  // masks run on to byte R * NT (one byte per chunk slot of the registers),
+  // the kill mask with every slot past the row's ids marked removed, so that
+  // chunk i's bytes sit at fixed offsets.
+  {
+    uint4 *c4 = reinterpret_cast<uint4 *>(cnt);
+    for (int b = tid; b < kVCopies * kVStride / 4; b += NT) c4[b] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  stage_clear(s, sh, R * NT / 4, (V + EPC - 1) / EPC, R * NT / 4);
+  // The row through a buffer resource (one offset register per lane, the
+  // chunk's offset in a scalar; chunks past the row read as 0): its first
+  // chunks are asked for now, the others as the chunks are counted.
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, NG * 16, 0x00020000);
+  auto load_chunk = [&](int i) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, tid * 16, i * NT * 16, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
+  uint4 reg[R];
+#pragma unroll
+  for (int i = 0; i < PIPE0; ++i) reg[i] = load_chunk(i);
+  if (row_prologue_after_lens(a, row, ri)) return;
+  if (lds_addr(smem) + kVHistBytes > 65536) {  // (not with this block's layout)
+    if (tid == 0) a.out_tokens[row] = kPending;
+    return;
+  }
+  const int32_t *h = a.hist + (int64_t)row * a.hist_stride;
+  const int n_list = uni(stage(a, row, ri, s, sh, h, ea, woff));
+  if (n_list < 0) return;
+
+  // The seen ids' scores are gathered chunk index by chunk index, each right
+  // after its chunk was asked for, so that they read the lines that chunk
+  // brings in.  lbv[i]: the first list slot of chunk index i (the list is in
+  // id order; chunk index i holds ids [i * NT * EPC, (i + 1) * NT * EPC)).
+  int lbv[R + 1];
+#pragma unroll
+  for (int i = 0; i <= R; ++i) {
+    const int w = i * (NT * EPC / 32);
+    lbv[i] = w < a.mw ? uni((int)woff[w]) : n_list;
+  }
+  bool list_ovf = false;
+#pragma unroll
+  for (int i = 0; i < R; ++i) list_ovf |= lbv[i + 1] - lbv[i] > NT;
+  const __amdgpu_buffer_rsrc_t rsg =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, V * 2, 0x00020000);
+  auto gather_id = [&](int i) {  // the id at list slot lbv[i] + tid (clamped)
+    return s.list_id[min(lbv[i] + tid, max(lbv[i + 1] - 1, 0))];
+  };
+  auto gather_at = [&](int id) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b16(rsg, id * 2, 0, 0);
+  };
+  auto gather = [&](int i) { return gather_at(gather_id(i)); };
+  auto consume = [&](int i, uint32_t raw) {
+    if (lbv[i] + tid < lbv[i + 1]) s.list_val[lbv[i] + tid] = __uint_as_float(raw << 16);
+  };
+  uint32_t gr[R];
+#pragma unroll
+  for (int i = 0; i < PIPE0; ++i) gr[i] = gather(i);
+#pragma unroll
+  for (int i = PIPE0; i < PIPE; ++i) {
+    reg[i] = load_chunk(i);
+    gr[i] = gather(i);
+  }
+
+  // ---- 2. chunks as they land: count -----------------------------------------
+  // this lane's histogram copy, as an LDS address (the block has no static
+  // LDS, so the copies lie below 2^16 and bin addresses fit 16 bits)
+  const uint32_t lb = lds_addr(cnt) + (uint32_t)(lane & (kVCopies - 1)) * kVStride * 4u;
+  const uint32_t ninf = sconst(0xFF80FF80u);
+  VMap vm;
+  VMapP vp;
+  auto count_chunk = [&](uint4 c) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a2 = vaddr2(w[q], vp);
+      lds_add(a2 & 0xFFFFu, 1u);
+      lds_add(a2 >> 16, 1u);
+    }
+  };
+  // chunk i of this lane is chunk g = tid + i * NT: its kill byte is byte g
+  // of the kill mask (read one chunk ahead, so that the read does not queue
+  // behind the chunk's own histogram adds, and so are the list ids gathered)
+  const uint8_t *kbyte = reinterpret_cast<const uint8_t *>(s.kmask) + tid;
+  const int itail = tail_n > 0 ? NG / NT : -1, ttail = NG % NT;
+  // (every lane loaded the same tail: it is held in scalar registers)
+  const uint32_t tw0 = uni(ea.tw[0]), tw1 = uni(ea.tw[1]), tw2 = uni(ea.tw[2]), tw3 = uni(ea.tw[3]);
+  auto chunk_of = [&](int i) {  // (the tail, at its slot)
+    uint4 c = launder(reg[i]);
+    if (i == itail) {  // (uniform)
+      const bool t = tid == ttail;
+      c = make_uint4(t ? tw0 : c.x, t ? tw1 : c.y, t ? tw2 : c.z, t ? tw3 : c.w);
+    }
+    return c;
+  };
+  uint32_t kb_n = kbyte[0];
+  int gid_n = PIPE < R ? gather_id(PIPE) : 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (i + PIPE < R) {
+      reg[i + PIPE] = load_chunk(i + PIPE);
+      gr[i + PIPE] = gather_at(gid_n);
+      if (i + PIPE + 1 < R) gid_n = gather_id(i + PIPE + 1);
+    }
+    const uint32_t kb = kb_n;
+    if (i + 1 < R) kb_n = kbyte[(i + 1) * NT];
+    const uint4 c = vkill(chunk_of(i), kb, ninf);
+    reg[i] = c;
+    if (i >= 1) consume(i - 1, gr[i - 1]);  // (asked for before chunk i)
+    if (i == 0) {
+      // the maximum of every lane's first chunk places the bins
+      vp.c7fff = sconst(0x7FFF7FFFu);
+      vp.czm = sconst(kZoneMag | (kZoneMag << 16));
+      vp.c8000 = sconst(0x80008000u);
+      u16x2 m2 = vkeys2(c.x, vp);
+      m2 = __builtin_elementwise_max(m2, vkeys2(c.y, vp));
+      m2 = __builtin_elementwise_max(m2, vkeys2(c.z, vp));
+      m2 = __builtin_elementwise_max(m2, vkeys2(c.w, vp));
+      const uint32_t km = max((uint32_t)m2.x, (uint32_t)m2.y);
+      vm = make_vmap(base_key(uni(block_max_u32_lds<NT>(km, vs.kmax))));
+      vp = pack_vmap(vm, lb);
+    }
+    count_chunk(c);
+  }
+  consume(R - 1, gr[R - 1]);
+  if (list_ovf) {  // (uniform, rare) list slots past NT in one chunk index
+    for (int e = tid; e < n_list; e += NT) {
+      const int id = s.list_id[e];
+      if (e - (int)woff[id / (NT * EPC) * (NT * EPC / 32)] >= NT) s.list_val[e] = E::load1(rowp, id);
+    }
+  }
+  __syncthreads();  // the row has landed
+  float lmax = -INFINITY;
+  for (int k = tid; k < n_list; k += NT) {
+    const float y = penalize(s.list_val[k], a.rep);
+    s.list_val[k] = y;
+    lmax = fmaxf(lmax, y);
+  }
+  // fold the copies; the highest occupied bin
+  uint32_t c4[BPT];
+  auto fold = [&]() {
+    int top_b = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      const int b = tid * BPT + q;
+      c4[q] = 0u;
+      if (b < NB) {
+#pragma unroll
+        for (int k = 0; k < kVCopies; ++k) c4[q] += cnt[k * kVStride + b];
+        if (c4[q] && b >= 1) top_b = b;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < BPT; ++q)
+      if (tid * BPT + q < NB) cnt[tid * BPT + q] = c4[q];
+    return top_b;
+  };
+  const int btop = (int)uni(block_max_u32_lds<NT>((uint32_t)fold(), vs.kmax));
+  lmax = uni(block_max_f32<NT>(lmax, sh.red_f32));
+  const int zn = vm.zn, zp = vm.zp;  // the near-zero bins (or -1)
+  // Scores past the last bin (the row's maximum far above its first
+  // chunks'): the bisection decides.
+  bool fallback = btop == NB - 1 || (lmax > -INFINITY && vbin(vkey_floor(lmax), vm) == NB - 1);
+  if (tid == 0) {
+    sh.n_list = n_list;
+    sh.dense_pen = 0;
+  }
+  // the reference: an upper bound of the row's maximum (a near-zero bin:
+  // its upper edge)
+  const float kZone = __uint_as_float((uint32_t)(127 - kZoneExp) << 23);
+  const float dmax = btop < 1 ? -INFINITY
+                     : btop == zp ? kZone
+                     : btop == zn ? 0.0f
+                                  : vkey_value(vbin_key(btop, vm));
+  const float mx = fmaxf(dmax, lmax);
+  uint64_t kcut = 0ull;
+  int token = 0;
+  if (mx == -INFINITY) {  // every id removed: id 0, nothing kept
+    if (tid == 0) a.out_tokens[row] = 0;
+    if (a.out_processed) res_processed<1>(a, row, s, INFINITY, ~0ull, n_list);
+    return;
+  }
+  const float cref = mx * kLog2e;
+  auto mass = [&](float y) { return __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -cref)); };
+
+  // ---- 3. near-zero members, individual masses, bin masses ---------------------
+  // Near-zero members one by one, after the seen ids: (id, score), the two
+  // near-zero bins then holding individuals only.  If there are too many
+  // and they all hold one value (zeros, say), that value is a tie group in
+  // its bin instead.
+  int n_ind = n_list;
+  float zval = -INFINITY;  // the value of that tie group
+  int zgb = -1;            // its bin
+  if ((zn >= 1 && cnt[zn] > 0u) || (zp >= 1 && cnt[zp] > 0u)) {
+    if (tid == 0) vs.nz = 0;
+    __syncthreads();
+    float zlo = INFINITY, zhi = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint4 c = launder(reg[i]);
+      const int g = tid + i * NT;
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const float x = E::get(c, j);
+        if (fabsf(x) <= kZone) {
+          zlo = fminf(zlo, x);
+          zhi = fmaxf(zhi, x);
+          const int slot = atomicAdd(&vs.nz, 1);
+          if (slot < kZoneCap) {
+            s.list_id[n_list + slot] = g * EPC + j;
+            s.list_val[n_list + slot] = x;
+          }
+        }
+      }
+    }
+    zlo = -uni(block_max_f32<NT>(-zlo, sh.red_f32));
+    zhi = uni(block_max_f32<NT>(zhi, sh.red_f32));
+    const int nz = uni(vs.nz);
+    __syncthreads();
+    if (nz <= kZoneCap) {
+      n_ind = n_list + nz;
+      if (tid == 0) {  // the members are individuals now
+        if (zn >= 1) cnt[zn] = 0u;
+        if (zp >= 1) cnt[zp] = 0u;
+      }
+    } else if (zlo == zhi) {
+      zval = zlo + 0.0f;  // (-0 is +0; zeros of both signs join in the upper bin)
+      zgb = zval >= 0.0f ? zp : zn;
+      if (zgb < 1) {
+        fallback = true;
+      } else if (zval == 0.0f && zn >= 1 && tid == 0) {
+        cnt[zp] += cnt[zn];
+        cnt[zn] = 0u;
+      }
+    } else {
+      fallback = true;
+    }
+  }
+  // Value of bin b (-inf for a near-zero bin of individuals only) and its
+  // fixed-point unit: the ulp of the mass of the bin's lowest score, which
+  // every individual of the bin reaches or exceeds.
+  auto bin_value = [&](int b) {
+    return b == zgb ? zval : (b == zn || b == zp) ? -INFINITY : vkey_value(vbin_key(b, vm));
+  };
+  auto unit_expo = [&](int b) {
+    const float lo = b == zn ? -kZone : b == zp ? 0.0f : vkey_value(vbin_key(b, vm));
+    return (int)((__float_as_uint(mass(lo)) >> 23) & 0xFFu);
+  };
+  auto ind_bin = [&](float y) { return vbin(vkey_floor(y), vm); };
+  for (int b = tid; b < NB; b += NT) lfix[b] = 0ull;
+  __syncthreads();
+  int ovf = 0;
+  for (int k = tid; k < n_ind; k += NT) {
+    const float y = s.list_val[k];
+    const int b = ind_bin(y);
+    if (b < 1) continue;
+    const int eu = unit_expo(b);
+    const uint32_t eb = __float_as_uint(mass(y));
+    const int ek = (int)((eb >> 23) & 0xFFu);
+    if (eu == 0 || ek == 0) continue;  // below 2^-126 of the maximum: nothing
+    const int sft = ek - eu;
+    if (sft < 0 || sft > 24) { ovf = 1; continue; }
+    atomicAdd(reinterpret_cast<unsigned long long *>(&lfix[b]),
+              (unsigned long long)((eb & 0x7FFFFFu) | 0x800000u) << sft);
+  }
+  if (uni(block_sum_i32<NT>(ovf, sh.red_i32)) != 0) fallback = true;
+  // bin masses, in place of the fixed-point sums
+  double part = 0.0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    const int b = tid * BPT + q;
+    if (b < NB) {
+      double m = 0.0;
+      if (b >= 1) {
+        const uint32_t n = cnt[b];
+        const uint64_t l = lfix[b];
+        if (n) m = (double)n * (double)mass(bin_value(b));
+        if (l) {
+          const int eu = unit_expo(b);
+          m += (double)l * __longlong_as_double((long long)(eu - 150 + 1023) << 52);
+        }
+      }
+      bmass[b] = m;
+      part += m;
+    }
+  }
+
+  // ---- 4. cumulative masses: the boundary bin and the draw bin -------------
+  // Thread t owns bins [t*BPT, t*BPT + BPT); C(b) = mass of bins >= b.
+  double incl;  // mass of bins owned by threads >= tid
+  {
+    double v = part;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double t = __shfl_down(v, o, kWave);
+      if (lane + o < kWave) v += t;
+    }
+    if (lane == 0) sh.red_f64[wid] = v;
+    __syncthreads();
+    double after = 0.0;
+    for (int q = wid + 1; q < NW; ++q) after += sh.red_f64[q];
+    incl = v + after;
+  }
+  // (the mass above this thread's bins waits in LDS: registers are scarce
+  // while the row is held)
+  double *above = reinterpret_cast<double *>(smem + kVAboveOff);
+  above[tid] = incl - part;
+  if (tid == 0) {
+    sh.wprime = incl;
+    sh.bin_p = -1;
+  }
+  __syncthreads();
+  const double W = uni(sh.wprime);
+  const bool use_top_p = a.top_p < 1.0f;
+  const double pw = (double)a.top_p * W;
+  const double u = (double)a.uniforms[row];
+  {
+    double C = above[tid];
+    for (int q = BPT - 1; q >= 0; --q) {
+      const int b = tid * BPT + q;
+      if (b >= NB) continue;
+      const double Cb1 = C;
+      C += bmass[b];
+      if (use_top_p && Cb1 < pw && C >= pw) { sh.bin_p = b; sh.sbase = Cb1; }
+    }
+  }
+  __syncthreads();
+  const int bp = uni(sh.bin_p);
+  const double C_bp1 = bp >= 0 ? uni(sh.sbase) : 0.0;  // mass above the boundary bin
+
+  // View of bin b (all threads): its value, its individuals other than the
+  // value ordered by key into okey / oval, the tie group's size.  Returns
+  // false when the bin has more individuals than fit.
+  auto view_bin = [&](int b) -> bool {
+    if (tid == 0) {
+      vs.n_ind_b = 0;
+      vs.n_tie_b = 0;
+    }
+    const float v = bin_value(b);
+    __syncthreads();
+    for (int k = tid; k < n_ind; k += NT) {
+      const float y = s.list_val[k];
+      if (ind_bin(y) != b) continue;
+      if (y == v) {
+        atomicAdd(&vs.n_tie_b, 1);
+      } else {
+        const int slot = atomicAdd(&vs.n_ind_b, 1);
+        if (slot < kGatherCap) {
+          gkey[slot] = sel_key(y, (uint32_t)s.list_id[k]);
+          gval[slot] = mass(y);
+        }
+      }
+    }
+    __syncthreads();
+    const int ni = uni(vs.n_ind_b);
+    if (ni > kGatherCap) return false;
+    for (int i = tid; i < ni; i += NT) {
+      const uint64_t ki = gkey[i];
+      int r = 0;
+      for (int j = 0; j < ni; ++j) r += gkey[j] > ki;
+      okey[r] = ki;
+      oval[r] = gval[i];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int na = 0;
+      for (int q = 0; q < ni; ++q) na += key_score(okey[q]) > v;
+      vs.view.single = 1;
+      vs.view.v = v;
+      vs.view.e = v == -INFINITY ? 0.0f : mass(v);
+      vs.view.n_ind = ni;
+      vs.view.n_above = na;
+      vs.view.n_group = (int)cnt[b] + vs.n_tie_b;
+    }
+    __syncthreads();
+    return true;
+  };
+
+  double Wp = W;
+  int cut_kind = kNone, draw_kind = kNone;
+  int cut_pos = 0x7FFFFFFF;
+  int bs = -1;
+  double bs_start = 0.0;
+  if (!fallback && bp >= 0) {
+    if (!view_bin(bp)) {
+      fallback = true;
+    } else {
+      if (tid == 0) vs.walk[0] = single_walk(true, C_bp1, pw, vs.view, okey, oval, 0x7FFFFFFF);
+      __syncthreads();
+      cut_kind = uni(vs.walk[0].kind);
+      if (cut_kind == kFail) fallback = true;
+      Wp = uni(vs.walk[0].acc);
+      cut_pos = uni(vs.walk[0].pos);
+      if (cut_kind == kInd) kcut = uni(vs.walk[0].key);
+    }
+  }
+  const float bp_v = uni(vs.view.v);  // the boundary bin's value
+  const double target = u * Wp;
+  // The draw's bin: the bin whose cumulative mass interval holds the target
+  // (bp counts only its kept part); every thread checks its own bins.
+  if (!fallback) {
+    if (tid == 0) {
+      sh.bin_hi = -1;
+      sh.sbase = -1.0;
+    }
+    __syncthreads();
+    {
+      double C = above[tid];
+      for (int q = BPT - 1; q >= 0; --q) {
+        const int b = tid * BPT + q;
+        if (b >= NB || b < 1) continue;
+        const double m = (bp >= 0 && b == bp) ? (Wp - C_bp1) : bmass[b];
+        if (m > 0.0 && C <= target && target < C + m && (bp < 0 || b >= bp)) {
+          sh.bin_hi = b;
+          sh.sbase = C;
+        }
+        C += m;
+      }
+    }
+    __syncthreads();
+    bs = uni(sh.bin_hi);
+    bs_start = uni(sh.sbase);
+    if (bs < 0) {
+      fallback = true;  // rounding left the target outside every bin
+    } else if (bs == bp && bp >= 0) {
+      // same bin as the boundary: the view is still in place
+      if (tid == 0) vs.walk[1] = single_walk(false, bs_start, target, vs.view, okey, oval, cut_pos);
+      __syncthreads();
+      draw_kind = uni(vs.walk[1].kind);
+    } else if (!view_bin(bs)) {
+      fallback = true;
+    } else {
+      if (tid == 0) vs.walk[1] = single_walk(false, bs_start, target, vs.view, okey, oval, 0x7FFFFFFF);
+      __syncthreads();
+      draw_kind = uni(vs.walk[1].kind);
+    }
+    if (draw_kind == kFail) fallback = true;
+  }
+  const float bs_v = uni(vs.view.v);
+
+  // ---- 5. one pass over the registers: the draw's rank in its tie group -----
+  // (The boundary's own member is needed only for the final scores: such a
+  // call takes the bisection when the boundary falls inside a tie group.)
+  if (!fallback && a.out_processed && cut_kind == kGroup) fallback = true;
+  const bool g1 = !fallback && draw_kind == kGroup;
+  if (g1) {
+    if (tid == 0) {
+      vs.gv[1] = bs_v;
+      vs.gk[1] = vs.walk[1].rank + 1;
+      vs.gi[1] = -1;
+      vs.gid[1] = -1;
+      vs.ltie = 0;
+    }
+    __syncthreads();
+    const float vv = uni(vs.gv[1]);
+    // seen ids whose penalized score equals the group value join the group
+    // (rare): which chunks of which thread hold one, 16 bits per thread,
+    // two threads a word, in the (now idle) ordered-view buffer
+    uint32_t *tiew = reinterpret_cast<uint32_t *>(okey);
+    for (int q = tid; q < NT / 2; q += NT) tiew[q] = 0u;
+    __syncthreads();
+    for (int k = tid; k < n_list; k += NT) {
+      if (s.list_val[k] == vv) {
+        vs.ltie = 1;
+        const int gg = s.list_id[k] / EPC, t = gg % NT, ci = gg / NT;
+        atomicOr(&tiew[t >> 1], 1u << ((t & 1) * 16 + ci));
+      }
+    }
+    __syncthreads();
+    const bool ltie_all = uni(vs.ltie) != 0;
+    const uint32_t tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
+    // One pass over the registers: every lane counts the members in each of
+    // its chunks (a nonzero value by its bf16 pattern, a zero one by the
+    // pattern less the sign; seen ids equal to the value added from the
+    // list), in byte fields, summed over rows of 16 lanes by shifts within
+    // the row.  Then one wave per chunk index scans the 64 rows of the
+    // workgroup in id order; the chunk index and the row of the member
+    // follow, and that row names it.
+    const uint32_t pat = vv == 0.0f ? 0u : (__float_as_uint(vv) >> 16) * 0x10001u;
+    const uint32_t msk = vv == 0.0f ? 0x7FFF7FFFu : 0xFFFFFFFFu;
+    auto list_ties = [&](int i) {  // seen ids of chunk i equal to vv, per element bit j
+      uint32_t mb = 0u;
+      if ((tmask >> i) & 1u) {
+        const int g = tid + i * NT;
+        uint32_t bits = chunk_bits<1>(s.smask, g);
+        while (bits) {
+          const int j = __ffs(bits) - 1;
+          bits &= bits - 1;
+          if (s.list_val[list_slot(g * EPC + j, s.smask, woff)] == vv) mb |= 1u << j;
+        }
+      }
+      return mb;
+    };
+    uint32_t cb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint4 c = launder(reg[i]);
+      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+      uint32_t n = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = (w[q] & msk) ^ pat;
+        // a zero half of x is a member: bit 15 of (x & 7FFF) + 7FFF, or'ed
+        // with x, is clear exactly there
+        n += __popc(~(((x & 0x7FFF7FFFu) + 0x7FFF7FFFu) | x) & 0x80008000u);
+      }
+      cb[i >> 2] |= n << ((i & 3) * 8);
+      __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: the row holds the registers
+    }
+    if (ltie_all) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) cb[i >> 2] += (uint32_t)__popc(list_ties(i)) << ((i & 3) * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // inclusive sums along each row of 16 lanes
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x111, 0xF, 0xF, true);
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x112, 0xF, 0xF, true);
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x114, 0xF, 0xF, true);
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x118, 0xF, 0xF, true);
+    }
+    // (rows numbered wave * 4 + row: that is id order within a chunk index)
+    uint32_t *rsum = reinterpret_cast<uint32_t *>(gkey);  // 64 rows x 16 bytes
+    if ((lane & 15) == 15) {
+      const int u = wid * 4 + (lane >> 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rsum[u * 4 + k] = cb[k];
+    }
+    __syncthreads();
+    // wave wid scans chunk index wid over the 64 rows (lane = row)
+    int rc = 0, rinc = 0;
+    if (wid < R) {
+      rc = (int)((rsum[lane * 4 + (wid >> 2)] >> ((wid & 3) * 8)) & 0xFFu);
+      rinc = wave_incl_scan_i32(rc);
+      if (lane == kWave - 1) vs.wtot[0][0][wid] = rinc;  // the chunk index's total
+    }
+    __syncthreads();
+    if (tid < 16) {
+      const int T = tid < R ? vs.wtot[0][0][tid] : 0;
+      int inc = T;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const int y = __shfl_up(inc, o, 16);
+        if (tid >= o) inc += y;
+      }
+      const int k = vs.gk[1];
+      if (inc - T < k && k <= inc) {
+        vs.gi[1] = tid;
+        vs.gr[1] = k - (inc - T);
+      }
+    }
+    __syncthreads();
+    const int ii = uni(vs.gi[1]);
+    if (ii >= 0) {
+      if (wid == ii) {
+        const int k = uni(vs.gr[1]);
+        if (rinc - rc < k && k <= rinc) {
+          vs.gw[1] = lane;             // the row
+          vs.gk[0] = k - (rinc - rc);  // the member's rank in it
+        }
+      }
+      __syncthreads();
+      const int ur = uni(vs.gw[1]);
+      if (wid == ur / 4 && (lane >> 4) == ur % 4) {
+        // members among this lane's elements of chunk ii (every chunk is
+        // tested with a constant index: selecting reg[ii] would become a
+        // run-time index and send the whole row through scratch memory)
+        uint32_t mbits = 0u;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const uint4 c = launder(reg[i]);
+          const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+          uint32_t mb = 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x = (w[q] & msk) ^ pat;
+            mb |= ((x & 0xFFFFu) == 0u ? 1u : 0u) << (2 * q);
+            mb |= ((x >> 16) == 0u ? 1u : 0u) << (2 * q + 1);
+          }
+          mbits = i == ii ? mb : mbits;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ltie_all) mbits |= list_ties(ii);
+        const int cnt_l = __popc(mbits);
+        int inc = cnt_l;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const int y = __shfl_up(inc, o, 16);
+          if ((lane & 15) >= o) inc += y;
+        }
+        const int r0 = vs.gk[0];
+        if (inc - cnt_l < r0 && r0 <= inc) {
+          int r = r0 - (inc - cnt_l);
+          uint32_t bits = mbits;
+          int j = 0;
+          while (bits) {
+            j = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (--r == 0) break;
+          }
+          vs.gid[1] = (tid + ii * NT) * EPC + j;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (g1 && vs.gid[1] < 0) fallback = true;
+  if (!fallback && draw_kind == kGroup) token = vs.gid[1];
+  if (!fallback && draw_kind == kInd) token = (int)key_index(vs.walk[1].key);
+
+  if (fallback) token = bisect_select<1, true>(a, row, s, sh, -INFINITY, cref, &kcut);
+  if (tid == 0) a.out_tokens[row] = token;
+  if (a.out_processed) res_processed<1>(a, row, s, -INFINITY, kcut, n_list);
+}
+
+template <int R>
+static hipError_t launch_vres_t(const SelectArgs &a, size_t lds, hipStream_t st) {
+  static bool attr = false;  // benign race: every writer stores the same value
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_vres<R>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kSelectMaxDynLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_vres<R>), dim3(a.B), dim3(NT), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_vres(const SelectArgs &a, int res, size_t lds, hipStream_t st) {
+  if (a.dtype != 1) return hipErrorInvalidValue;
+  if (res == 16) return launch_vres_t<16>(a, lds, st);
+  if (res == 8) return launch_vres_t<8>(a, lds, st);
+  return launch_vres_t<4>(a, lds, st);
+}
+
+}  // namespace tsel

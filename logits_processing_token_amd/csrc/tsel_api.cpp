@@ -118,6 +118,51 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   return *lds_bytes <= budget;
 }
 
+// On-chip layout of the value-bin resident kernel (bf16): the histogram
+// copies from byte 0 (the kernel computes bin offsets from there in 16
+// bits), then the kill and seen masks, the list (seen ids, then the listed
+// near-zero scores) and the list offset of every mask word.
+bool plan_vres(const tsel_params *p, int res, tsel::SelectArgs *a, size_t *lds_bytes) {
+  const int32_t V = p->vocab;
+  const int32_t mw = (V + 31) / 32;
+  // the kill and seen masks run to one byte per chunk slot of the registers,
+  // the list offsets to one per four slots
+  const size_t slots = (size_t)res * tsel::kSelectThreads;
+  const size_t kmask_bytes = align16(std::max<size_t>((size_t)mw * 4, slots));
+  const size_t smask_bytes = kmask_bytes;
+  const size_t woff = align16(std::max<size_t>(2 * (size_t)mw, slots / 2));
+  const size_t budget = (size_t)tsel::kSelectMaxDynLds;
+  size_t off = align16((size_t)tsel::kVHistBytes);
+  const size_t fixed = off + kmask_bytes + smask_bytes + woff + tsel::kVSharedBytes;
+  size_t lcap = (size_t)std::min<int64_t>(std::max<int64_t>(p->hist_stride, 0), V) + 8;
+  lcap = std::min<size_t>((lcap + 3) & ~size_t(3), kMaxList);
+  if (fixed + 8 * (64 + (size_t)tsel::kZoneCap) > budget) return false;
+  if (fixed + 8 * (lcap + tsel::kZoneCap) > budget)  // longer histories: the streamed path
+    lcap = ((budget - fixed) / 8 - tsel::kZoneCap) & ~size_t(3);
+  const size_t lall = lcap + tsel::kZoneCap;
+  a->mw = mw;
+  a->lcap = (int32_t)lcap;
+  a->nb = tsel::kVBins;
+  a->ccap = 0;
+  a->bin_mant = 0;
+  a->tcap = 0;
+  a->off_kmask = (uint32_t)off;
+  off += kmask_bytes;
+  a->off_smask = (uint32_t)off;
+  off += smask_bytes;
+  a->off_list_id = (uint32_t)off;
+  off += 4 * lall;
+  a->off_list_val = (uint32_t)off;
+  off += 4 * lall;
+  a->off_woff = (uint32_t)align16(off);
+  off = a->off_woff + woff;
+  a->off_sh = (uint32_t)align16(off);
+  off = a->off_sh + tsel::kVSharedBytes;
+  a->off_lut = a->off_rhist = a->off_area = 0;  // unused here
+  *lds_bytes = off;
+  return off <= budget;
+}
+
 // Chunks of 16 bytes per lane that hold a whole row in registers on the full
 // path (0: the row is re-read from memory on each pass).
 int resident_chunks(const tsel_params *p) {
@@ -214,6 +259,15 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
     tsel::SelectArgs r = a;
     size_t rlds = 0;
     if (a.top_k <= 0 && a.temperature == 1.0f && res > 0 && a.V >= epc &&
+        a.dtype == TSEL_BF16 && plan_vres(params, res, &r, &rlds)) {
+      // bf16 row held in registers, one histogram bin per bf16 value; rows
+      // with more distinct seen ids than the list holds are left pending
+      // for the streamed path
+      e = tsel::launch_vres(r, res, rlds, s);
+      const int64_t most_seen = std::min<int64_t>(std::max(params->hist_stride, 0), a.V);
+      if (e == hipSuccess && r.lcap < most_seen)
+        e = tsel::launch_full(a, res, lds, s, 1);
+    } else if (a.top_k <= 0 && a.temperature == 1.0f && res > 0 && a.V >= epc &&
         plan_layout(params, SelectKernel::kRes, &r, &rlds)) {
       // Row held in registers.  A row with more distinct seen ids than the
       // on-chip list holds is left pending for the streamed path.

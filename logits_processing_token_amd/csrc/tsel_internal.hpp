@@ -21,6 +21,23 @@ constexpr int kBinAbove = 16;
 constexpr int kGatherCap = 256;           // elements of one mass sub-bin ordered on chip
 constexpr float kRefSlack = 2.0f;           // reference = first-chunk max + this (nats)
 
+// Value-bin resident kernel (bf16 rows): one bin per bf16 value.
+constexpr int kVBins = 4032;                // bins; bin 0 takes the dropped scores
+constexpr int kVStride = kVBins + 8;        // words between histogram copies (bank offset 8)
+constexpr int kVCopies = 4;                 // histogram copies, by lane
+constexpr int kZoneExp = 8;                 // scores below 2^-kZoneExp in magnitude share a bin
+constexpr float kDropNats = 36.0f;          // bins start this far below the first chunks' max
+constexpr int kZoneCap = 512;               // near-zero scores listed one by one
+constexpr int kVHistBytes = kVCopies * kVStride * 4;  // the copies, from LDS byte 0
+constexpr int kVMassOff = kVStride * 4;     // after the fold: per-bin masses (doubles)
+constexpr int kVViewOff = kVMassOff + kVBins * 8;     // then the ordered view of one bin
+constexpr int kVRowSharedBytes = 1024;      // the row's shared scalars, then the kernel's own
+constexpr int kVSharedBytes = 4096;
+constexpr int kVAboveOff = kVViewOff + 24 * kGatherCap;  // then one double per thread
+static_assert(kVAboveOff + 8 * kSelectThreads <= kVHistBytes, "beyond the copies");
+static_assert((kVCopies - 1) * kVStride * 4 + (kVBins - 1) * 4 < 65536,
+              "bin offsets are computed in 16 bits");
+
 
 // Arguments of the selection kernels (passed by value).
 struct SelectArgs {
@@ -52,6 +69,8 @@ struct SelectArgs {
   int32_t tcap;             // top_k candidate capacity
   uint32_t off_smask, off_list_id, off_list_val, off_lut, off_rhist, off_area;
   uint32_t off_woff;        // resident path: list offset of each thread's mask words
+  uint32_t off_kmask;       // kill mask (0 but on the value-bin path)
+  uint32_t off_sh;          // value-bin path: its shared scalars (no static LDS)
 };
 
 hipError_t launch_greedy(const SelectArgs &a, size_t lds, hipStream_t s);
@@ -60,6 +79,8 @@ hipError_t launch_topk(const SelectArgs &a, size_t lds, hipStream_t s);
 hipError_t launch_full(const SelectArgs &a, int res, size_t lds, hipStream_t s, int pending);
 // sampling without top_k at temperature 1, row held in `res` chunks per lane
 hipError_t launch_res(const SelectArgs &a, int res, size_t lds, hipStream_t s);
+// the same on bf16 rows with one histogram bin per bf16 value
+hipError_t launch_vres(const SelectArgs &a, int res, size_t lds, hipStream_t s);
 
 hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
                          int64_t row_bytes, int32_t chunks, const int32_t *cand,
