@@ -29,8 +29,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "logit rows/sec + achieved HBM GB/s (% peak), B=256 V=128256 full chain"
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_res_b256_v128256_traffic.txt")
-KERNEL_SOURCES = ("logits_processing_token_amd/csrc/k_res.hip",
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_vres_b256_v128256_traffic.txt")
+KERNEL_SOURCES = ("logits_processing_token_amd/csrc/k_vres.hip",
+                  "logits_processing_token_amd/csrc/k_res_common.hpp",
                   "logits_processing_token_amd/csrc/k_mass.hpp",
                   "logits_processing_token_amd/csrc/k_select_common.hpp",
                   "logits_processing_token_amd/csrc/tsel_device.hpp",

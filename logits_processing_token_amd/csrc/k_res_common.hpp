@@ -167,14 +167,14 @@ __device__ __forceinline__ void res_processed(const SelectArgs &a, int row, cons
   }
 }
 
-// The small loads of a resident row, issued at the very start together with
-// the row's own (none of them waits for the row's lengths): history ids
-// (up to the history stride; entries past the row's length are ignored
-// later), kill-mask words and the row tail (V % EPC ids after the last whole
-// chunk, as one more chunk).  Every load is unconditional and in bounds -- an
-// absent mask or history reads word 0 of the lengths and discards it, every
-// lane loads the same few tail elements -- so that no branch splits the loads
-// and the row's chunks can later be waited for one at a time.
+// The small loads of a resident row, issued at the very start (none of them
+// waits for the row's lengths): this thread's four history ids (slots 4 tid
+// to 4 tid + 3; slots past the row's length are ignored later), its four
+// kill-mask words and the row tail (V % EPC ids after the last whole chunk,
+// as one more chunk).  All go through buffer resources, which read 0 past
+// their end: no index is clamped, an absent mask or history is a resource
+// of length 0, and no branch splits the loads, so that the row's chunks can
+// later be waited for one at a time.
 struct Early {
   int hreg[kHpt];
   uint32_t km[kMpt];    // bad words | suppress
@@ -182,37 +182,46 @@ struct Early {
   uint32_t tw[4];
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int DT>
 __device__ __forceinline__ void early_loads(const SelectArgs &a, int row, const char *rowp,
                                             Early &e) {
   using E = Elem<DT>;
   constexpr int EPC = E::EPC;
-  const int tid = threadIdx.x, V = a.V, mw = a.mw;
+  static_assert(kHpt == 4 && kMpt == 4, "four words per thread");
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, V = a.V;
   const int NG = V / EPC;
-  const uint32_t *lens_u = reinterpret_cast<const uint32_t *>(a.lens);
+  const uint32_t mbytes = 4u * (uint32_t)a.mw;
   const int32_t *hp = a.hist_stride > 0 ? a.hist + (int64_t)row * a.hist_stride : a.lens;
-  const int hlast = max(a.hist_stride, 1) - 1;
+  const u32x4_t hv = __builtin_amdgcn_raw_buffer_load_b128(
+      buf_rsrc(hp, 4u * (uint32_t)max(a.hist_stride, 0)), tid * 16, 0, 0);
+  const u32x4_t m0 = __builtin_amdgcn_raw_buffer_load_b128(
+      buf_rsrc(a.bad_mask ? (const void *)a.bad_mask : a.lens, a.bad_mask ? mbytes : 0u), tid * 16, 0, 0);
+  const u32x4_t m1 = __builtin_amdgcn_raw_buffer_load_b128(
+      buf_rsrc(a.sup_mask ? (const void *)a.sup_mask : a.lens, a.sup_mask ? mbytes : 0u), tid * 16, 0, 0);
+  const u32x4_t m2 = __builtin_amdgcn_raw_buffer_load_b128(
+      buf_rsrc(a.begin_mask ? (const void *)a.begin_mask : a.lens, a.begin_mask ? mbytes : 0u), tid * 16, 0, 0);
 #pragma unroll
-  for (int k = 0; k < kHpt; ++k) e.hreg[k] = hp[min(tid + k * NT, hlast)];
-  const uint32_t *m0p = a.bad_mask ? a.bad_mask : lens_u;
-  const uint32_t *m1p = a.sup_mask ? a.sup_mask : lens_u;
-  const uint32_t *m2p = a.begin_mask ? a.begin_mask : lens_u;
-  const uint32_t m0k = a.bad_mask ? ~0u : 0u, m1k = a.sup_mask ? ~0u : 0u;
-  const uint32_t m2k = a.begin_mask ? ~0u : 0u;
-#pragma unroll
-  for (int q = 0; q < kMpt; ++q) {
-    const int w = min(tid * kMpt + q, mw - 1);
-    e.km[q] = (m0p[m0k ? w : 0] & m0k) | (m1p[m1k ? w : 0] & m1k);
-    e.kbeg[q] = m2p[m2k ? w : 0] & m2k;
+  for (int k = 0; k < 4; ++k) {
+    e.hreg[k] = (int)hv[k];
+    e.km[k] = m0[k] | m1[k];
+    e.kbeg[k] = m2[k];
   }
+  // the tail: every lane reads the same few elements (0 past the row,
+  // replaced by -inf)
   const int tail_n = V - NG * EPC;
+  const __amdgpu_buffer_rsrc_t rr = buf_rsrc(rowp, (uint32_t)V * (DT == 1 ? 2u : 4u));
 #pragma unroll
   for (int q = 0; q < 4; ++q) e.tw[q] = E::kNegInf;
 #pragma unroll
   for (int j = 0; j < EPC - 1; ++j) {
-    const int v = min(NG * EPC + j, V - 1);
-    const uint32_t bits = DT == 1 ? (uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v]
-                                  : reinterpret_cast<const uint32_t *>(rowp)[v];
+    const uint32_t bits =
+        DT == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr, (NG * EPC + j) * 2, 0, 0)
+                : __builtin_amdgcn_raw_buffer_load_b32(rr, (NG * EPC + j) * 4, 0, 0);
     const uint32_t ninf = DT == 1 ? 0xFF80u : 0xFF800000u;
     put_elem<DT>(e.tw, j, j < tail_n ? bits : ninf);
   }
@@ -224,11 +233,19 @@ __device__ __forceinline__ void early_loads(const SelectArgs &a, int row, const 
 __device__ __forceinline__ void stage_clear(const Lds &s, RowShared &sh, int kwords, int pad_byte,
                                             int swords) {
   const int tid = threadIdx.x;
-  for (int w = tid; w < kwords; w += NT) {
-    const int b0 = 4 * w;
-    s.kmask[w] = b0 + 4 <= pad_byte ? 0u : b0 >= pad_byte ? ~0u : ~0u << (8 * (pad_byte - b0));
+  // (16 bytes a store; both masks start 16-byte aligned and span whole
+  // multiples of 4 words, rounded up here)
+  for (int w4 = tid; w4 < (kwords + 3) / 4; w4 += NT) {
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b0 = 16 * w4 + 4 * q;
+      v[q] = b0 + 4 <= pad_byte ? 0u : b0 >= pad_byte ? ~0u : ~0u << (8 * (pad_byte - b0));
+    }
+    reinterpret_cast<uint4 *>(s.kmask)[w4] = make_uint4(v[0], v[1], v[2], v[3]);
   }
-  for (int w = tid; w < swords; w += NT) s.smask[w] = 0u;
+  for (int w4 = tid; w4 < (swords + 3) / 4; w4 += NT)
+    reinterpret_cast<uint4 *>(s.smask)[w4] = make_uint4(0u, 0u, 0u, 0u);
   if (tid == 0) sh.n_coll = 0;
 }
 
@@ -247,7 +264,7 @@ __device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo
 #pragma unroll
   for (int k = 0; k < kHpt; ++k) {
     const int v = e.hreg[k];
-    if (tid + k * NT < L && v >= 0 && v < V) atomicOr(&s.smask[v >> 5], 1u << (v & 31));
+    if (tid * kHpt + k < L && v >= 0 && v < V) atomicOr(&s.smask[v >> 5], 1u << (v & 31));
   }
   for (int i = kHpt * NT + tid; i < L; i += NT) {  // long histories
     const int v = h[i];

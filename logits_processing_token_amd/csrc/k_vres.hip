@@ -168,7 +168,7 @@ struct VShared {
   int gi[2], gw[2], gr[2];
   int gid[2];
   int wtot[2][NW][16];
-  int n_ind_b, n_tie_b;
+  int n_ind_b, n_tie_b, n_above_b;
   int ltie;
   int nz;
   uint32_t kmax[NW];
@@ -596,6 +596,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     if (tid == 0) {
       vs.n_ind_b = 0;
       vs.n_tie_b = 0;
+      vs.n_above_b = 0;
     }
     const float v = bin_value(b);
     __syncthreads();
@@ -621,11 +622,11 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       for (int j = 0; j < ni; ++j) r += gkey[j] > ki;
       okey[r] = ki;
       oval[r] = gval[i];
+      if (key_score(ki) > v) atomicAdd(&vs.n_above_b, 1);
     }
     __syncthreads();
     if (tid == 0) {
-      int na = 0;
-      for (int q = 0; q < ni; ++q) na += key_score(okey[q]) > v;
+      const int na = vs.n_above_b;
       vs.view.single = 1;
       vs.view.v = v;
       vs.view.e = v == -INFINITY ? 0.0f : mass(v);

@@ -102,14 +102,17 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes.
+// Inclusive prefix sum over the 64 lanes, by data-parallel lane moves (no
+// LDS round trip): shifts by 1, 2, 4 and 8 within each row of 16 lanes,
+// then the last lane of row 0 broadcast into row 1 and of row 2 into row 3,
+// then lane 31 into rows 2 and 3.  (Lanes a move does not reach add 0.)
 __device__ __forceinline__ int wave_incl_scan_i32(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int w = __shfl_up(v, o, kWave);
-    if (lane >= o) v += w;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 
