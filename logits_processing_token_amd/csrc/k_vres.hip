@@ -460,6 +460,15 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     for (int i = 0; i < R; ++i) {
       const uint4 c = launder(reg[i]);
       const int g = tid + i * NT;
+      // (a chunk is looked into only if one of its magnitudes is in reach:
+      // max(|u| - Z, 0) is 0 in some half)
+      const u16x2 zm = __builtin_bit_cast(u16x2, kZoneMag | (kZoneMag << 16));
+      const u16x2 msk = __builtin_bit_cast(u16x2, 0x7FFF7FFFu);
+      u16x2 t = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.x) & msk, zm);
+      t = __builtin_elementwise_min(t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.y) & msk, zm));
+      t = __builtin_elementwise_min(t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.z) & msk, zm));
+      t = __builtin_elementwise_min(t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.w) & msk, zm));
+      if (t.x != 0 && t.y != 0) continue;
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
         const float x = E::get(c, j);

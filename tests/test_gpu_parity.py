@@ -190,6 +190,69 @@ def test_resident_rows_of_one_value():
         _assert_select(w)
 
 
+@pytest.mark.parametrize("n_zone", [40, 3000])
+def test_value_bins_near_zero(n_zone):
+    """bf16 scores of magnitude at most 2^-8 share two histogram bins and are
+    listed one by one (40 per row); more than the list holds, with several
+    values among them, leave the row to the bisection (3000).  They are the
+    rows' largest scores, zeros of both signs among them, and some are seen
+    ids (penalized near zero)."""
+    V = 50000
+    s = dict(repetition_penalty=1.3, do_sample=True, top_p=0.999)
+    w = synth.random_select(91 + n_zone, 8, V, 300, dtype="bf16", settings=s, sigma=1.0,
+                            id_range=3000)
+    g = np.random.default_rng(n_zone)
+    x = (g.standard_normal((w.batch, V)).astype(np.float32) - np.float32(6.0))
+    for b in range(w.batch):
+        idx = g.choice(V, size=n_zone, replace=False)
+        vals = g.uniform(-2.0 ** -8, 2.0 ** -8, size=n_zone).astype(np.float32)
+        vals[::7] = 0.0
+        vals[1::7] = -0.0
+        x[b, idx] = vals
+        w.history[b, :20] = idx[:20]
+    w.logits[:] = synth.bf16_bits(x)
+    _assert_select(w, max_low_mismatch_frac=0.25)
+
+
+def test_value_bins_zeros_of_both_signs():
+    """Rows of zeros of both signs: too many near-zero scores to list, all of
+    one value, form one tie group across the two near-zero bins."""
+    V = 40000
+    w = synth.random_select(17, 4, V, 64, dtype="bf16",
+                            settings=dict(do_sample=True, top_p=0.6, repetition_penalty=1.5))
+    z = np.zeros((w.batch, V), np.float32)
+    z[:, 1::3] = -0.0
+    w.logits[:] = synth.bf16_bits(z)
+    _assert_select(w)
+
+
+def test_value_bins_crowded_list():
+    """A history of 3000 distinct ids below 3000: one chunk index of the
+    registers holds more seen ids than one gather per lane reaches; the rest
+    are read after the row."""
+    V, H = 60000, 3000
+    w = synth.random_select(23, 4, V, H, dtype="bf16",
+                            settings=dict(repetition_penalty=1.4, do_sample=True, top_p=0.9))
+    for b in range(w.batch):
+        w.history[b] = np.random.default_rng(b).permutation(H)
+    _assert_select(w)
+
+
+def test_value_bins_past_the_last_bin():
+    """The first chunks of every lane far below the row's maximum: the value
+    bins, placed from those chunks, end below the maximum, and the bisection
+    decides."""
+    V = 50000
+    w = synth.random_select(29, 4, V, 100, dtype="bf16",
+                            settings=dict(do_sample=True, top_p=0.95, repetition_penalty=1.2))
+    x = np.random.default_rng(29).standard_normal((w.batch, V)).astype(np.float32)
+    x[:, :8192] = -1000.0
+    x[:, 9000] = 100.0
+    x[:, 9001] = 99.5
+    w.logits[:] = synth.bf16_bits(x)
+    _assert_select(w)
+
+
 def test_constant_logits_bisection():
     """Every score equal: the top_p boundary and the sample fall inside one
     histogram bin far larger than the collect buffer (bisection path)."""
