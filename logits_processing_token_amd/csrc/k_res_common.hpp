@@ -122,6 +122,96 @@ __device__ inline WalkResult single_walk(bool cut, double start, double goal, co
   return last;  // rounding at the end: the last element within the limit
 }
 
+// The same walk by one whole wave (every lane of the wave calls it; lane 0
+// stores the result).  The individuals' masses are summed in runs of 64 by a
+// wave scan and a ballot names the first position that reaches the goal; the
+// tie group's share is solved in closed form as in the serial walk.  The
+// partial sums are grouped differently from the serial walk's, so the two can
+// differ by rounding where the goal falls within an ulp of a partial sum.
+__device__ __forceinline__ void wave_walk(bool cut, double start, double goal, const BinView &bv,
+                                 const uint64_t *okey, const float *oval, int pos_lim,
+                                 WalkResult *out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double e = (double)bv.e;
+  const int na = bv.n_above, ni = bv.n_ind, ng = bv.n_group;
+  double A = start;
+  int kind = kFail, rank = -1, pos = -1, qk = -1;  // qk: the individual of a kInd result
+  // Individuals [q0, q1) at positions po + q: true when the walk ends among them.
+  auto run = [&](int q0, int q1, int po) -> bool {
+    for (int b0 = q0; b0 < q1; b0 += kWave) {
+      const int q = b0 + lane;
+      const bool in = q < q1 && (cut || po + q <= pos_lim);
+      const uint64_t inb = __ballot(in);
+      if (inb == 0ull) return false;
+      const double P = A + wave_incl_scan_f64_dpp(in ? (double)oval[q] : 0.0);
+      const uint64_t hit = __ballot(in && (cut ? P >= goal : P > goal));
+      const int f = hit ? __ffsll((unsigned long long)hit) - 1 : 63 - __clzll((long long)inb);
+      kind = kInd;
+      qk = b0 + f;
+      pos = po + qk;
+      A = __shfl(P, hit ? f : kWave - 1, kWave);
+      if (hit) return true;
+    }
+    return false;
+  };
+  if (cut) {
+    // (a part that starts with the goal reached adds nothing)
+    bool end = A >= goal || run(0, na, 0);
+    if (!end && ng > 0) {
+      if (A >= goal) {
+        end = true;
+      } else {
+        const double q = (goal - A) / e;
+        long long j = q < (double)ng ? (long long)ceil(q) : (long long)ng;
+        if (j < 1) j = 1;
+        while (j > 1 && A + (double)(j - 1) * e >= goal) --j;
+        while (j < ng && A + (double)j * e < goal) ++j;
+        kind = kGroup;
+        if (j < ng) {
+          rank = (int)j - 1;
+          pos = na + (int)j - 1;
+          A += (double)j * e;
+          end = true;
+        } else {
+          A += (double)ng * e;
+          rank = ng - 1;
+          pos = na + ng - 1;
+        }
+      }
+    }
+    if (!end && !(A >= goal)) run(na, ni, ng);
+  } else {
+    bool end = run(0, na, 0);
+    const int n_eff = pos_lim - na >= ng ? ng : pos_lim - na + 1;
+    if (!end && n_eff > 0) {
+      const double q = (goal - A) / e;
+      long long j = q < (double)n_eff ? (long long)floor(q) : (long long)(n_eff - 1);
+      if (j < 0) j = 0;
+      while (j > 0 && A + (double)j * e > goal) --j;
+      while (j < n_eff - 1 && A + (double)(j + 1) * e <= goal) ++j;
+      kind = kGroup;
+      rank = (int)j;
+      pos = na + (int)j;
+      if (A + (double)(j + 1) * e > goal) {
+        end = true;
+      } else {
+        A += (double)n_eff * e;
+        rank = n_eff - 1;
+        pos = na + n_eff - 1;
+      }
+    }
+    if (!end) run(na, ni, ng);
+    A = 0.0;
+  }
+  if (lane == 0) {
+    out->kind = kind;
+    out->key = qk >= 0 ? okey[qk] : 0ull;
+    out->rank = rank;
+    out->pos = pos;
+    out->acc = kind == kFail ? (cut ? A : 0.0) : A;
+  }
+}
+
 // Slot on the list of seen id v (alive seen ids are listed in id order;
 // woff[w] is the list offset of mask word w).
 __device__ __forceinline__ int list_slot(int v, const uint32_t *amask, const uint16_t *woff) {

@@ -103,10 +103,12 @@ struct VMapP {
   u16x2 bk1, top;
   uint32_t lb, c7fff, czm, c8000;
 };
-__device__ __forceinline__ u16x2 vkeys2(uint32_t w, const VMapP &m) {
+__device__ __forceinline__ u16x2 vmag2(uint32_t w, const VMapP &m) {  // the clamped magnitudes
+  return __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, w) & __builtin_bit_cast(u16x2, m.c7fff),
+                                       __builtin_bit_cast(u16x2, m.czm));
+}
+__device__ __forceinline__ u16x2 vkeys2(uint32_t w, u16x2 t, const VMapP &m) {
   const u16x2 u = __builtin_bit_cast(u16x2, w);
-  const u16x2 t = __builtin_elementwise_sub_sat(u & __builtin_bit_cast(u16x2, m.c7fff),
-                                                __builtin_bit_cast(u16x2, m.czm));
   const i16x2 sx = __builtin_bit_cast(i16x2, u) >> (i16x2)(int16_t)15;
   uint32_t k;  // t ^ sx ^ 0x8000 in one three-input operation
   asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96"
@@ -114,9 +116,12 @@ __device__ __forceinline__ u16x2 vkeys2(uint32_t w, const VMapP &m) {
       : "v"(__builtin_bit_cast(uint32_t, t)), "v"(__builtin_bit_cast(uint32_t, sx)), "s"(m.c8000));
   return __builtin_bit_cast(u16x2, k);
 }
-__device__ __forceinline__ uint32_t vaddr2(uint32_t w, const VMapP &m) {
+__device__ __forceinline__ u16x2 vkeys2(uint32_t w, const VMapP &m) {
+  return vkeys2(w, vmag2(w, m), m);
+}
+__device__ __forceinline__ uint32_t vaddr2(uint32_t w, u16x2 t, const VMapP &m) {
   const u16x2 idx =
-      __builtin_elementwise_min(__builtin_elementwise_sub_sat(vkeys2(w, m), m.bk1), m.top);
+      __builtin_elementwise_min(__builtin_elementwise_sub_sat(vkeys2(w, t, m), m.bk1), m.top);
   uint32_t a;
   asm("v_pk_mad_u16 %0, %1, 4, %2 op_sel_hi:[1,0,1]"
       : "=v"(a)
@@ -329,11 +334,25 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   const uint32_t ninf = sconst(0xFF80FF80u);
   VMap vm;
   VMapP vp;
+  // A near-zero score has a clamped magnitude of 0: every lane keeps the
+  // least of its halves (the magnitudes stay below the binary16 infinity,
+  // so a binary16 minimum orders them as integers), which tells the lanes
+  // that hold one.
+  uint32_t zacc = 0x7BFF7BFFu;
   auto count_chunk = [&](uint4 c) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    u16x2 t[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = vmag2(w[q], vp);
+    asm("v_pk_minimum3_f16 %0, %0, %1, %2"
+        : "+v"(zacc)
+        : "v"(__builtin_bit_cast(uint32_t, t[0])), "v"(__builtin_bit_cast(uint32_t, t[1])));
+    asm("v_pk_minimum3_f16 %0, %0, %1, %2"
+        : "+v"(zacc)
+        : "v"(__builtin_bit_cast(uint32_t, t[2])), "v"(__builtin_bit_cast(uint32_t, t[3])));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t a2 = vaddr2(w[q], vp);
+      const uint32_t a2 = vaddr2(w[q], t[q], vp);
       lds_add(a2 & 0xFFFFu, 1u);
       lds_add(a2 >> 16, 1u);
     }
@@ -456,37 +475,52 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     if (tid == 0) vs.nz = 0;
     __syncthreads();
     float zlo = INFINITY, zhi = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const uint4 c = launder(reg[i]);
-      const int g = tid + i * NT;
-      // (a chunk is looked into only if one of its magnitudes is in reach:
-      // max(|u| - Z, 0) is 0 in some half)
+    // Lanes that saw one: which of their chunks hold one (a magnitude within
+    // reach: max(|u| - Z, 0) is 0 in some half), one bit each; then those
+    // chunks one at a time, picked from the registers by index.  (Short
+    // code: it runs cold, on few rows and few waves.)
+    if ((zacc & 0xFFFFu) == 0u || (zacc >> 16) == 0u) {
       const u16x2 zm = __builtin_bit_cast(u16x2, kZoneMag | (kZoneMag << 16));
       const u16x2 msk = __builtin_bit_cast(u16x2, 0x7FFF7FFFu);
-      u16x2 t = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.x) & msk, zm);
-      t = __builtin_elementwise_min(t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.y) & msk, zm));
-      t = __builtin_elementwise_min(t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.z) & msk, zm));
-      t = __builtin_elementwise_min(t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, c.w) & msk, zm));
-      if (t.x != 0 && t.y != 0) continue;
+      auto near = [&](uint32_t w) {  // per half: 0 where the magnitude is in reach
+        return __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, w) & msk, zm);
+      };
+      uint32_t zb = 0u;
 #pragma unroll
-      for (int j = 0; j < EPC; ++j) {
-        const float x = E::get(c, j);
-        if (fabsf(x) <= kZone) {
-          zlo = fminf(zlo, x);
-          zhi = fmaxf(zhi, x);
-          const int slot = atomicAdd(&vs.nz, 1);
-          if (slot < kZoneCap) {
-            s.list_id[n_list + slot] = g * EPC + j;
-            s.list_val[n_list + slot] = x;
+      for (int i = 0; i < R; ++i) {
+        const uint4 c = reg[i];
+        u16x2 t = __builtin_elementwise_min(near(c.x), near(c.y));
+        t = __builtin_elementwise_min(t, __builtin_elementwise_min(near(c.z), near(c.w)));
+        zb |= (t.x == 0 || t.y == 0) ? 1u << i : 0u;
+      }
+      while (zb) {
+        const int i = __ffs(zb) - 1;
+        zb &= zb - 1u;
+        uint4 c = reg[0];
+#pragma unroll
+        for (int k = 1; k < R; ++k)
+          if (i == k) c = reg[k];
+        const int g = tid + i * NT;
+        for (int j = 0; j < EPC; ++j) {
+          const float x = E::get(c, j);
+          if (fabsf(x) <= kZone) {
+            zlo = fminf(zlo, x);
+            zhi = fmaxf(zhi, x);
+            const int slot = atomicAdd(&vs.nz, 1);
+            if (slot < kZoneCap) {
+              s.list_id[n_list + slot] = g * EPC + j;
+              s.list_val[n_list + slot] = x;
+            }
           }
         }
       }
     }
-    zlo = -uni(block_max_f32<NT>(-zlo, sh.red_f32));
-    zhi = uni(block_max_f32<NT>(zhi, sh.red_f32));
-    const int nz = uni(vs.nz);
     __syncthreads();
+    const int nz = uni(vs.nz);
+    if (nz > kZoneCap) {  // too many to list: are they all one value?
+      zlo = -uni(block_max_f32<NT>(-zlo, sh.red_f32));
+      zhi = uni(block_max_f32<NT>(zhi, sh.red_f32));
+    }
     if (nz <= kZoneCap) {
       n_ind = n_list + nz;
       if (tid == 0) {  // the members are individuals now
@@ -647,6 +681,21 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     return true;
   };
 
+  // The walks run on wave 0 alone, its share of the row parked in LDS
+  // meanwhile: the walk gets the registers the row held.  (The fence keeps
+  // the compiler from forwarding the stored chunks past the walk.)
+  uint4 *park = reinterpret_cast<uint4 *>(smem + a.off_park);
+  auto park_row = [&]() {
+#pragma unroll
+    for (int i = 0; i < R; ++i) park[i * kWave + lane] = reg[i];
+    asm volatile("" ::: "memory");
+  };
+  auto unpark_row = [&]() {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < R; ++i) reg[i] = park[i * kWave + lane];
+  };
+
   double Wp = W;
   int cut_kind = kNone, draw_kind = kNone;
   int cut_pos = 0x7FFFFFFF;
@@ -656,7 +705,11 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     if (!view_bin(bp)) {
       fallback = true;
     } else {
-      if (tid == 0) vs.walk[0] = single_walk(true, C_bp1, pw, vs.view, okey, oval, 0x7FFFFFFF);
+      if (uni(wid) == 0) {
+        park_row();
+        wave_walk(true, C_bp1, pw, vs.view, okey, oval, 0x7FFFFFFF, &vs.walk[0]);
+        unpark_row();
+      }
       __syncthreads();
       cut_kind = uni(vs.walk[0].kind);
       if (cut_kind == kFail) fallback = true;
@@ -693,17 +746,20 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     bs_start = uni(sh.sbase);
     if (bs < 0) {
       fallback = true;  // rounding left the target outside every bin
-    } else if (bs == bp && bp >= 0) {
-      // same bin as the boundary: the view is still in place
-      if (tid == 0) vs.walk[1] = single_walk(false, bs_start, target, vs.view, okey, oval, cut_pos);
-      __syncthreads();
-      draw_kind = uni(vs.walk[1].kind);
-    } else if (!view_bin(bs)) {
-      fallback = true;
     } else {
-      if (tid == 0) vs.walk[1] = single_walk(false, bs_start, target, vs.view, okey, oval, 0x7FFFFFFF);
-      __syncthreads();
-      draw_kind = uni(vs.walk[1].kind);
+      // (the same bin as the boundary: the view is still in place)
+      const bool same = bs == bp && bp >= 0;
+      if (!same && !view_bin(bs)) {
+        fallback = true;
+      } else {
+        if (uni(wid) == 0) {
+          park_row();
+          wave_walk(false, bs_start, target, vs.view, okey, oval, same ? cut_pos : 0x7FFFFFFF, &vs.walk[1]);
+          unpark_row();
+        }
+        __syncthreads();
+        draw_kind = uni(vs.walk[1].kind);
+      }
     }
     if (draw_kind == kFail) fallback = true;
   }
@@ -889,7 +945,7 @@ static hipError_t launch_vres_t(const SelectArgs &a, size_t lds, hipStream_t st)
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_vres<R>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kSelectMaxDynLds);
+                                       (int)kVMaxDynLds);
     if (e != hipSuccess) return e;
     attr = true;
   }

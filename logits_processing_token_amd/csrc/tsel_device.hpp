@@ -126,6 +126,25 @@ __device__ __forceinline__ double wave_incl_scan_f64(double v) {
   return v;
 }
 
+// The same by row moves: each step moves the two halves of a double.
+template <int CTRL, int ROWS, bool BC>
+__device__ __forceinline__ double dpp_move_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROWS, 0xF, BC);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROWS, 0xF, BC);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+__device__ __forceinline__ double wave_incl_scan_f64_dpp(double v) {
+  v += dpp_move_f64<0x111, 0xF, true>(v);   // row_shr:1
+  v += dpp_move_f64<0x112, 0xF, true>(v);   // row_shr:2
+  v += dpp_move_f64<0x114, 0xF, true>(v);   // row_shr:4
+  v += dpp_move_f64<0x118, 0xF, true>(v);   // row_shr:8
+  v += dpp_move_f64<0x142, 0xA, false>(v);  // row_bcast:15
+  v += dpp_move_f64<0x143, 0xC, false>(v);  // row_bcast:31
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // waits for every global load the wave has in flight; a kernel that stages

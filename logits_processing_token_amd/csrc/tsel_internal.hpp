@@ -12,6 +12,7 @@ constexpr int kSelectThreads = 1024;        // one workgroup (16 wave64s) per ro
 constexpr int kLdsBytes = 160 * 1024;       // LDS of one gfx950 compute unit
 constexpr int kSelectStaticLds = 12288;     // upper bound of the kernels' static LDS
 constexpr int kSelectMaxDynLds = kLdsBytes - kSelectStaticLds;
+constexpr int kVMaxDynLds = kLdsBytes;     // the value-bin kernel has no static LDS
 constexpr int kMaxVerifyK = 1023;           // drafts per row a verify call accepts
 
 // Mass histogram of the full path: bins cover masses from 2^-kBinBelow to
@@ -71,6 +72,7 @@ struct SelectArgs {
   uint32_t off_woff;        // resident path: list offset of each thread's mask words
   uint32_t off_kmask;       // kill mask (0 but on the value-bin path)
   uint32_t off_sh;          // value-bin path: its shared scalars (no static LDS)
+  uint32_t off_park;        // value-bin path: one wave's share of the row, parked
 };
 
 hipError_t launch_greedy(const SelectArgs &a, size_t lds, hipStream_t s);
