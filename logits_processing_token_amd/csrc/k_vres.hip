@@ -165,6 +165,8 @@ __device__ __forceinline__ void lds_add(uint32_t addr, uint32_t v) {
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+constexpr int kTieCap = 128;
+
 struct VShared {
   BinView view;
   WalkResult walk[2];
@@ -174,7 +176,7 @@ struct VShared {
   int gid[2];
   int wtot[2][NW][16];
   int n_ind_b, n_tie_b, n_above_b;
-  int ltie;
+  int tie_id[kTieCap];  // ids of the viewed bin's individuals equal to its value
   int nz;
   uint32_t kmax[NW];
 };
@@ -647,7 +649,8 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       const float y = s.list_val[k];
       if (ind_bin(y) != b) continue;
       if (y == v) {
-        atomicAdd(&vs.n_tie_b, 1);
+        const int slot = atomicAdd(&vs.n_tie_b, 1);
+        if (slot < kTieCap) vs.tie_id[slot] = s.list_id[k];
       } else {
         const int slot = atomicAdd(&vs.n_ind_b, 1);
         if (slot < kGatherCap) {
@@ -772,30 +775,37 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   const bool g1 = !fallback && draw_kind == kGroup;
   if (g1) {
     if (tid == 0) {
-      vs.gv[1] = bs_v;
       vs.gk[1] = vs.walk[1].rank + 1;
       vs.gi[1] = -1;
       vs.gid[1] = -1;
-      vs.ltie = 0;
     }
-    __syncthreads();
-    const float vv = uni(vs.gv[1]);
-    // seen ids whose penalized score equals the group value join the group
-    // (rare): which chunks of which thread hold one, 16 bits per thread,
-    // two threads a word, in the (now idle) ordered-view buffer
+    const float vv = bs_v;
+    // Individuals (seen ids, penalized) equal to the group value join the
+    // group: the view of the draw's bin counted them and kept their ids
+    // while they fit.  Which chunks of which thread hold one, 16 bits per
+    // thread, two threads a word, in the (now idle) ordered-view buffer.
+    const int ntie = uni(vs.n_tie_b);
+    const bool ltie_all = ntie > 0;
     uint32_t *tiew = reinterpret_cast<uint32_t *>(okey);
-    for (int q = tid; q < NT / 2; q += NT) tiew[q] = 0u;
-    __syncthreads();
-    for (int k = tid; k < n_list; k += NT) {
-      if (s.list_val[k] == vv) {
-        vs.ltie = 1;
-        const int gg = s.list_id[k] / EPC, t = gg % NT, ci = gg / NT;
+    uint32_t tmask = 0u;
+    if (ltie_all) {
+      for (int q = tid; q < NT / 2; q += NT) tiew[q] = 0u;
+      __syncthreads();
+      auto mark = [&](int id) {
+        const int gg = id / EPC, t = gg % NT, ci = gg / NT;
         atomicOr(&tiew[t >> 1], 1u << ((t & 1) * 16 + ci));
+      };
+      if (ntie <= kTieCap) {
+        if (tid < ntie) mark(vs.tie_id[tid]);
+      } else {
+        for (int k = tid; k < n_list; k += NT)
+          if (s.list_val[k] == vv) mark(s.list_id[k]);
       }
+      __syncthreads();
+      tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
+    } else {
+      __syncthreads();
     }
-    __syncthreads();
-    const bool ltie_all = uni(vs.ltie) != 0;
-    const uint32_t tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
     // One pass over the registers: every lane counts the members in each of
     // its chunks (a nonzero value by its bf16 pattern, a zero one by the
     // pattern less the sign; seen ids equal to the value added from the
@@ -818,20 +828,22 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       }
       return mb;
     };
+    // (a member leaves a zero half in (w & msk) ^ pat; 1 - that half,
+    // saturated, is 1 exactly there; the four words' halves are added in
+    // place and the two halves by a dot product with (1, 1))
+    const u16x2 one2 = {1, 1};
+    auto members = [&](const uint4 &c) -> uint32_t {
+      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+      u16x2 y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        y[q] = __builtin_elementwise_sub_sat(one2, __builtin_bit_cast(u16x2, (w[q] & msk) ^ pat));
+      return __builtin_amdgcn_udot2((y[0] + y[1]) + (y[2] + y[3]), one2, 0u, false);
+    };
     uint32_t cb[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const uint4 c = launder(reg[i]);
-      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-      uint32_t n = 0u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t x = (w[q] & msk) ^ pat;
-        // a zero half of x is a member: bit 15 of (x & 7FFF) + 7FFF, or'ed
-        // with x, is clear exactly there
-        n += __popc(~(((x & 0x7FFF7FFFu) + 0x7FFF7FFFu) | x) & 0x80008000u);
-      }
-      cb[i >> 2] |= n << ((i & 3) * 8);
+      cb[i >> 2] |= members(launder(reg[i])) << ((i & 3) * 8);
       __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: the row holds the registers
     }
     if (ltie_all) {
@@ -888,23 +900,20 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       __syncthreads();
       const int ur = uni(vs.gw[1]);
       if (wid == ur / 4 && (lane >> 4) == ur % 4) {
-        // members among this lane's elements of chunk ii (every chunk is
-        // tested with a constant index: selecting reg[ii] would become a
-        // run-time index and send the whole row through scratch memory)
+        // members among this lane's elements of chunk ii (the chunk picked
+        // by a chain of selects: indexing reg[ii] at run time would send
+        // the whole row through scratch memory)
+        uint4 c = reg[0];
+#pragma unroll
+        for (int k = 1; k < R; ++k)
+          if (ii == k) c = reg[k];
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
         uint32_t mbits = 0u;
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const uint4 c = launder(reg[i]);
-          const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-          uint32_t mb = 0u;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t x = (w[q] & msk) ^ pat;
-            mb |= ((x & 0xFFFFu) == 0u ? 1u : 0u) << (2 * q);
-            mb |= ((x >> 16) == 0u ? 1u : 0u) << (2 * q + 1);
-          }
-          mbits = i == ii ? mb : mbits;
-          __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t x = (w[q] & msk) ^ pat;
+          mbits |= ((x & 0xFFFFu) == 0u ? 1u : 0u) << (2 * q);
+          mbits |= ((x >> 16) == 0u ? 1u : 0u) << (2 * q + 1);
         }
         if (ltie_all) mbits |= list_ties(ii);
         const int cnt_l = __popc(mbits);
