@@ -179,6 +179,9 @@ struct VShared {
   int tie_id[kTieCap];  // ids of the viewed bin's individuals equal to its value
   int nz;
   uint32_t kmax[NW];
+  float fmax[NW];
+  int ovf;
+  int view_ntie;  // the view's individuals equal to its value
 };
 
 template <int NT_>
@@ -417,28 +420,34 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     s.list_val[k] = y;
     lmax = fmaxf(lmax, y);
   }
-  // fold the copies; the highest occupied bin
-  uint32_t c4[BPT];
-  auto fold = [&]() {
-    int top_b = 0;
+  // fold the copies (each thread its own bins, so no barrier between the
+  // reads and the writes); the highest occupied bin and the seen ids' top
+  // score in one workgroup reduction
+  uint32_t top_b = 0u;
 #pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-      const int b = tid * BPT + q;
-      c4[q] = 0u;
-      if (b < NB) {
+  for (int q = 0; q < BPT; ++q) {
+    const int b = tid * BPT + q;
+    if (b < NB) {
+      uint32_t c = 0u;
 #pragma unroll
-        for (int k = 0; k < kVCopies; ++k) c4[q] += cnt[k * kVStride + b];
-        if (c4[q] && b >= 1) top_b = b;
-      }
+      for (int k = 0; k < kVCopies; ++k) c += cnt[k * kVStride + b];
+      cnt[b] = c;
+      if (c && b >= 1) top_b = (uint32_t)b;
     }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < BPT; ++q)
-      if (tid * BPT + q < NB) cnt[tid * BPT + q] = c4[q];
-    return top_b;
-  };
-  const int btop = (int)uni(block_max_u32_lds<NT>((uint32_t)fold(), vs.kmax));
-  lmax = uni(block_max_f32<NT>(lmax, sh.red_f32));
+  }
+  {
+    const uint32_t tw = wave_max_u32_uni(top_b);
+    const float lw = wave_max_f32_uni(lmax);
+    if (lane == 0) {
+      vs.kmax[wid] = tw;
+      vs.fmax[wid] = lw;
+    }
+    lds_barrier();
+    top_b = lane < NW ? vs.kmax[lane] : 0u;
+    lmax = lane < NW ? vs.fmax[lane] : -INFINITY;
+  }
+  const int btop = (int)wave_max_u32_uni(top_b);
+  lmax = wave_max_f32_uni(lmax);
   const int zn = vm.zn, zp = vm.zp;  // the near-zero bins (or -1)
   // Scores past the last bin (the row's maximum far above its first
   // chunks'): the bisection decides.
@@ -554,8 +563,8 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   };
   auto ind_bin = [&](float y) { return vbin(vkey_floor(y), vm); };
   for (int b = tid; b < NB; b += NT) lfix[b] = 0ull;
+  if (tid == 0) vs.ovf = 0;
   __syncthreads();
-  int ovf = 0;
   for (int k = tid; k < n_ind; k += NT) {
     const float y = s.list_val[k];
     const int b = ind_bin(y);
@@ -565,11 +574,12 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     const int ek = (int)((eb >> 23) & 0xFFu);
     if (eu == 0 || ek == 0) continue;  // below 2^-126 of the maximum: nothing
     const int sft = ek - eu;
-    if (sft < 0 || sft > 24) { ovf = 1; continue; }
+    if (sft < 0 || sft > 24) { vs.ovf = 1; continue; }
     atomicAdd(reinterpret_cast<unsigned long long *>(&lfix[b]),
               (unsigned long long)((eb & 0x7FFFFFu) | 0x800000u) << sft);
   }
-  if (uni(block_sum_i32<NT>(ovf, sh.red_i32)) != 0) fallback = true;
+  __syncthreads();
+  if (uni(vs.ovf) != 0) fallback = true;
   // bin masses, in place of the fixed-point sums
   double part = 0.0;
 #pragma unroll
@@ -594,29 +604,32 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // ---- 4. cumulative masses: the boundary bin and the draw bin -------------
   // Thread t owns bins [t*BPT, t*BPT + BPT); C(b) = mass of bins >= b.
   double incl;  // mass of bins owned by threads >= tid
+  double W;     // the row's mass (every thread sums the wave totals alike)
   {
-    double v = part;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double t = __shfl_down(v, o, kWave);
-      if (lane + o < kWave) v += t;
-    }
+    const double v = wave_suffix_scan_f64_dpp(part);
     if (lane == 0) sh.red_f64[wid] = v;
+    if (tid == 0) {
+      sh.bin_p = -1;
+      vs.n_ind_b = 0;  // (the counters of the first view)
+      vs.n_tie_b = 0;
+      vs.n_above_b = 0;
+    }
     __syncthreads();
     double after = 0.0;
-    for (int q = wid + 1; q < NW; ++q) after += sh.red_f64[q];
+    W = 0.0;
+#pragma unroll
+    for (int q = NW - 1; q >= 0; --q) {
+      const double t = sh.red_f64[q];
+      if (q > wid) after += t;
+      W += t;
+    }
     incl = v + after;
+    W = uni(W);
   }
   // (the mass above this thread's bins waits in LDS: registers are scarce
   // while the row is held)
   double *above = reinterpret_cast<double *>(smem + kVAboveOff);
   above[tid] = incl - part;
-  if (tid == 0) {
-    sh.wprime = incl;
-    sh.bin_p = -1;
-  }
-  __syncthreads();
-  const double W = uni(sh.wprime);
   const bool use_top_p = a.top_p < 1.0f;
   const double pw = (double)a.top_p * W;
   const double u = (double)a.uniforms[row];
@@ -637,14 +650,11 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // View of bin b (all threads): its value, its individuals other than the
   // value ordered by key into okey / oval, the tie group's size.  Returns
   // false when the bin has more individuals than fit.
+  // The counters start at zero (cleared before an earlier barrier); the
+  // view is written by thread 0 and read by its own wave until the next
+  // barrier.
   auto view_bin = [&](int b) -> bool {
-    if (tid == 0) {
-      vs.n_ind_b = 0;
-      vs.n_tie_b = 0;
-      vs.n_above_b = 0;
-    }
     const float v = bin_value(b);
-    __syncthreads();
     for (int k = tid; k < n_ind; k += NT) {
       const float y = s.list_val[k];
       if (ind_bin(y) != b) continue;
@@ -679,8 +689,8 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       vs.view.n_ind = ni;
       vs.view.n_above = na;
       vs.view.n_group = (int)cnt[b] + vs.n_tie_b;
+      vs.view_ntie = vs.n_tie_b;
     }
-    __syncthreads();
     return true;
   };
 
@@ -729,6 +739,9 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     if (tid == 0) {
       sh.bin_hi = -1;
       sh.sbase = -1.0;
+      vs.n_ind_b = 0;  // (the counters of a second view)
+      vs.n_tie_b = 0;
+      vs.n_above_b = 0;
     }
     __syncthreads();
     {
@@ -784,7 +797,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     // group: the view of the draw's bin counted them and kept their ids
     // while they fit.  Which chunks of which thread hold one, 16 bits per
     // thread, two threads a word, in the (now idle) ordered-view buffer.
-    const int ntie = uni(vs.n_tie_b);
+    const int ntie = uni(vs.view_ntie);
     const bool ltie_all = ntie > 0;
     uint32_t *tiew = reinterpret_cast<uint32_t *>(okey);
     uint32_t tmask = 0u;

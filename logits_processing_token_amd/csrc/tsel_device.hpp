@@ -145,6 +145,48 @@ __device__ __forceinline__ double wave_incl_scan_f64_dpp(double v) {
   return v;
 }
 
+// Suffix sums within the wave (lane l gets the sum over lanes >= l): row
+// moves to the left within each row of 16 lanes, then the totals of the rows
+// above added from scalar registers.
+__device__ __forceinline__ double wave_suffix_scan_f64_dpp(double v) {
+  v += dpp_move_f64<0x101, 0xF, true>(v);  // row_shl:1
+  v += dpp_move_f64<0x102, 0xF, true>(v);  // row_shl:2
+  v += dpp_move_f64<0x104, 0xF, true>(v);  // row_shl:4
+  v += dpp_move_f64<0x108, 0xF, true>(v);  // row_shl:8
+  // (the first lane of row r now holds row r's total)
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  auto lane_value = [&](int l) {
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, l);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), l);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+  };
+  const double t3 = lane_value(48), t2 = lane_value(32), t1 = lane_value(16);
+  const double s3 = t3, s2 = t2 + t3, s1 = t1 + s2;
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  return v + (row == 0 ? s1 : row == 1 ? s2 : row == 2 ? s3 : 0.0);
+}
+
+// Maximum over the wave by row moves (quad swaps, half-row and row mirrors,
+// then the row broadcasts), read from the last lane into a scalar register.
+__device__ __forceinline__ float wave_max_f32_uni(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_uni(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // waits for every global load the wave has in flight; a kernel that stages
