@@ -268,18 +268,10 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   float *oval = reinterpret_cast<float *>(okey + kGatherCap);
   uint64_t *gkey = reinterpret_cast<uint64_t *>(oval + kGatherCap);
   float *gval = reinterpret_cast<float *>(gkey + kGatherCap);
-  // While the small loads fly: clear the histogram and the masks.  Both
-  // masks run on to byte R * NT (one byte per chunk slot of the registers),
-  // the kill mask with every slot past the row's ids marked removed, so that
-  // chunk i's bytes sit at fixed offsets.
-  {
-    uint4 *c4 = reinterpret_cast<uint4 *>(cnt);
-    for (int b = tid; b < kVCopies * kVStride / 4; b += NT) c4[b] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  stage_clear(s, sh, R * NT / 4, (V + EPC - 1) / EPC, R * NT / 4);
   // The row through a buffer resource (one offset register per lane, the
   // chunk's offset in a scalar; chunks past the row read as 0): its first
-  // chunks are asked for now, the others as the chunks are counted.
+  // chunks are asked for now, before the clearing below, the others as the
+  // chunks are counted.
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, NG * 16, 0x00020000);
   auto load_chunk = [&](int i) {
@@ -289,6 +281,15 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   uint4 reg[R];
 #pragma unroll
   for (int i = 0; i < PIPE0; ++i) reg[i] = load_chunk(i);
+  // While the small loads fly: clear the histogram and the masks.  Both
+  // masks run on to byte R * NT (one byte per chunk slot of the registers),
+  // the kill mask with every slot past the row's ids marked removed, so that
+  // chunk i's bytes sit at fixed offsets.
+  {
+    uint4 *c4 = reinterpret_cast<uint4 *>(cnt);
+    for (int b = tid; b < kVCopies * kVStride / 4; b += NT) c4[b] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  stage_clear(s, sh, R * NT / 4, (V + EPC - 1) / EPC, R * NT / 4);
   if (row_prologue_after_lens(a, row, ri)) return;
   if (lds_addr(smem) + kVHistBytes > 65536) {  // (not with this block's layout)
     if (tid == 0) a.out_tokens[row] = kPending;
@@ -302,11 +303,13 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // after its chunk was asked for, so that they read the lines that chunk
   // brings in.  lbv[i]: the first list slot of chunk index i (the list is in
   // id order; chunk index i holds ids [i * NT * EPC, (i + 1) * NT * EPC)).
+  // (lane i reads entry i; the entries then come out of the lanes)
   int lbv[R + 1];
+  {
+    const int w = lane * (NT * EPC / 32);
+    const int lv = lane <= R ? (w < a.mw ? (int)woff[w] : n_list) : 0;
 #pragma unroll
-  for (int i = 0; i <= R; ++i) {
-    const int w = i * (NT * EPC / 32);
-    lbv[i] = w < a.mw ? uni((int)woff[w]) : n_list;
+    for (int i = 0; i <= R; ++i) lbv[i] = __builtin_amdgcn_readlane(lv, i);
   }
   bool list_ovf = false;
 #pragma unroll
