@@ -301,19 +301,22 @@ __device__ __forceinline__ void early_loads(const SelectArgs &a, int row, const 
     e.km[k] = m0[k] | m1[k];
     e.kbeg[k] = m2[k];
   }
-  // the tail: every lane reads the same few elements (0 past the row,
-  // replaced by -inf)
+  // the tail: every lane reads the same partial chunk, its whole words by
+  // one 16-byte load through a resource that ends at the row's last whole
+  // word (the words past it read as 0), and the last element of an odd bf16
+  // row by itself; elements past the row become -inf
   const int tail_n = V - NG * EPC;
-  const __amdgpu_buffer_rsrc_t rr = buf_rsrc(rowp, (uint32_t)V * (DT == 1 ? 2u : 4u));
+  const uint32_t row_bytes = (uint32_t)V * (DT == 1 ? 2u : 4u);
+  const u32x4_t tv = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(rowp, row_bytes & ~3u), NG * 16, 0, 0);
+  const uint32_t last =
+      DT == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(rowp, row_bytes), (V - 1) * 2, 0, 0) : 0u;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) e.tw[q] = E::kNegInf;
+  for (int q = 0; q < 4; ++q) e.tw[q] = tv[q];
+  const uint32_t ninf = DT == 1 ? 0xFF80u : 0xFF800000u;
 #pragma unroll
-  for (int j = 0; j < EPC - 1; ++j) {
-    const uint32_t bits =
-        DT == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr, (NG * EPC + j) * 2, 0, 0)
-                : __builtin_amdgcn_raw_buffer_load_b32(rr, (NG * EPC + j) * 4, 0, 0);
-    const uint32_t ninf = DT == 1 ? 0xFF80u : 0xFF800000u;
-    put_elem<DT>(e.tw, j, j < tail_n ? bits : ninf);
+  for (int j = 0; j < EPC; ++j) {
+    if (j >= tail_n) put_elem<DT>(e.tw, j, ninf);
+    else if (DT == 1 && (V & 1) && j == tail_n - 1) put_elem<DT>(e.tw, j, last);
   }
 }
 

@@ -251,8 +251,13 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   const int NG = V / EPC;  // whole chunks (>= 1 on this path)
   const char *rowp = a.logits + (int64_t)row * a.row_bytes;
   // ---- 0. the small loads: lengths, history, masks, tail --------------------
+  // (the lengths are asked for first and read only after the clearing
+  // below, so that their latency hides behind it; the loads issued in
+  // between do not depend on them)
   RowInfo ri;
-  row_lens_vector(a, row, ri);
+  const int len0 = __builtin_nontemporal_load(a.lens + row);
+  const int len1 = __builtin_nontemporal_load(a.lens + a.B + row);
+  const int len2 = __builtin_nontemporal_load(a.lens + 2 * a.B + row);
   Early ea;
   early_loads<1>(a, row, rowp, ea);
   const int tail_n = V - NG * EPC;
@@ -290,6 +295,9 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     for (int b = tid; b < kVCopies * kVStride / 4; b += NT) c4[b] = make_uint4(0u, 0u, 0u, 0u);
   }
   stage_clear(s, sh, R * NT / 4, (V + EPC - 1) / EPC, R * NT / 4);
+  ri.L = __builtin_amdgcn_readfirstlane(len0);
+  ri.P = __builtin_amdgcn_readfirstlane(len1);
+  ri.M = __builtin_amdgcn_readfirstlane(len2);
   if (row_prologue_after_lens(a, row, ri)) return;
   if (lds_addr(smem) + kVHistBytes > 65536) {  // (not with this block's layout)
     if (tid == 0) a.out_tokens[row] = kPending;
