@@ -149,7 +149,11 @@ __device__ __forceinline__ void wave_walk(bool cut, double start, double goal, c
       kind = kInd;
       qk = b0 + f;
       pos = po + qk;
-      A = __shfl(P, hit ? f : kWave - 1, kWave);
+      const int src = hit ? f : kWave - 1;  // (uniform: read that lane directly)
+      const unsigned long long pb = (unsigned long long)__double_as_longlong(P);
+      const unsigned plo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)pb, src);
+      const unsigned phi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(pb >> 32), src);
+      A = __longlong_as_double((long long)(((unsigned long long)phi << 32) | plo));
       if (hit) return true;
     }
     return false;
@@ -161,7 +165,9 @@ __device__ __forceinline__ void wave_walk(bool cut, double start, double goal, c
       if (A >= goal) {
         end = true;
       } else {
-        const double q = (goal - A) / e;
+        // (a first guess by the reciprocal, by the division when the mass is
+        // below the normal range; the loops below settle j exactly)
+        const double q = bv.e >= 1.17549435e-38f ? (goal - A) * (double)__frcp_rn(bv.e) : (goal - A) / e;
         long long j = q < (double)ng ? (long long)ceil(q) : (long long)ng;
         if (j < 1) j = 1;
         while (j > 1 && A + (double)(j - 1) * e >= goal) --j;
@@ -184,7 +190,7 @@ __device__ __forceinline__ void wave_walk(bool cut, double start, double goal, c
     bool end = run(0, na, 0);
     const int n_eff = pos_lim - na >= ng ? ng : pos_lim - na + 1;
     if (!end && n_eff > 0) {
-      const double q = (goal - A) / e;
+      const double q = bv.e >= 1.17549435e-38f ? (goal - A) * (double)__frcp_rn(bv.e) : (goal - A) / e;
       long long j = q < (double)n_eff ? (long long)floor(q) : (long long)(n_eff - 1);
       if (j < 0) j = 0;
       while (j > 0 && A + (double)j * e > goal) --j;

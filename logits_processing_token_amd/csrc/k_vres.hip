@@ -827,8 +827,6 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       }
       __syncthreads();
       tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
-    } else {
-      __syncthreads();
     }
     // One pass over the registers: every lane counts the members in each of
     // its chunks (a nonzero value by its bf16 pattern, a zero one by the
@@ -897,33 +895,35 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       if (lane == kWave - 1) vs.wtot[0][0][wid] = rinc;  // the chunk index's total
     }
     __syncthreads();
-    if (tid < 16) {
-      const int T = tid < R ? vs.wtot[0][0][tid] : 0;
-      int inc = T;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const int y = __shfl_up(inc, o, 16);
-        if (tid >= o) inc += y;
-      }
+    // (inclusive sums within a row of 16 lanes by row moves)
+    auto row16_incl_scan = [](int v) {
+      v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+      v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+      v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+      v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+      return v;
+    };
+    if (wid == 0) {
+      const int T = lane < R ? vs.wtot[0][0][lane] : 0;
+      const int inc = row16_incl_scan(T);
       const int k = vs.gk[1];
-      if (inc - T < k && k <= inc) {
-        vs.gi[1] = tid;
+      if (lane < 16 && inc - T < k && k <= inc) {
+        vs.gi[1] = lane;
         vs.gr[1] = k - (inc - T);
       }
     }
     __syncthreads();
     const int ii = uni(vs.gi[1]);
     if (ii >= 0) {
-      if (wid == ii) {
-        const int k = uni(vs.gr[1]);
-        if (rinc - rc < k && k <= rinc) {
-          vs.gw[1] = lane;             // the row
-          vs.gk[0] = k - (rinc - rc);  // the member's rank in it
-        }
-      }
-      __syncthreads();
-      const int ur = uni(vs.gw[1]);
-      if (wid == ur / 4 && (lane >> 4) == ur % 4) {
+      // every wave scans the rows of chunk index ii again and names the row
+      // that holds the member; its wave goes on
+      const int k = uni(vs.gr[1]);
+      const int rc2 = (int)((rsum[lane * 4 + (ii >> 2)] >> ((ii & 3) * 8)) & 0xFFu);
+      const int rinc2 = wave_incl_scan_i32(rc2);
+      const uint64_t hit = __ballot(rinc2 - rc2 < k && k <= rinc2);
+      const int ur = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+      const int r0 = k - __builtin_amdgcn_readlane(rinc2 - rc2, ur < 0 ? 0 : ur);  // rank in its row
+      if (ur >= 0 && wid == ur / 4 && (lane >> 4) == ur % 4) {
         // members among this lane's elements of chunk ii (the chunk picked
         // by a chain of selects: indexing reg[ii] at run time would send
         // the whole row through scratch memory)
@@ -941,13 +941,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
         }
         if (ltie_all) mbits |= list_ties(ii);
         const int cnt_l = __popc(mbits);
-        int inc = cnt_l;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const int y = __shfl_up(inc, o, 16);
-          if ((lane & 15) >= o) inc += y;
-        }
-        const int r0 = vs.gk[0];
+        const int inc = row16_incl_scan(cnt_l);
         if (inc - cnt_l < r0 && r0 <= inc) {
           int r = r0 - (inc - cnt_l);
           uint32_t bits = mbits;
