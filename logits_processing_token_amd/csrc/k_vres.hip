@@ -324,8 +324,10 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   for (int i = 0; i < R; ++i) list_ovf |= lbv[i + 1] - lbv[i] > NT;
   const __amdgpu_buffer_rsrc_t rsg =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, V * 2, 0x00020000);
-  auto gather_id = [&](int i) {  // the id at list slot lbv[i] + tid (clamped)
-    return s.list_id[min(lbv[i] + tid, max(lbv[i + 1] - 1, 0))];
+  // (a lane past the chunk index's entries asks for an id far past the row:
+  // its load reads nothing and returns 0, which no one uses)
+  auto gather_id = [&](int i) {  // the id at list slot lbv[i] + tid
+    return lbv[i] + tid < lbv[i + 1] ? s.list_id[lbv[i] + tid] : 0x3FFFFFFF;
   };
   auto gather_at = [&](int id) -> uint32_t {
     return __builtin_amdgcn_raw_buffer_load_b16(rsg, id * 2, 0, 0);
