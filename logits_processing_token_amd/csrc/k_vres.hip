@@ -744,8 +744,93 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       if (cut_kind == kInd) kcut = uni(vs.walk[0].key);
     }
   }
-  const float bp_v = uni(vs.view.v);  // the boundary bin's value
   const double target = u * Wp;
+  // The count pass for the draw's member (all threads), run while wave 0
+  // walks the draw's bin: every lane counts the members of the bin's value
+  // vv in each of its chunks (a nonzero value by its bf16 pattern, a zero
+  // one by the pattern less the sign; seen ids equal to the value added from
+  // the list), in byte fields, summed over rows of 16 lanes by shifts within
+  // the row, into rsum.  Seen ids equal to vv are marked per thread and
+  // chunk, 16 bits per thread, two threads a word, over the per-thread
+  // masses above (idle once the draw's bin is found).
+  float vv = 0.0f;
+  uint32_t pat = 0u, msk = 0xFFFFFFFFu, tmask = 0u;
+  bool ltie_all = false;
+  uint32_t *tiew = reinterpret_cast<uint32_t *>(above);
+  uint32_t *rsum = reinterpret_cast<uint32_t *>(gkey);  // 64 rows x 16 bytes
+  auto list_ties = [&](int i) {  // seen ids of chunk i equal to vv, per element bit j
+    uint32_t mb = 0u;
+    if ((tmask >> i) & 1u) {
+      const int g = tid + i * NT;
+      uint32_t bits = chunk_bits<1>(s.smask, g);
+      while (bits) {
+        const int j = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (s.list_val[list_slot(g * EPC + j, s.smask, woff)] == vv) mb |= 1u << j;
+      }
+    }
+    return mb;
+  };
+  auto count_setup = [&](float v, int ntie) {  // (ntie: the view's individuals equal to v)
+    vv = v;
+    ltie_all = ntie > 0;
+    if (ltie_all) {
+      for (int q = tid; q < NT / 2; q += NT) tiew[q] = 0u;
+      __syncthreads();
+      auto mark = [&](int id) {
+        const int gg = id / EPC, t = gg % NT, ci = gg / NT;
+        atomicOr(&tiew[t >> 1], 1u << ((t & 1) * 16 + ci));
+      };
+      if (ntie <= kTieCap) {
+        if (tid < ntie) mark(vs.tie_id[tid]);
+      } else {
+        for (int k = tid; k < n_list; k += NT)
+          if (s.list_val[k] == vv) mark(s.list_id[k]);
+      }
+      __syncthreads();
+      tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
+    }
+    pat = vv == 0.0f ? 0u : (__float_as_uint(vv) >> 16) * 0x10001u;
+    msk = vv == 0.0f ? 0x7FFF7FFFu : 0xFFFFFFFFu;
+  };
+  auto count_rows = [&]() {
+    // (a member leaves a zero half in (w & msk) ^ pat; 1 - that half,
+    // saturated, is 1 exactly there; the four words' halves are added in
+    // place and the two halves by a dot product with (1, 1))
+    const u16x2 one2 = {1, 1};
+    auto members = [&](const uint4 &c) -> uint32_t {
+      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+      u16x2 y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        y[q] = __builtin_elementwise_sub_sat(one2, __builtin_bit_cast(u16x2, (w[q] & msk) ^ pat));
+      return __builtin_amdgcn_udot2((y[0] + y[1]) + (y[2] + y[3]), one2, 0u, false);
+    };
+    uint32_t cb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      cb[i >> 2] |= members(launder(reg[i])) << ((i & 3) * 8);
+      __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: the row holds the registers
+    }
+    if (ltie_all) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) cb[i >> 2] += (uint32_t)__popc(list_ties(i)) << ((i & 3) * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // inclusive sums along each row of 16 lanes
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x111, 0xF, 0xF, true);
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x112, 0xF, 0xF, true);
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x114, 0xF, 0xF, true);
+      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x118, 0xF, 0xF, true);
+    }
+    // (rows numbered wave * 4 + row: that is id order within a chunk index)
+    if ((lane & 15) == 15) {
+      const int u = wid * 4 + (lane >> 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rsum[u * 4 + k] = cb[k];
+    }
+  };
+
   // The draw's bin: the bin whose cumulative mass interval holds the target
   // (bp counts only its kept part); every thread checks its own bins.
   if (!fallback) {
@@ -781,18 +866,19 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       if (!same && !view_bin(bs)) {
         fallback = true;
       } else {
+        count_setup(bin_value(bs), same ? uni(vs.view_ntie) : uni(vs.n_tie_b));
         if (uni(wid) == 0) {
           park_row();
           wave_walk(false, bs_start, target, vs.view, okey, oval, same ? cut_pos : 0x7FFFFFFF, &vs.walk[1]);
           unpark_row();
         }
+        count_rows();  // (wave 0 after its walk, the others meanwhile)
         __syncthreads();
         draw_kind = uni(vs.walk[1].kind);
       }
     }
     if (draw_kind == kFail) fallback = true;
   }
-  const float bs_v = uni(vs.view.v);
 
   // ---- 5. one pass over the registers: the draw's rank in its tie group -----
   // (The boundary's own member is needed only for the final scores: such a
@@ -805,90 +891,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       vs.gi[1] = -1;
       vs.gid[1] = -1;
     }
-    const float vv = bs_v;
-    // Individuals (seen ids, penalized) equal to the group value join the
-    // group: the view of the draw's bin counted them and kept their ids
-    // while they fit.  Which chunks of which thread hold one, 16 bits per
-    // thread, two threads a word, in the (now idle) ordered-view buffer.
-    const int ntie = uni(vs.view_ntie);
-    const bool ltie_all = ntie > 0;
-    uint32_t *tiew = reinterpret_cast<uint32_t *>(okey);
-    uint32_t tmask = 0u;
-    if (ltie_all) {
-      for (int q = tid; q < NT / 2; q += NT) tiew[q] = 0u;
-      __syncthreads();
-      auto mark = [&](int id) {
-        const int gg = id / EPC, t = gg % NT, ci = gg / NT;
-        atomicOr(&tiew[t >> 1], 1u << ((t & 1) * 16 + ci));
-      };
-      if (ntie <= kTieCap) {
-        if (tid < ntie) mark(vs.tie_id[tid]);
-      } else {
-        for (int k = tid; k < n_list; k += NT)
-          if (s.list_val[k] == vv) mark(s.list_id[k]);
-      }
-      __syncthreads();
-      tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
-    }
-    // One pass over the registers: every lane counts the members in each of
-    // its chunks (a nonzero value by its bf16 pattern, a zero one by the
-    // pattern less the sign; seen ids equal to the value added from the
-    // list), in byte fields, summed over rows of 16 lanes by shifts within
-    // the row.  Then one wave per chunk index scans the 64 rows of the
-    // workgroup in id order; the chunk index and the row of the member
-    // follow, and that row names it.
-    const uint32_t pat = vv == 0.0f ? 0u : (__float_as_uint(vv) >> 16) * 0x10001u;
-    const uint32_t msk = vv == 0.0f ? 0x7FFF7FFFu : 0xFFFFFFFFu;
-    auto list_ties = [&](int i) {  // seen ids of chunk i equal to vv, per element bit j
-      uint32_t mb = 0u;
-      if ((tmask >> i) & 1u) {
-        const int g = tid + i * NT;
-        uint32_t bits = chunk_bits<1>(s.smask, g);
-        while (bits) {
-          const int j = __ffs(bits) - 1;
-          bits &= bits - 1;
-          if (s.list_val[list_slot(g * EPC + j, s.smask, woff)] == vv) mb |= 1u << j;
-        }
-      }
-      return mb;
-    };
-    // (a member leaves a zero half in (w & msk) ^ pat; 1 - that half,
-    // saturated, is 1 exactly there; the four words' halves are added in
-    // place and the two halves by a dot product with (1, 1))
-    const u16x2 one2 = {1, 1};
-    auto members = [&](const uint4 &c) -> uint32_t {
-      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-      u16x2 y[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        y[q] = __builtin_elementwise_sub_sat(one2, __builtin_bit_cast(u16x2, (w[q] & msk) ^ pat));
-      return __builtin_amdgcn_udot2((y[0] + y[1]) + (y[2] + y[3]), one2, 0u, false);
-    };
-    uint32_t cb[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      cb[i >> 2] |= members(launder(reg[i])) << ((i & 3) * 8);
-      __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: the row holds the registers
-    }
-    if (ltie_all) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) cb[i >> 2] += (uint32_t)__popc(list_ties(i)) << ((i & 3) * 8);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {  // inclusive sums along each row of 16 lanes
-      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x111, 0xF, 0xF, true);
-      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x112, 0xF, 0xF, true);
-      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x114, 0xF, 0xF, true);
-      cb[k] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cb[k], 0x118, 0xF, 0xF, true);
-    }
-    // (rows numbered wave * 4 + row: that is id order within a chunk index)
-    uint32_t *rsum = reinterpret_cast<uint32_t *>(gkey);  // 64 rows x 16 bytes
-    if ((lane & 15) == 15) {
-      const int u = wid * 4 + (lane >> 4);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) rsum[u * 4 + k] = cb[k];
-    }
-    __syncthreads();
+    // (the members were counted while the draw was walked)
     // wave wid scans chunk index wid over the 64 rows (lane = row)
     int rc = 0, rinc = 0;
     if (wid < R) {
