@@ -225,6 +225,7 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
     return chunk_bits<DT>(s.kmask, ok ? g : 0);
   };
   uint32_t kb_n = chunk_kill(0);
+  tail_words<DT>(ea, V);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     if (i + PIPE < R) reg[i + PIPE] = load16(rowp + (int64_t)min(tid + (i + PIPE) * NT, glast) * 16);

@@ -275,7 +275,8 @@ struct Early {
   int hreg[kHpt];
   uint32_t km[kMpt];    // bad words | suppress
   uint32_t kbeg[kMpt];  // begin-suppress, for rows where it applies
-  uint32_t tw[4];
+  uint32_t tw[4];       // the tail chunk as loaded, then (tail_words) as used
+  uint32_t tlast;       // the last element of an odd bf16 row
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
@@ -314,15 +315,26 @@ __device__ __forceinline__ void early_loads(const SelectArgs &a, int row, const 
   const int tail_n = V - NG * EPC;
   const uint32_t row_bytes = (uint32_t)V * (DT == 1 ? 2u : 4u);
   const u32x4_t tv = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(rowp, row_bytes & ~3u), NG * 16, 0, 0);
-  const uint32_t last =
-      DT == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(rowp, row_bytes), (V - 1) * 2, 0, 0) : 0u;
+  e.tlast = DT == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(rowp, row_bytes), (V - 1) * 2, 0, 0) : 0u;
 #pragma unroll
   for (int q = 0; q < 4; ++q) e.tw[q] = tv[q];
+  (void)tail_n;
+}
+
+// The tail chunk made whole, where it is used: the empty asm keeps the
+// compiler from reading the loaded words (and so waiting for every load
+// before them) right after they were asked for, ahead of the row's loads.
+template <int DT>
+__device__ __forceinline__ void tail_words(Early &e, int V) {
+  using E = Elem<DT>;
+  constexpr int EPC = E::EPC;
+  asm volatile("" : "+v"(e.tw[0]), "+v"(e.tw[1]), "+v"(e.tw[2]), "+v"(e.tw[3]), "+v"(e.tlast));
+  const int tail_n = V - (V / EPC) * EPC;
   const uint32_t ninf = DT == 1 ? 0xFF80u : 0xFF800000u;
 #pragma unroll
   for (int j = 0; j < EPC; ++j) {
     if (j >= tail_n) put_elem<DT>(e.tw, j, ninf);
-    else if (DT == 1 && (V & 1) && j == tail_n - 1) put_elem<DT>(e.tw, j, last);
+    else if (DT == 1 && (V & 1) && j == tail_n - 1) put_elem<DT>(e.tw, j, e.tlast);
   }
 }
 

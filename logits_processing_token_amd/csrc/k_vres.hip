@@ -381,6 +381,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   const uint8_t *kbyte = reinterpret_cast<const uint8_t *>(s.kmask) + tid;
   const int itail = tail_n > 0 ? NG / NT : -1, ttail = NG % NT;
   // (every lane loaded the same tail: it is held in scalar registers)
+  tail_words<1>(ea, V);
   const uint32_t tw0 = uni(ea.tw[0]), tw1 = uni(ea.tw[1]), tw2 = uni(ea.tw[2]), tw3 = uni(ea.tw[3]);
   auto chunk_of = [&](int i) {  // (the tail, at its slot)
     uint4 c = launder(reg[i]);
