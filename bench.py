@@ -161,18 +161,21 @@ def main() -> int:
     first_tokens = out.cpu().numpy().copy()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    # One event pair on the launch stream brackets the K launches: the mean
+    # launch duration includes the gaps between launches (an event pair per
+    # launch would put its own timestamp packets between the kernels).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     print(f"bench: timing {K} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(K):
-        ev[i][0].record()
         step(i)
-        ev[i][1].record()
+    ev1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kernel_ms = ev0.elapsed_time(ev1) / K
 
     alg = algorithmic_bytes(w)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
