@@ -333,8 +333,14 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     return __builtin_amdgcn_raw_buffer_load_b16(rsg, id * 2, 0, 0);
   };
   auto gather = [&](int i) { return gather_at(gather_id(i)); };
+  // (a gathered score is penalized as it lands; lmax: the seen ids' top)
+  float lmax = -INFINITY;
   auto consume = [&](int i, uint32_t raw) {
-    if (lbv[i] + tid < lbv[i + 1]) s.list_val[lbv[i] + tid] = __uint_as_float(raw << 16);
+    if (lbv[i] + tid < lbv[i + 1]) {
+      const float y = penalize(__uint_as_float(raw << 16), a.rep);
+      s.list_val[lbv[i] + tid] = y;
+      lmax = fmaxf(lmax, y);
+    }
   };
   uint32_t gr[R];
 #pragma unroll
@@ -424,16 +430,14 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   if (list_ovf) {  // (uniform, rare) list slots past NT in one chunk index
     for (int e = tid; e < n_list; e += NT) {
       const int id = s.list_id[e];
-      if (e - (int)woff[id / (NT * EPC) * (NT * EPC / 32)] >= NT) s.list_val[e] = E::load1(rowp, id);
+      if (e - (int)woff[id / (NT * EPC) * (NT * EPC / 32)] >= NT) {
+        const float y = penalize(E::load1(rowp, id), a.rep);
+        s.list_val[e] = y;
+        lmax = fmaxf(lmax, y);
+      }
     }
   }
   __syncthreads();  // the row has landed
-  float lmax = -INFINITY;
-  for (int k = tid; k < n_list; k += NT) {
-    const float y = penalize(s.list_val[k], a.rep);
-    s.list_val[k] = y;
-    lmax = fmaxf(lmax, y);
-  }
   // fold the copies (each thread its own bins, so no barrier between the
   // reads and the writes); the highest occupied bin and the seen ids' top
   // score in one workgroup reduction
