@@ -166,6 +166,10 @@ __device__ __forceinline__ void lds_add(uint32_t addr, uint32_t v) {
 }
 
 constexpr int kTieCap = 128;
+// A listed individual's id (below 2^18 on this path) carries its bin in the
+// bits above, set when its score is known.
+constexpr int kIdBits = 18;
+constexpr int32_t kIdMask = (1 << kIdBits) - 1;
 
 struct VShared {
   BinView view;
@@ -333,14 +337,23 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     return __builtin_amdgcn_raw_buffer_load_b16(rsg, id * 2, 0, 0);
   };
   auto gather = [&](int i) { return gather_at(gather_id(i)); };
-  // (a gathered score is penalized as it lands; lmax: the seen ids' top)
+  VMap vm;  // the value bins (placed by the first chunks, before any consume)
+  // (a gathered score is penalized as it lands, and its bin noted beside its
+  // id; lmax: the seen ids' top)
   float lmax = -INFINITY;
   auto consume = [&](int i, uint32_t raw) {
     if (lbv[i] + tid < lbv[i + 1]) {
       const float y = penalize(__uint_as_float(raw << 16), a.rep);
       s.list_val[lbv[i] + tid] = y;
+      s.list_id[lbv[i] + tid] |= vbin(vkey_floor(y), vm) << kIdBits;
       lmax = fmaxf(lmax, y);
     }
+  };
+  // (the bisection and the final scores read plain ids)
+  auto untag = [&](int n) {
+    __syncthreads();
+    for (int k = tid; k < n; k += NT) s.list_id[k] &= kIdMask;
+    __syncthreads();
   };
   uint32_t gr[R];
 #pragma unroll
@@ -356,7 +369,6 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // LDS, so the copies lie below 2^16 and bin addresses fit 16 bits)
   const uint32_t lb = lds_addr(cnt) + (uint32_t)(lane & (kVCopies - 1)) * kVStride * 4u;
   const uint32_t ninf = sconst(0xFF80FF80u);
-  VMap vm;
   VMapP vp;
   // A near-zero score has a clamped magnitude of 0: every lane keeps the
   // least of its halves (the magnitudes stay below the binary16 infinity,
@@ -429,10 +441,11 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   consume(R - 1, gr[R - 1]);
   if (list_ovf) {  // (uniform, rare) list slots past NT in one chunk index
     for (int e = tid; e < n_list; e += NT) {
-      const int id = s.list_id[e];
+      const int id = s.list_id[e] & kIdMask;
       if (e - (int)woff[id / (NT * EPC) * (NT * EPC / 32)] >= NT) {
         const float y = penalize(E::load1(rowp, id), a.rep);
         s.list_val[e] = y;
+        s.list_id[e] = id | (vbin(vkey_floor(y), vm) << kIdBits);
         lmax = fmaxf(lmax, y);
       }
     }
@@ -486,7 +499,10 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   int token = 0;
   if (mx == -INFINITY) {  // every id removed: id 0, nothing kept
     if (tid == 0) a.out_tokens[row] = 0;
-    if (a.out_processed) res_processed<1>(a, row, s, INFINITY, ~0ull, n_list);
+    if (a.out_processed) {
+      untag(n_list);
+      res_processed<1>(a, row, s, INFINITY, ~0ull, n_list);
+    }
     return;
   }
   const float cref = mx * kLog2e;
@@ -537,7 +553,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
             zhi = fmaxf(zhi, x);
             const int slot = atomicAdd(&vs.nz, 1);
             if (slot < kZoneCap) {
-              s.list_id[n_list + slot] = g * EPC + j;
+              s.list_id[n_list + slot] = (g * EPC + j) | (vbin(vkey_floor(x), vm) << kIdBits);
               s.list_val[n_list + slot] = x;
             }
           }
@@ -579,14 +595,13 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     const float lo = b == zn ? -kZone : b == zp ? 0.0f : vkey_value(vbin_key(b, vm));
     return (int)((__float_as_uint(mass(lo)) >> 23) & 0xFFu);
   };
-  auto ind_bin = [&](float y) { return vbin(vkey_floor(y), vm); };
   for (int b = tid; b < NB; b += NT) lfix[b] = 0ull;
   if (tid == 0) vs.ovf = 0;
   __syncthreads();
   for (int k = tid; k < n_ind; k += NT) {
-    const float y = s.list_val[k];
-    const int b = ind_bin(y);
+    const int b = s.list_id[k] >> kIdBits;
     if (b < 1) continue;
+    const float y = s.list_val[k];
     const int eu = unit_expo(b);
     const uint32_t eb = __float_as_uint(mass(y));
     const int ek = (int)((eb >> 23) & 0xFFu);
@@ -674,15 +689,17 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   auto view_bin = [&](int b) -> bool {
     const float v = bin_value(b);
     for (int k = tid; k < n_ind; k += NT) {
+      const int tagged = s.list_id[k];
+      if ((tagged >> kIdBits) != b) continue;
       const float y = s.list_val[k];
-      if (ind_bin(y) != b) continue;
+      const int id = tagged & kIdMask;
       if (y == v) {
         const int slot = atomicAdd(&vs.n_tie_b, 1);
-        if (slot < kTieCap) vs.tie_id[slot] = s.list_id[k];
+        if (slot < kTieCap) vs.tie_id[slot] = id;
       } else {
         const int slot = atomicAdd(&vs.n_ind_b, 1);
         if (slot < kGatherCap) {
-          gkey[slot] = sel_key(y, (uint32_t)s.list_id[k]);
+          gkey[slot] = sel_key(y, (uint32_t)id);
           gval[slot] = mass(y);
         }
       }
@@ -790,7 +807,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
         if (tid < ntie) mark(vs.tie_id[tid]);
       } else {
         for (int k = tid; k < n_list; k += NT)
-          if (s.list_val[k] == vv) mark(s.list_id[k]);
+          if (s.list_val[k] == vv) mark(s.list_id[k] & kIdMask);
       }
       __syncthreads();
       tmask = (tiew[tid >> 1] >> ((tid & 1) * 16)) & 0xFFFFu;
@@ -971,6 +988,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   if (!fallback && draw_kind == kGroup) token = vs.gid[1];
   if (!fallback && draw_kind == kInd) token = (int)key_index(vs.walk[1].key);
 
+  if (fallback || a.out_processed) untag(n_ind);
   if (fallback) token = bisect_select<1, true>(a, row, s, sh, -INFINITY, cref, &kcut);
   if (tid == 0) a.out_tokens[row] = token;
   if (a.out_processed) res_processed<1>(a, row, s, -INFINITY, kcut, n_list);
