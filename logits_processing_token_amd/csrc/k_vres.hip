@@ -170,6 +170,10 @@ constexpr int kTieCap = 128;
 // bits above, set when its score is known.
 constexpr int kIdBits = 18;
 constexpr int32_t kIdMask = (1 << kIdBits) - 1;
+// A bin's count holds its dense elements in the low bits and, from the fixed
+// point masses on, its listed individuals above them.
+constexpr int kIndShift = 18;
+constexpr uint32_t kDenseMask = (1u << kIndShift) - 1u;
 
 struct VShared {
   BinView view;
@@ -601,6 +605,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   for (int k = tid; k < n_ind; k += NT) {
     const int b = s.list_id[k] >> kIdBits;
     if (b < 1) continue;
+    atomicAdd(&cnt[b], 1u << kIndShift);
     const float y = s.list_val[k];
     const int eu = unit_expo(b);
     const uint32_t eb = __float_as_uint(mass(y));
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     if (b < NB) {
       double m = 0.0;
       if (b >= 1) {
-        const uint32_t n = cnt[b];
+        const uint32_t n = cnt[b] & kDenseMask;
         const uint64_t l = lfix[b];
         if (n) m = (double)n * (double)mass(bin_value(b));
         if (l) {
@@ -688,6 +693,19 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // barrier.
   auto view_bin = [&](int b) -> bool {
     const float v = bin_value(b);
+    const uint32_t cb_ = uni(cnt[b]);
+    if ((cb_ >> kIndShift) == 0u) {  // (no individuals: the view is the group alone)
+      if (tid == 0) {
+        vs.view.single = 1;
+        vs.view.v = v;
+        vs.view.e = v == -INFINITY ? 0.0f : mass(v);
+        vs.view.n_ind = 0;
+        vs.view.n_above = 0;
+        vs.view.n_group = (int)(cb_ & kDenseMask);
+        vs.view_ntie = 0;
+      }
+      return true;
+    }
     for (int k = tid; k < n_ind; k += NT) {
       const int tagged = s.list_id[k];
       if ((tagged >> kIdBits) != b) continue;
@@ -723,7 +741,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       vs.view.e = v == -INFINITY ? 0.0f : mass(v);
       vs.view.n_ind = ni;
       vs.view.n_above = na;
-      vs.view.n_group = (int)cnt[b] + vs.n_tie_b;
+      vs.view.n_group = (int)(cnt[b] & kDenseMask) + vs.n_tie_b;
       vs.view_ntie = vs.n_tie_b;
     }
     return true;
