@@ -196,14 +196,10 @@ template <int NT_>
 __device__ __forceinline__ uint32_t block_max_u32_lds(uint32_t v, uint32_t *scratch) {
   constexpr int NW_ = NT_ / kWave;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  v = wave_max_u32_uni(v);  // (row moves, no LDS round trips)
   if (lane == 0) scratch[wid] = v;
   lds_barrier();
-  v = lane < NW_ ? scratch[lane] : 0u;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-  return v;
+  return wave_max_u32_uni(lane < NW_ ? scratch[lane] : 0u);
 }
 
 // The map for a first binned key bk (>= the smallest finite key).
