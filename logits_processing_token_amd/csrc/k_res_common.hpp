@@ -416,7 +416,21 @@ __device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo
     }
   }
   int n_list = 0;
-  const int my_off = block_excl_scan_i32<NT, true>(my_cnt, sh.red_i32, &n_list);
+  // Exclusive prefix of the counts over the workgroup: one barrier (the
+  // wave totals' slots were last read before the barrier above), the
+  // totals' prefix by row moves, read out of its lanes.
+  int my_off;
+  {
+    constexpr int NW_ = NT / kWave;
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    const int incl = wave_incl_scan_i32(my_cnt);
+    if (lane == kWave - 1) sh.red_i32[wid] = incl;
+    lds_barrier();
+    const int wsum = lane < NW_ ? sh.red_i32[lane] : 0;
+    const int wincl = wave_incl_scan_i32(wsum);
+    my_off = __builtin_amdgcn_readlane(wincl - wsum, uni(wid)) + incl - my_cnt;
+    n_list = __builtin_amdgcn_readlane(wincl, NW_ - 1);
+  }
   if (n_list > a.lcap) {  // too many seen ids for the list: the streamed path decides
     if (tid == 0) a.out_tokens[row] = kPending;
     return -1;
