@@ -743,21 +743,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     return true;
   };
 
-  // The walks run on wave 0 alone, its share of the row parked in LDS
-  // meanwhile: the walk gets the registers the row held.  (The fence keeps
-  // the compiler from forwarding the stored chunks past the walk.)
-  uint4 *park = reinterpret_cast<uint4 *>(smem + a.off_park);
-  auto park_row = [&]() {
-#pragma unroll
-    for (int i = 0; i < R; ++i) park[i * kWave + lane] = reg[i];
-    asm volatile("" ::: "memory");
-  };
-  auto unpark_row = [&]() {
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < R; ++i) reg[i] = park[i * kWave + lane];
-  };
-
+  // (the walks run on wave 0 alone; the others wait at the barrier after)
   double Wp = W;
   int cut_kind = kNone, draw_kind = kNone;
   int cut_pos = 0x7FFFFFFF;
@@ -768,9 +754,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       fallback = true;
     } else {
       if (uni(wid) == 0) {
-        park_row();
         wave_walk(true, C_bp1, pw, vs.view, okey, oval, 0x7FFFFFFF, &vs.walk[0]);
-        unpark_row();
       }
       __syncthreads();
       cut_kind = uni(vs.walk[0].kind);
@@ -904,9 +888,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       } else {
         count_setup(bin_value(bs), same ? uni(vs.view_ntie) : uni(vs.n_tie_b));
         if (uni(wid) == 0) {
-          park_row();
           wave_walk(false, bs_start, target, vs.view, okey, oval, same ? cut_pos : 0x7FFFFFFF, &vs.walk[1]);
-          unpark_row();
         }
         count_rows();  // (wave 0 after its walk, the others meanwhile)
         __syncthreads();

@@ -131,11 +131,9 @@ bool plan_vres(const tsel_params *p, int res, tsel::SelectArgs *a, size_t *lds_b
   const size_t kmask_bytes = align16(std::max<size_t>((size_t)mw * 4, slots));
   const size_t smask_bytes = kmask_bytes;
   const size_t woff = align16(std::max<size_t>(2 * (size_t)mw, slots / 2));
-  // the walking wave's chunks while it walks
-  const size_t park = (size_t)res * 64 * 16;  // 64 lanes, 16 bytes a chunk
   const size_t budget = (size_t)tsel::kVMaxDynLds;
   size_t off = align16((size_t)tsel::kVHistBytes);
-  const size_t fixed = off + kmask_bytes + smask_bytes + woff + tsel::kVSharedBytes + park;
+  const size_t fixed = off + kmask_bytes + smask_bytes + woff + tsel::kVSharedBytes;
   size_t lcap = (size_t)std::min<int64_t>(std::max<int64_t>(p->hist_stride, 0), V) + 8;
   lcap = std::min<size_t>((lcap + 3) & ~size_t(3), kMaxList);
   if (fixed + 8 * (64 + (size_t)tsel::kZoneCap) > budget) return false;
@@ -160,8 +158,6 @@ bool plan_vres(const tsel_params *p, int res, tsel::SelectArgs *a, size_t *lds_b
   off = a->off_woff + woff;
   a->off_sh = (uint32_t)align16(off);
   off = a->off_sh + tsel::kVSharedBytes;
-  a->off_park = (uint32_t)off;
-  off += park;
   a->off_lut = a->off_rhist = a->off_area = 0;  // unused here
   *lds_bytes = off;
   return off <= budget;

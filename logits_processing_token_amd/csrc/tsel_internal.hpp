@@ -72,7 +72,6 @@ struct SelectArgs {
   uint32_t off_woff;        // resident path: list offset of each thread's mask words
   uint32_t off_kmask;       // kill mask (0 but on the value-bin path)
   uint32_t off_sh;          // value-bin path: its shared scalars (no static LDS)
-  uint32_t off_park;        // value-bin path: one wave's share of the row, parked
 };
 
 hipError_t launch_greedy(const SelectArgs &a, size_t lds, hipStream_t s);
