@@ -2,9 +2,11 @@
 // in registers, with one histogram bin per bf16 value, for gfx950.
 //
 // One 1024-thread workgroup per row; the row (up to 16 chunks of 16 bytes per
-// lane) arrives with eight chunks in flight per lane while the history and
-// the masks are staged in LDS.  Each landed chunk loses its removed ids
-// (-inf) and is counted into a histogram whose bins are the bf16 values
+// lane) arrives with four chunks in flight per lane, the first four asked
+// for before the history and the masks are staged in LDS.  The seen ids'
+// scores are gathered as their chunks arrive and penalized as they land.
+// Each landed chunk loses its removed and seen ids (-inf) and is counted
+// into a histogram whose bins are the bf16 values
 // themselves: a score's bin is its ordered 16-bit pattern less an offset,
 // worked out two scores at a time with packed 16-bit integer operations, so
 // that the row costs no exponential and no float arithmetic per element.
