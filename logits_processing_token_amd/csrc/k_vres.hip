@@ -731,7 +731,11 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       oval[r] = gval[i];
       if (key_score(ki) > v) atomicAdd(&vs.n_above_b, 1);
     }
-    __syncthreads();
+    // (up to 64 individuals were ordered by wave 0 alone, which also writes
+    // and walks the view: no barrier then, only an order among its lanes;
+    // the other waves touch none of the view's arrays meanwhile)
+    if (ni > kWave) __syncthreads();
+    else __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     if (tid == 0) {
       const int na = vs.n_above_b;
       vs.view.single = 1;
@@ -774,12 +778,14 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // the list), in byte fields, summed over rows of 16 lanes by shifts within
   // the row, into rsum.  Seen ids equal to vv are marked per thread and
   // chunk, 16 bits per thread, two threads a word, over the per-thread
-  // masses above (idle once the draw's bin is found).
+  // masses above (idle once the draw's bin is found); rsum follows them
+  // there, clear of the arrays the view's ordering reads.
   float vv = 0.0f;
   uint32_t pat = 0u, msk = 0xFFFFFFFFu, tmask = 0u;
   bool ltie_all = false;
   uint32_t *tiew = reinterpret_cast<uint32_t *>(above);
-  uint32_t *rsum = reinterpret_cast<uint32_t *>(gkey);  // 64 rows x 16 bytes
+  uint32_t *rsum = tiew + NT / 2;  // 64 rows x 16 bytes
+  static_assert(4 * (NT / 2) + 64 * 16 <= 8 * NT, "tie words and row sums within the masses");
   auto list_ties = [&](int i) {  // seen ids of chunk i equal to vv, per element bit j
     uint32_t mb = 0u;
     if ((tmask >> i) & 1u) {

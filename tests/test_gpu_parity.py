@@ -214,6 +214,26 @@ def test_value_bins_near_zero(n_zone):
     _assert_select(w, max_low_mismatch_frac=0.25)
 
 
+@pytest.mark.parametrize("n_seen", [40, 64, 65, 250])
+@pytest.mark.parametrize("topp", [1.0, 0.5])
+def test_value_bins_seen_ids_of_one_score(n_seen, topp):
+    """n_seen seen ids share one logit that the penalty moves off the bf16
+    grid: they are one bin's individuals, all of one score, and hold most of
+    the mass, so the draw (and at top_p 0.5 the boundary too) walks them in
+    id order; up to 64 of them are ordered by one wave, more by the block."""
+    V = 40000
+    w = synth.random_select(500 + n_seen, 16, V, n_seen, dtype="bf16", sigma=1.0,
+                            settings=dict(repetition_penalty=1.3, do_sample=True, top_p=topp))
+    g = np.random.default_rng(n_seen)
+    x = g.standard_normal((w.batch, V)).astype(np.float32) - np.float32(6.0)
+    for b in range(w.batch):
+        ids = g.choice(V, size=n_seen, replace=False)
+        x[b, ids] = 4.0
+        w.history[b] = ids
+    w.logits[:] = synth.bf16_bits(x)
+    _assert_select(w)
+
+
 def test_value_bins_zeros_of_both_signs():
     """Rows of zeros of both signs: too many near-zero scores to list, all of
     one value, form one tie group across the two near-zero bins."""
