@@ -646,6 +646,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     if (lane == 0) sh.red_f64[wid] = v;
     if (tid == 0) {
       sh.bin_p = -1;
+      sh.bin_hi = -1;  // (the draw's bin, searched after the boundary's walk)
       vs.n_ind_b = 0;  // (the counters of the first view)
       vs.n_tie_b = 0;
       vs.n_above_b = 0;
@@ -862,14 +863,13 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // The draw's bin: the bin whose cumulative mass interval holds the target
   // (bp counts only its kept part); every thread checks its own bins.
   if (!fallback) {
+    // (the counters of a second view, first counted after the barrier that
+    // ends the search)
     if (tid == 0) {
-      sh.bin_hi = -1;
-      sh.sbase = -1.0;
-      vs.n_ind_b = 0;  // (the counters of a second view)
+      vs.n_ind_b = 0;
       vs.n_tie_b = 0;
       vs.n_above_b = 0;
     }
-    __syncthreads();
     {
       double C = above[tid];
       for (int q = BPT - 1; q >= 0; --q) {
