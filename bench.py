@@ -109,6 +109,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=8, help="distinct input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="time only the first ROWS rows of the batch (a latency sweep; "
+                         "the metric's own line is the whole batch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -131,6 +134,12 @@ def main() -> int:
     dev = torch.device("cuda:0")
     print("bench: generating the workload", file=sys.stderr, flush=True)
     w = synth.c3_select()
+    sweep = 0 < args.rows < w.batch
+    if sweep:
+        n = args.rows
+        w = synth.SelectWorkload(w.name, w.logits[:n].copy(), w.history[:n].copy(),
+                                 w.lens[:n].copy(), w.prompt_lens[:n].copy(),
+                                 w.max_lengths[:n].copy(), w.settings, w.uniforms[:n].copy())
     B, V = w.logits.shape
 
     if args.copy_calibration:
@@ -143,6 +152,8 @@ def main() -> int:
 
     d = harness.upload_select(w)
     R = max(1, args.rotate)
+    if sweep:  # (enough copies that a few rows still come from HBM, not the caches)
+        R = max(R, -(-(768 << 20) // (d["logits"].numel() * d["logits"].element_size())))
     logits = [d["logits"]] + [d["logits"].clone() for _ in range(R - 1)]
     hists = [d["hist"]] + [d["hist"].clone() for _ in range(R - 1)]
     out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -179,7 +190,8 @@ def main() -> int:
 
     alg = algorithmic_bytes(w)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    # (the counters were taken on the whole batch)
+    traffic = None if sweep else measured_traffic()
     result = {
         "metric": METRIC,
         "value": B * K / elapsed,
@@ -197,7 +209,8 @@ def main() -> int:
                                "over a random permutation + N(0,1); history 4096; "
                                "repetition_penalty 1.05; 100 suppress_tokens; 50 bad words; "
                                "temperature 1.0; top_p 0.95; inverse-CDF sampling",
-                   "batch": B, "vocab": V, "logits_dtype": "bf16", "rotated_copies": R},
+                   "batch": B, "vocab": V, "logits_dtype": "bf16", "rotated_copies": R,
+                   **({"rows_timed": f"the first {B} rows of the batch"} if sweep else {})},
         "kernel_ms": kernel_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
