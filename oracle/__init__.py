@@ -82,6 +82,9 @@ def _load():
         lib.oracle_verify_row.argtypes = [
             C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_void_p,
             C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        lib.oracle_finish_row.restype = C.c_int32
+        lib.oracle_finish_row.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                          C.c_int32, C.c_void_p]
         lib.oracle_mask_build.restype = None
         lib.oracle_mask_build.argtypes = [C.c_int32, C.c_void_p, C.c_int32,
                                           C.c_void_p]
@@ -245,3 +248,21 @@ def mask_build(vocab: int, ids: Sequence[int]) -> np.ndarray:
     mask = np.empty((vocab + 31) // 32, np.uint32)
     lib.oracle_mask_build(vocab, a.ctypes.data, a.size, mask.ctypes.data)
     return mask
+
+
+def finish_step(tokens, lens, max_lengths, eos_ids, finished):
+    """The end of one decode step, row by row: (emitted tokens [B] int32,
+    finished flags [B] uint8).  tokens: the step's selected tokens (-1 for
+    none); lens: the rows' lengths before them; finished: the flags before
+    the step (not modified)."""
+    lib = _load()
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    L = np.ascontiguousarray(lens, dtype=np.int32)
+    M = np.ascontiguousarray(max_lengths, dtype=np.int32)
+    e = _ids(eos_ids)
+    fin = np.array(finished, dtype=np.uint8, copy=True).reshape(-1)
+    out = np.empty(t.shape[0], np.int32)
+    for b in range(t.shape[0]):
+        out[b] = lib.oracle_finish_row(int(t[b]), int(L[b]), int(M[b]), e.ctypes.data, e.size,
+                                       fin[b:].ctypes.data)
+    return out, fin

@@ -429,3 +429,28 @@ void oracle_mask_build(int32_t V, const int32_t *ids, int32_t n, uint32_t *mask)
   for (int32_t i = 0; i < n; ++i)
     if (in_vocab(ids[i], V)) mask[ids[i] >> 5] |= 1u << (ids[i] & 31);
 }
+
+/* The end of one decode step for one row ("Transmuter.Generation
+ * (transmuter v2.0.0)", function doc of generate/5, the on_token callback
+ * and the return value: a row with no new token reports -1, a finished row
+ * has no more tokens, the eos token is not returned; mlxcel inference
+ * pipeline, decode loop, "EOS 감지와 정지": a sampled id in the merged stop
+ * set ends the row and is not emitted, and the loop also ends at the
+ * maximum length).  t: the step's selected token (-1: none); L: the row's
+ * length before it; M: its maximum length; *fin: 0 or 1, updated. */
+int32_t oracle_finish_row(int32_t t, int32_t L, int32_t M, const int32_t *eos, int32_t n_eos,
+                          uint8_t *fin) {
+  if (*fin || t < 0) { /* no new token: nothing more from this row */
+    *fin = 1;
+    return -1;
+  }
+  for (int32_t i = 0; i < n_eos; ++i) {
+    if (eos[i] == t) { /* a stop id: the row ends, the id is not emitted */
+      *fin = 1;
+      return -1;
+    }
+  }
+  /* the token is emitted; the row is then L + 1 long */
+  *fin = (int64_t)L + 1 >= (int64_t)M ? 1 : 0;
+  return t;
+}

@@ -205,3 +205,23 @@ def test_mask_build_bits():
         if 0 <= i < V:
             want[i // 32] |= np.uint64(1) << np.uint64(i % 32)
     assert m.astype(np.uint64).tolist() == want.tolist()
+
+
+@pytest.mark.parametrize("case", DOC["finish"], ids=[c["id"] for c in DOC["finish"]])
+def test_golden_finish(case):
+    out, fin = oracle.finish_step([case["token"]], [case["len"]], [case["max_length"]],
+                                  case["eos"], [case["finished"]])
+    assert out[0] == case["expect"]["token"], case["cite"]
+    assert fin[0] == case["expect"]["finished"], case["cite"]
+
+
+def test_finish_batch_rows_independent():
+    """A batch gives each row the result it gets alone (the golden cases
+    stacked in one call, the finished flags of the input left untouched)."""
+    cs = [c for c in DOC["finish"] if c["eos"] == [2]]
+    fin_in = np.array([c["finished"] for c in cs], np.uint8)
+    out, fin = oracle.finish_step([c["token"] for c in cs], [c["len"] for c in cs],
+                                  [c["max_length"] for c in cs], [2], fin_in)
+    assert out.tolist() == [c["expect"]["token"] for c in cs]
+    assert fin.tolist() == [c["expect"]["finished"] for c in cs]
+    assert fin_in.tolist() == [c["finished"] for c in cs]
