@@ -191,6 +191,38 @@ tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_
 size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab);
 
 /*
+ * tsel_finish_step -- the end of one decode step for every row, on the
+ * device, so that a decode loop needs no host read per step
+ * ("Transmuter.Generation (transmuter v2.0.0)", function doc of generate/5:
+ * a row with no new token reports -1, a finished row has no more tokens and
+ * the eos token is not returned; mlxcel inference pipeline, decode loop,
+ * EOS detection and stopping: a sampled id in the merged stop set ends the
+ * row unemitted, and the loop also ends at the maximum length).  For row b
+ * with selected token t = tokens[b]:
+ *   finished[b] != 0, or t < 0:   out_tokens[b] = -1, finished[b] = 1;
+ *   t one of eos_ids:             out_tokens[b] = -1, finished[b] = 1;
+ *   otherwise:                    out_tokens[b] = t,
+ *                                 finished[b] = (lens[b] + 1 >= max_lengths[b]).
+ *
+ *  tokens       device int32 [B]: the step's tokens (tsel_process_select's
+ *               out_tokens, -1 for none).
+ *  lens         device int32 [B]: each row's length before this token
+ *               (prompt + tokens so far), as in tsel_process_select.
+ *  max_lengths  device int32 [B]: each row's maximum length.
+ *  eos_ids      device int32 [n_eos], the merged stop set (NULL when
+ *               n_eos == 0; duplicates allowed).
+ *  finished     device uint8 [B], 0 or 1: read, then overwritten with the
+ *               flag after this step.
+ *  out_tokens   device int32 [B]; may be the tokens buffer itself.
+ * The call owns no memory; it is asynchronous on `stream`.
+ * Errors: TSEL_ERR_INVALID_ARG for B < 0, n_eos < 0, or NULL required
+ * pointers; TSEL_ERR_UNSUPPORTED for n_eos > 256.  B == 0 does nothing.
+ */
+tsel_status tsel_finish_step(int32_t batch, const int32_t *tokens, const int32_t *lens,
+                             const int32_t *max_lengths, const int32_t *eos_ids, int32_t n_eos,
+                             uint8_t *finished, int32_t *out_tokens, void *stream);
+
+/*
  * tsel_selftest_exp2_monotone -- counts the binary32 inputs x in
  * [lo, hi] (taken in numeric order) for which the device's exp2 instruction
  * gives exp2(next(x)) < exp2(x).  Sampling without top_k maps histogram bins

@@ -295,6 +295,19 @@ tsel_status tsel_mask_build(int32_t vocab, const int32_t *ids, int32_t n_ids, ui
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 
+tsel_status tsel_finish_step(int32_t batch, const int32_t *tokens, const int32_t *lens,
+                             const int32_t *max_lengths, const int32_t *eos_ids, int32_t n_eos,
+                             uint8_t *finished, int32_t *out_tokens, void *stream) {
+  if (batch < 0 || n_eos < 0 || (n_eos > 0 && !eos_ids)) return TSEL_ERR_INVALID_ARG;
+  if (batch > 0 && (!tokens || !lens || !max_lengths || !finished || !out_tokens))
+    return TSEL_ERR_INVALID_ARG;
+  if (n_eos > tsel::kMaxFinishEos) return TSEL_ERR_UNSUPPORTED;
+  if (batch == 0) return TSEL_OK;
+  hipError_t e = tsel::launch_finish(batch, tokens, lens, max_lengths, eos_ids, n_eos, finished,
+                                     out_tokens, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
 tsel_status tsel_selftest_exp2_monotone(float lo, float hi, unsigned long long *violations,
                                         void *stream) {
   if (!violations || !(lo <= hi)) return TSEL_ERR_INVALID_ARG;

@@ -92,6 +92,10 @@ int verify_chunks(int32_t V, int32_t dtype);
 hipError_t launch_exp2_monotone(uint32_t k0, uint32_t k1, unsigned long long *violations,
                                 hipStream_t s);
 
+constexpr int kMaxFinishEos = 256;  // stop ids one end-of-step call takes
+hipError_t launch_finish(int32_t B, const int32_t *tokens, const int32_t *lens,
+                         const int32_t *max_lengths, const int32_t *eos, int32_t n_eos,
+                         uint8_t *finished, int32_t *out, hipStream_t s);
 hipError_t launch_mask_build(int32_t V, const int32_t *ids, int32_t n, uint32_t *mask,
                              hipStream_t s);
 

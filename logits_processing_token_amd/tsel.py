@@ -28,7 +28,7 @@ TSEL_MAX_EOS = 8
 EXPORTS = (
     "tsel_process_select", "tsel_process_select_workspace_size", "tsel_validate_params",
     "tsel_mask_build", "tsel_verify", "tsel_verify_workspace_size", "tsel_status_string",
-    "tsel_selftest_exp2_monotone",
+    "tsel_selftest_exp2_monotone", "tsel_finish_step",
 )
 
 
@@ -81,6 +81,8 @@ def load() -> C.CDLL:
     lib.tsel_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.tsel_status_string.restype = C.c_char_p
     lib.tsel_status_string.argtypes = [i32]
+    lib.tsel_finish_step.restype = i32
+    lib.tsel_finish_step.argtypes = [i32, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.tsel_selftest_exp2_monotone.restype = i32
     lib.tsel_selftest_exp2_monotone.argtypes = [C.c_float, C.c_float, vp, vp]
     _lib = lib
@@ -165,6 +167,30 @@ def mask_build(vocab: int, ids, out_mask=None, stream=None):
     st = lib.tsel_mask_build(vocab, _ptr(ids), int(ids.numel()), _ptr(out_mask), _stream(stream))
     _check(st, "tsel_mask_build")
     return out_mask
+
+
+def finish_step(tokens, lens, max_lengths, eos_ids, finished, out_tokens=None, stream=None):
+    """The end of one decode step on the device: out_tokens (int32 [B]: the
+    emitted token or -1) and finished (uint8 [B], updated in place).  eos_ids
+    is an int32 device tensor (possibly empty); tokens, lens and max_lengths
+    are contiguous int32 device tensors of B rows.  Returns out_tokens."""
+    import torch
+    B = int(tokens.numel())
+    for name, t, dt in (("tokens", tokens, torch.int32), ("lens", lens, torch.int32),
+                        ("max_lengths", max_lengths, torch.int32),
+                        ("finished", finished, torch.uint8)):
+        if t.dtype != dt or t.numel() != B or not t.is_contiguous():
+            raise ValueError(f"finish_step: {name} must be a contiguous {dt} tensor of {B} rows")
+    if eos_ids.dtype != torch.int32 or not eos_ids.is_contiguous():
+        raise ValueError("finish_step: eos_ids must be a contiguous int32 tensor")
+    if out_tokens is None:
+        out_tokens = torch.empty_like(tokens)
+    n_eos = int(eos_ids.numel())
+    st = load().tsel_finish_step(B, _ptr(tokens), _ptr(lens), _ptr(max_lengths),
+                                 _ptr(eos_ids) if n_eos else None, n_eos, _ptr(finished),
+                                 _ptr(out_tokens), _stream(stream))
+    _check(st, "tsel_finish_step")
+    return out_tokens
 
 
 def selftest_exp2_monotone(lo: float, hi: float, stream=None) -> int:

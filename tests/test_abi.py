@@ -123,6 +123,24 @@ def test_entry_points_reject_before_any_gpu_call():
                            None) == tsel.TSEL_ERR_UNSUPPORTED
 
 
+
+def test_finish_step_rejects_before_any_gpu_call():
+    """The end-of-step call: an empty batch does nothing; bad sizes, missing
+    pointers and too many stop ids are refused on the host."""
+    lib = tsel.load()
+    f = C.c_void_p(0x1000)
+    assert lib.tsel_finish_step(0, None, None, None, None, 0, None, None, None) == tsel.TSEL_OK
+    assert lib.tsel_finish_step(-1, f, f, f, f, 1, f, f, None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_finish_step(4, f, f, f, f, -1, f, f, None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_finish_step(4, f, f, f, None, 2, f, f, None) == tsel.TSEL_ERR_INVALID_ARG
+    for k in range(5):
+        args = [f, f, f, f, f]
+        args[k] = None
+        t, L, M, fin, out = args
+        assert lib.tsel_finish_step(4, t, L, M, f, 1, fin, out, None) == tsel.TSEL_ERR_INVALID_ARG
+    assert lib.tsel_finish_step(4, f, f, f, f, 257, f, f, None) == tsel.TSEL_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(tsel.status_string(s), str)

@@ -346,3 +346,43 @@ def test_verify_random(k, dtype):
     gpu = harness.run_gpu_verify(w)
     ora = oracle.verify(w.logits, w.candidates)
     assert harness.compare_verify(gpu, ora) == []
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,n_eos", [(1, 1), (255, 0), (256, 8), (257, 3), (5000, 256)])
+def test_finish_step(B, n_eos):
+    """The end of a decode step against the oracle, bit for bit: tokens with
+    -1s and stop ids among them, rows already finished, lengths around the
+    maximum; several workgroups and a ragged last one; the largest stop set."""
+    import torch
+    from logits_processing_token_amd import tsel
+    _say(f"case finish_step: B={B} n_eos={n_eos}")
+    g = np.random.default_rng(B * 7 + n_eos)
+    V = 1000
+    eos = g.choice(V, size=n_eos, replace=n_eos > V).astype(np.int32)
+    tok = g.integers(0, V, size=B).astype(np.int32)
+    if n_eos:
+        pick = g.random(B) < 0.2
+        tok[pick] = eos[g.integers(0, n_eos, size=int(pick.sum()))]
+    tok[g.random(B) < 0.1] = -1
+    M = g.integers(1, 60, size=B).astype(np.int32)
+    L = (M + g.integers(-3, 2, size=B)).astype(np.int32)
+    fin = (g.random(B) < 0.3).astype(np.uint8)
+    want_t, want_f = oracle.finish_step(tok, L, M, eos, fin)
+    dev = torch.device("cuda:0")
+    d_tok = torch.from_numpy(tok).to(dev)
+    d_fin = torch.from_numpy(fin).to(dev)
+    out = tsel.finish_step(d_tok, torch.from_numpy(L).to(dev), torch.from_numpy(M).to(dev),
+                           torch.from_numpy(eos).to(dev), d_fin)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want_t)
+    assert np.array_equal(d_fin.cpu().numpy(), want_f)
+    # in place: the tokens buffer takes the emitted tokens; a second step
+    # from the flags just written
+    d_fin2 = d_fin.clone()
+    tsel.finish_step(d_tok, torch.from_numpy(L + 1).to(dev), torch.from_numpy(M).to(dev),
+                     torch.from_numpy(eos).to(dev), d_fin2, out_tokens=d_tok)
+    torch.cuda.synchronize()
+    want_t2, want_f2 = oracle.finish_step(tok, L + 1, M, eos, want_f)
+    assert np.array_equal(d_tok.cpu().numpy(), want_t2)
+    assert np.array_equal(d_fin2.cpu().numpy(), want_f2)
