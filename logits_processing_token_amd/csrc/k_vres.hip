@@ -838,7 +838,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     uint32_t cb[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      cb[i >> 2] |= members(launder(reg[i])) << ((i & 3) * 8);
+      cb[i >> 2] |= members(reg[i]) << ((i & 3) * 8);
       __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: the row holds the registers
     }
     if (ltie_all) {
