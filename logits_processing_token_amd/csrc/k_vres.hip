@@ -456,17 +456,25 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // fold the copies (each thread its own bins, so no barrier between the
   // reads and the writes); the highest occupied bin and the seen ids' top
   // score in one workgroup reduction
+  // (a thread's four bins are adjacent words: one 16-byte read per copy)
+  static_assert(BPT == 4 && NB % 4 == 0 && kVStride % 4 == 0, "four bins a thread, 16-byte rows");
   uint32_t top_b = 0u;
+  if (tid * BPT < NB) {
+    uint4 c = reinterpret_cast<const uint4 *>(cnt)[tid];
 #pragma unroll
-  for (int q = 0; q < BPT; ++q) {
-    const int b = tid * BPT + q;
-    if (b < NB) {
-      uint32_t c = 0u;
-#pragma unroll
-      for (int k = 0; k < kVCopies; ++k) c += cnt[k * kVStride + b];
-      cnt[b] = c;
-      if (c && b >= 1) top_b = (uint32_t)b;
+    for (int k = 1; k < kVCopies; ++k) {
+      const uint4 d = reinterpret_cast<const uint4 *>(cnt + k * kVStride)[tid];
+      c.x += d.x;
+      c.y += d.y;
+      c.z += d.z;
+      c.w += d.w;
     }
+    reinterpret_cast<uint4 *>(cnt)[tid] = c;
+    const int b0 = tid * BPT;
+    if (c.x && b0 >= 1) top_b = (uint32_t)b0;
+    if (c.y) top_b = (uint32_t)(b0 + 1);
+    if (c.z) top_b = (uint32_t)(b0 + 2);
+    if (c.w) top_b = (uint32_t)(b0 + 3);
   }
   {
     const uint32_t tw = wave_max_u32_uni(top_b);
