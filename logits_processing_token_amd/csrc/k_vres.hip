@@ -625,24 +625,32 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   __syncthreads();
   if (uni(vs.ovf) != 0) fallback = true;
   // bin masses, in place of the fixed-point sums
+  // (a thread's four bins come in 16-byte reads and leave in 16-byte writes)
   double part = 0.0;
+  if (tid * BPT < NB) {
+    const uint4 n4 = reinterpret_cast<const uint4 *>(cnt)[tid];
+    const ulonglong2 la = reinterpret_cast<const ulonglong2 *>(lfix)[2 * tid];
+    const ulonglong2 lb = reinterpret_cast<const ulonglong2 *>(lfix)[2 * tid + 1];
+    const uint32_t nq[4] = {n4.x, n4.y, n4.z, n4.w};
+    const uint64_t lq[4] = {la.x, la.y, lb.x, lb.y};
+    double mq[4];
 #pragma unroll
-  for (int q = 0; q < BPT; ++q) {
-    const int b = tid * BPT + q;
-    if (b < NB) {
+    for (int q = 0; q < BPT; ++q) {
+      const int b = tid * BPT + q;
       double m = 0.0;
       if (b >= 1) {
-        const uint32_t n = cnt[b] & kDenseMask;
-        const uint64_t l = lfix[b];
+        const uint32_t n = nq[q] & kDenseMask;
         if (n) m = (double)n * (double)mass(bin_value(b));
-        if (l) {
+        if (lq[q]) {
           const int eu = unit_expo(b);
-          m += (double)l * __longlong_as_double((long long)(eu - 150 + 1023) << 52);
+          m += (double)lq[q] * __longlong_as_double((long long)(eu - 150 + 1023) << 52);
         }
       }
-      bmass[b] = m;
+      mq[q] = m;
       part += m;
     }
+    reinterpret_cast<double2 *>(bmass)[2 * tid] = make_double2(mq[0], mq[1]);
+    reinterpret_cast<double2 *>(bmass)[2 * tid + 1] = make_double2(mq[2], mq[3]);
   }
 
   // ---- 4. cumulative masses: the boundary bin and the draw bin -------------
@@ -678,13 +686,16 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   const bool use_top_p = a.top_p < 1.0f;
   const double pw = (double)a.top_p * W;
   const double u = (double)a.uniforms[row];
-  {
+  if (tid * BPT < NB) {
     double C = above[tid];
+    const double2 ma = reinterpret_cast<const double2 *>(bmass)[2 * tid];
+    const double2 mb = reinterpret_cast<const double2 *>(bmass)[2 * tid + 1];
+    const double mq[4] = {ma.x, ma.y, mb.x, mb.y};
+#pragma unroll
     for (int q = BPT - 1; q >= 0; --q) {
       const int b = tid * BPT + q;
-      if (b >= NB) continue;
       const double Cb1 = C;
-      C += bmass[b];
+      C += mq[q];
       if (use_top_p && Cb1 < pw && C >= pw) { sh.bin_p = b; sh.sbase = Cb1; }
     }
   }
@@ -878,12 +889,16 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       vs.n_tie_b = 0;
       vs.n_above_b = 0;
     }
-    {
+    if (tid * BPT < NB) {
       double C = above[tid];
+      const double2 ma = reinterpret_cast<const double2 *>(bmass)[2 * tid];
+      const double2 mb = reinterpret_cast<const double2 *>(bmass)[2 * tid + 1];
+      const double mq[4] = {ma.x, ma.y, mb.x, mb.y};
+#pragma unroll
       for (int q = BPT - 1; q >= 0; --q) {
         const int b = tid * BPT + q;
-        if (b >= NB || b < 1) continue;
-        const double m = (bp >= 0 && b == bp) ? (Wp - C_bp1) : bmass[b];
+        if (b < 1) continue;
+        const double m = (bp >= 0 && b == bp) ? (Wp - C_bp1) : mq[q];
         if (m > 0.0 && C <= target && target < C + m && (bp < 0 || b >= bp)) {
           sh.bin_hi = b;
           sh.sbase = C;
