@@ -401,19 +401,25 @@ __device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo
     if (q >= 0 && q < V) atomicOr(&s.kmask[q >> 5], 1u << (q & 31));
   }
   lds_barrier();
-  uint32_t aq[kMpt];
+  // (a thread's four words in one 16-byte read and write per mask; words
+  // past mw, inside the masks' rounded-up span, hold no seen id, and their
+  // early-loaded words read as 0, so taking them along changes nothing)
+  uint32_t aq[kMpt] = {0u, 0u, 0u, 0u};
   int my_cnt = 0;
+  if (tid * kMpt < mw) {
+    const uint4 k4 = reinterpret_cast<const uint4 *>(s.kmask)[tid];
+    const uint4 s4 = reinterpret_cast<const uint4 *>(s.smask)[tid];
+    const uint32_t kq[kMpt] = {k4.x, k4.y, k4.z, k4.w}, sq[kMpt] = {s4.x, s4.y, s4.z, s4.w};
+    uint32_t kn[kMpt];
 #pragma unroll
-  for (int q = 0; q < kMpt; ++q) {
-    const int w = tid * kMpt + q;
-    aq[q] = 0u;
-    if (w < mw) {
-      const uint32_t K = s.kmask[w] | e.km[q] | (ri.begin_active ? e.kbeg[q] : 0u), S = s.smask[w];
-      aq[q] = S & ~K;
-      s.kmask[w] = K | S;
-      s.smask[w] = aq[q];
+    for (int q = 0; q < kMpt; ++q) {
+      const uint32_t K = kq[q] | e.km[q] | (ri.begin_active ? e.kbeg[q] : 0u);
+      aq[q] = sq[q] & ~K;
+      kn[q] = K | sq[q];
       my_cnt += __popc(aq[q]);
     }
+    reinterpret_cast<uint4 *>(s.kmask)[tid] = make_uint4(kn[0], kn[1], kn[2], kn[3]);
+    reinterpret_cast<uint4 *>(s.smask)[tid] = make_uint4(aq[0], aq[1], aq[2], aq[3]);
   }
   int n_list = 0;
   // Exclusive prefix of the counts over the workgroup: one barrier (the
