@@ -63,32 +63,39 @@ class _Res(C.Structure):
         ("topk_threshold", C.c_float), ("margin", C.c_double),
         ("greedy_margin", C.c_double), ("n_admissible", C.c_int32),
         ("admissible", C.c_int32 * MAX_ADMISSIBLE),
+        ("keep_min", C.c_int32), ("keep_max", C.c_int32),
     ]
 
 
 _lib = None
 
 
+def bind(path: str):
+    """The oracle library at ``path`` with its call signatures declared (the
+    pin tests also bind copies of the oracle built with a planted mistake)."""
+    lib = C.CDLL(path)
+    lib.oracle_select_row.restype = C.c_int
+    lib.oracle_select_row.argtypes = [
+        C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+        C.POINTER(_Cfg), C.c_float, C.c_void_p, C.POINTER(_Res)]
+    lib.oracle_verify_row.restype = None
+    lib.oracle_verify_row.argtypes = [
+        C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_void_p,
+        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.oracle_finish_row.restype = C.c_int32
+    lib.oracle_finish_row.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                      C.c_int32, C.c_void_p]
+    lib.oracle_mask_build.restype = None
+    lib.oracle_mask_build.argtypes = [C.c_int32, C.c_void_p, C.c_int32,
+                                      C.c_void_p]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         build(force=False)
-        lib = C.CDLL(_LIB)
-        lib.oracle_select_row.restype = C.c_int
-        lib.oracle_select_row.argtypes = [
-            C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
-            C.POINTER(_Cfg), C.c_float, C.c_void_p, C.POINTER(_Res)]
-        lib.oracle_verify_row.restype = None
-        lib.oracle_verify_row.argtypes = [
-            C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_void_p,
-            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
-        lib.oracle_finish_row.restype = C.c_int32
-        lib.oracle_finish_row.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
-                                          C.c_int32, C.c_void_p]
-        lib.oracle_mask_build.restype = None
-        lib.oracle_mask_build.argtypes = [C.c_int32, C.c_void_p, C.c_int32,
-                                          C.c_void_p]
-        _lib = lib
+        _lib = bind(_LIB)
     return _lib
 
 
@@ -136,8 +143,9 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
     logits: [B, V] float32, or uint16 holding bf16 bit patterns.
     history: [B, H] int32, chronological ids; row b uses its first lens[b].
     Returns a dict of numpy arrays indexed like ``rows``: token, n_finite,
-    topk_threshold, margin, greedy_margin, admissible (list of arrays) and,
-    when asked, processed [len(rows), V] float32.
+    topk_threshold, margin, greedy_margin, admissible (list of arrays),
+    keep_min and keep_max (the kept counts top_p allows under the margin
+    policy's perturbation) and, when asked, processed [len(rows), V] float32.
     """
     lib = _load()
     logits = np.ascontiguousarray(logits)
@@ -169,6 +177,7 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
         "token": np.empty(n, np.int32), "n_finite": np.empty(n, np.int32),
         "topk_threshold": np.empty(n, np.float32), "margin": np.empty(n, np.float64),
         "greedy_margin": np.empty(n, np.float64), "admissible": [None] * n,
+        "keep_min": np.empty(n, np.int32), "keep_max": np.empty(n, np.int32),
     }
     processed = np.empty((n, V), np.float32) if want_processed else None
     esize = logits.itemsize
@@ -192,6 +201,8 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
         out["margin"][i] = res.margin
         out["greedy_margin"][i] = res.greedy_margin
         out["admissible"][i] = np.array(res.admissible[:res.n_admissible], np.int32)
+        out["keep_min"][i] = res.keep_min
+        out["keep_max"][i] = res.keep_max
 
     if threads > 1 and n > 1:
         with ThreadPoolExecutor(max_workers=threads) as ex:

@@ -69,6 +69,9 @@ typedef struct {
   double greedy_margin;          /* (x1 - x2) / max(1, |x1|) */
   int32_t n_admissible;
   int32_t admissible[ORACLE_MAX_ADMISSIBLE];
+  int32_t keep_min, keep_max;    /* ids top_p keeps for sure / may keep when
+                                    each normalized mass before an id moves
+                                    by at most eps (sampling; else n_finite) */
 } oracle_row_result;
 
 /* ------------------------------------------------------------------ */
@@ -301,6 +304,7 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
     float den = fabsf(x1) > 1.0f ? fabsf(x1) : 1.0f;
     res->greedy_margin = (x1 > -INFINITY) ? ((double)x1 - (double)x2) / den : 0.0;
     for (int32_t v = 0; v < V; ++v) res->n_finite += x[v] > -INFINITY;
+    res->keep_min = res->keep_max = res->n_finite;
     if (x_out) memcpy(x_out, x, sizeof(float) * (size_t)V);
     free(x); free(order); free(buf);
     return 0;
@@ -343,6 +347,7 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
     int32_t na = 0;
     if (n == 0) {
       res->admissible[na++] = t;
+      res->keep_min = res->keep_max = 0;
     } else {
       double m = (double)pre[order[0]];
       double W = 0.0;
@@ -363,6 +368,8 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
         kmin = must < 1 ? 1 : must;
         kmax = may < 1 ? 1 : may;
       }
+      res->keep_min = kmin;
+      res->keep_max = kmax;
       if (kmax - kmin > 4 * ORACLE_MAX_ADMISSIBLE) kmax = kmin + 4 * ORACLE_MAX_ADMISSIBLE;
       for (int32_t K = kmin; K <= kmax; ++K) {
         double Wp = 0.0;
