@@ -9,11 +9,12 @@
  *    Work is enqueued asynchronously on it; results are valid after the
  *    caller synchronizes the stream.
  *  - The caller allocates and frees every buffer (logits, history, masks,
- *    outputs, workspace).  The library keeps no allocation and no mutable
- *    global state between calls, so independent calls may run concurrently
- *    on different streams.  (The pages' generation loop likewise frees only
- *    the tensors it made and never the caller's: "Transmuter.Generation",
- *    section "Device memory".)
+ *    outputs, workspace).  The library keeps no allocation between calls and
+ *    no state that changes a result (it only remembers, per device, that a
+ *    kernel's LDS limit is raised), so independent calls may run
+ *    concurrently on different streams.  (The pages' generation loop
+ *    likewise frees only the tensors it made and never the caller's:
+ *    "Transmuter.Generation", section "Device memory".)
  *  - Return value: TSEL_OK, or a negative tsel_status that is decided on the
  *    host before anything is enqueued (invalid or unsupported arguments), or
  *    TSEL_ERR_LAUNCH when the runtime refuses a launch.  Faults inside a

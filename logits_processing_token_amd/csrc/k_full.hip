@@ -529,14 +529,9 @@ __global__ __launch_bounds__(NT, 1) void k_full(SelectArgs a, int pending_only) 
 // ---------------------------------------------------------------------------
 template <int DT, int RES, bool SIMPLE>
 static hipError_t launch_full_t(const SelectArgs &a, size_t lds, hipStream_t st, int pending) {
-  static bool attr = false;  // benign race: every writer stores the same value
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_full<DT, RES, SIMPLE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kSelectMaxDynLds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // devices where the limit is raised
+  const void *fn = reinterpret_cast<const void *>(&k_full<DT, RES, SIMPLE>);
+  if (hipError_t e = ensure_dyn_lds(fn, (int)kSelectMaxDynLds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL((k_full<DT, RES, SIMPLE>), dim3(a.B), dim3(NT), lds, st, a, pending);
   return hipGetLastError();
 }

@@ -46,14 +46,9 @@ __global__ __launch_bounds__(NT, 1) void k_greedy(SelectArgs a) {
 
 template <int DT>
 hipError_t launch_greedy_t(const SelectArgs &a, size_t lds, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_greedy<DT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kSelectMaxDynLds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // devices where the limit is raised
+  const void *fn = reinterpret_cast<const void *>(&k_greedy<DT>);
+  if (hipError_t e = ensure_dyn_lds(fn, (int)kSelectMaxDynLds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL(k_greedy<DT>, dim3(a.B), dim3(NT), lds, st, a);
   return hipGetLastError();
 }

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "tsel_device.hpp"
 #include "tsel_internal.hpp"
 
@@ -68,9 +69,10 @@ __global__ __launch_bounds__(VT) void k_verify(const char *logits, int64_t row_b
       const float x = DT == 1 ? __uint_as_float(
                                     (uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
                               : reinterpret_cast<const float *>(rowp)[v];
-      if (x > bv || (x == bv && v < bi)) { bv = x; bi = v; }
+      if (x > bv) { bv = x; bi = v; }  // (tail ids follow this lane's others)
     }
   }
+  // (a lane that saw only -inf keeps key 0, below every real key)
   uint64_t key = bi == 0x7FFFFFFF ? 0ull : sel_key(bv, (uint32_t)bi);
   key = wave_max_u64(key);
   if ((tid & (kWave - 1)) == 0) red[tid / kWave] = key;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(VT) void k_verify(const char *logits, int64_t row_b
       const uint64_t v = __hip_atomic_load(p + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       m = v > m ? v : m;
     }
-    sel[j] = (int)key_index(m);
+    sel[j] = m == 0ull ? 0 : (int)key_index(m);  // every score -inf: the lowest id
   }
   __syncthreads();
   if (tid == 0) {

@@ -1023,14 +1023,9 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
 
 template <int R>
 static hipError_t launch_vres_t(const SelectArgs &a, size_t lds, hipStream_t st) {
-  static bool attr = false;  // benign race: every writer stores the same value
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_vres<R>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kVMaxDynLds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // devices where the limit is raised
+  const void *fn = reinterpret_cast<const void *>(&k_vres<R>);
+  if (hipError_t e = ensure_dyn_lds(fn, (int)kVMaxDynLds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL((k_vres<R>), dim3(a.B), dim3(NT), lds, st, a);
   return hipGetLastError();
 }

@@ -18,6 +18,7 @@ constexpr int32_t kMaxList = 8192 + 8;  // sparse list: distinct seen ids + row 
 
 inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
+
 tsel_status check_params(const tsel_params *p, bool uniforms_given) {
   if (!p) return TSEL_ERR_INVALID_ARG;
   if (p->batch < 0 || p->vocab < 1) return TSEL_ERR_INVALID_ARG;
@@ -322,17 +323,18 @@ tsel_status tsel_selftest_exp2_monotone(float lo, float hi, unsigned long long *
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 
+static size_t verify_partial_bytes(int32_t batch, int32_t k, int32_t vocab);
+
 size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab) {
   if (batch <= 0 || k < 0 || vocab < 1) return 0;
-  const int S = std::max(tsel::verify_chunks(vocab, TSEL_F32), tsel::verify_chunks(vocab, TSEL_BF16));
-  const size_t partials = (size_t)batch * (size_t)(k + 1) * (size_t)S * 8;
-  return align16(partials) + align16((size_t)batch * 4);
+  return align16(verify_partial_bytes(batch, k, vocab)) + align16((size_t)batch * 4);
 }
 
-tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_t k,
-                        int32_t vocab, int64_t row_stride, const int32_t *candidates,
-                        int32_t *out_n_match, int32_t *out_tokens, int32_t *out_next,
-                        int32_t *out_k, void *workspace, size_t workspace_bytes, void *stream) {
+// Host checks shared by both verify entry points (TSEL_OK to go on).
+static tsel_status check_verify(const void *logits, int32_t dtype, int32_t batch, int32_t k,
+                                int32_t vocab, int64_t row_stride, const int32_t *candidates,
+                                const int32_t *out_n_match, const int32_t *out_tokens,
+                                const int32_t *out_next, const int32_t *out_k) {
   if (batch < 0 || k < 0 || vocab < 1 || row_stride < vocab) return TSEL_ERR_INVALID_ARG;
   if (dtype != TSEL_F32 && dtype != TSEL_BF16) return TSEL_ERR_INVALID_ARG;
   if (batch == 0) return TSEL_OK;
@@ -342,15 +344,30 @@ tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_
   const int64_t esize = dtype == TSEL_BF16 ? 2 : 4;
   if (reinterpret_cast<uintptr_t>(logits) % 16 != 0 || (row_stride * esize) % 16 != 0)
     return TSEL_ERR_UNSUPPORTED;
+  if ((int64_t)batch * (k + 1) > 65535) return TSEL_ERR_UNSUPPORTED;  // grid y limit
+  return TSEL_OK;
+}
+
+static size_t verify_partial_bytes(int32_t batch, int32_t k, int32_t vocab) {
+  const int Smax = std::max(tsel::verify_chunks(vocab, TSEL_F32), tsel::verify_chunks(vocab, TSEL_BF16));
+  return (size_t)batch * (size_t)(k + 1) * (size_t)Smax * 8;
+}
+
+tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_t k,
+                        int32_t vocab, int64_t row_stride, const int32_t *candidates,
+                        int32_t *out_n_match, int32_t *out_tokens, int32_t *out_next,
+                        int32_t *out_k, void *workspace, size_t workspace_bytes, void *stream) {
+  tsel_status st = check_verify(logits, dtype, batch, k, vocab, row_stride, candidates,
+                                out_n_match, out_tokens, out_next, out_k);
+  if (st != TSEL_OK || batch == 0) return st;
   const size_t need = tsel_verify_workspace_size(batch, k, vocab);
   if (!workspace || workspace_bytes < need) return TSEL_ERR_WORKSPACE;
-  if ((int64_t)batch * (k + 1) > 65535) return TSEL_ERR_UNSUPPORTED;  // grid y limit
+  const int64_t esize = dtype == TSEL_BF16 ? 2 : 4;
   const int S = tsel::verify_chunks(vocab, dtype);
-  const int Smax = std::max(tsel::verify_chunks(vocab, TSEL_F32), tsel::verify_chunks(vocab, TSEL_BF16));
   char *ws = static_cast<char *>(workspace);
   uint64_t *partials = reinterpret_cast<uint64_t *>(ws);
-  uint32_t *counters = reinterpret_cast<uint32_t *>(
-      ws + align16((size_t)batch * (size_t)(k + 1) * (size_t)Smax * 8));
+  uint32_t *counters =
+      reinterpret_cast<uint32_t *>(ws + align16(verify_partial_bytes(batch, k, vocab)));
   hipError_t e = tsel::launch_verify(logits, dtype, batch, k, vocab, row_stride * esize, S,
                                      candidates, out_n_match, out_tokens, out_next, out_k,
                                      partials, counters, static_cast<hipStream_t>(stream));

@@ -6,7 +6,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace tsel {
+
+// Raises a kernel's dynamic LDS limit on the current device the first time
+// it launches there.  `done` holds one bit per device id below 64 (higher
+// ids set the attribute on every launch); two threads racing on a first
+// launch both set the same value, which is harmless.
+inline hipError_t ensure_dyn_lds(const void *fn, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 constexpr int kSelectThreads = 1024;        // one workgroup (16 wave64s) per row
 constexpr int kLdsBytes = 160 * 1024;       // LDS of one gfx950 compute unit
