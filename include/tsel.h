@@ -192,6 +192,28 @@ tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_
 size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab);
 
 /*
+ * tsel_verify_noalloc -- tsel_verify for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that forbid
+ * allocation).  Same arguments, results and checks as tsel_verify, without
+ * the workspace: its partial maxima and per-row counters live in a
+ * file-scope device array of TSEL_NOALLOC_SCRATCH_BYTES that each GPU holds
+ * from its first call until the process ends.  The first call on a device
+ * (device ids below 64) takes the array's address and clears it with a small
+ * kernel on `stream`; no call allocates or frees memory.  Every call on one
+ * GPU shares that GPU's array, so calls that overlap in time on one GPU race
+ * and give wrong results: the caller orders them (e.g. one stream).
+ * Errors: as tsel_verify; TSEL_ERR_UNSUPPORTED when
+ * tsel_verify_workspace_size(batch, k, vocab) exceeds
+ * TSEL_NOALLOC_SCRATCH_BYTES; TSEL_ERR_LAUNCH also for a device id of 64 or
+ * more.
+ */
+#define TSEL_NOALLOC_SCRATCH_BYTES (1u << 20)
+tsel_status tsel_verify_noalloc(const void *logits, int32_t dtype, int32_t batch, int32_t k,
+                                int32_t vocab, int64_t row_stride, const int32_t *candidates,
+                                int32_t *out_n_match, int32_t *out_tokens, int32_t *out_next,
+                                int32_t *out_k, void *stream);
+
+/*
  * tsel_finish_step -- the end of one decode step for every row, on the
  * device, so that a decode loop needs no host read per step
  * ("Transmuter.Generation (transmuter v2.0.0)", function doc of generate/5:

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "tsel_device.hpp"
 #include "tsel_internal.hpp"
@@ -113,6 +114,55 @@ __global__ __launch_bounds__(VT) void k_verify(const char *logits, int64_t row_b
   }
   __syncthreads();
   for (int j = tid; j <= k; j += VT) tokens[(int64_t)b * (k + 1) + j] = j <= nm_s ? sel[j] : -1;
+}
+
+// ---- the variant that allocates nothing -------------------------------------
+// Its partial maxima and per-row counters live in this file-scope array
+// instead of a caller workspace.  Every GPU the library runs on holds its own
+// copy until the process ends; in host code the name stands for no device
+// address, so the launches take the address hipGetSymbolAddress gives on
+// each device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_at[kNoAllocDevices];  // per device id: the array's address, once set up
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_clear_words(uint32_t *p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_verify_noalloc(const void *logits, int32_t dtype, int32_t B, int32_t k,
+                                 int32_t V, int64_t row_bytes, int32_t chunks,
+                                 size_t partial_bytes, const int32_t *cand, int32_t *n_match,
+                                 int32_t *tokens, int32_t *next, int32_t *k_out, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoAllocDevices) return hipErrorInvalidDevice;
+  char *base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_at[dev]) {
+      // set-up on this device (it is current): the array's address, then its
+      // counters cleared once; every call leaves them at zero again
+      void *p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      constexpr int n = (int)(kNoAllocScratchBytes / 4);
+      hipLaunchKernelGGL(k_clear_words, dim3(64), dim3(256), 0, s, static_cast<uint32_t *>(p), n);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      g_scratch_at[dev] = p;
+    }
+    base = static_cast<char *>(g_scratch_at[dev]);
+  }
+  uint64_t *partials = reinterpret_cast<uint64_t *>(base);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(base + ((partial_bytes + 15) & ~size_t(15)));
+  return launch_verify(logits, dtype, B, k, V, row_bytes, chunks, cand, n_match, tokens, next,
+                       k_out, partials, counters, s);
 }
 
 int verify_chunks(int32_t V, int32_t dtype) {

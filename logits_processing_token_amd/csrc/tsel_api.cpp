@@ -18,6 +18,7 @@ constexpr int32_t kMaxList = 8192 + 8;  // sparse list: distinct seen ids + row 
 
 inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
+static_assert(TSEL_NOALLOC_SCRATCH_BYTES == tsel::kNoAllocScratchBytes, "one limit");
 
 tsel_status check_params(const tsel_params *p, bool uniforms_given) {
   if (!p) return TSEL_ERR_INVALID_ARG;
@@ -371,6 +372,23 @@ tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_
   hipError_t e = tsel::launch_verify(logits, dtype, batch, k, vocab, row_stride * esize, S,
                                      candidates, out_n_match, out_tokens, out_next, out_k,
                                      partials, counters, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
+tsel_status tsel_verify_noalloc(const void *logits, int32_t dtype, int32_t batch, int32_t k,
+                                int32_t vocab, int64_t row_stride, const int32_t *candidates,
+                                int32_t *out_n_match, int32_t *out_tokens, int32_t *out_next,
+                                int32_t *out_k, void *stream) {
+  tsel_status st = check_verify(logits, dtype, batch, k, vocab, row_stride, candidates,
+                                out_n_match, out_tokens, out_next, out_k);
+  if (st != TSEL_OK || batch == 0) return st;
+  if (tsel_verify_workspace_size(batch, k, vocab) > tsel::kNoAllocScratchBytes)
+    return TSEL_ERR_UNSUPPORTED;
+  const int64_t esize = dtype == TSEL_BF16 ? 2 : 4;
+  hipError_t e = tsel::launch_verify_noalloc(
+      logits, dtype, batch, k, vocab, row_stride * esize, tsel::verify_chunks(vocab, dtype),
+      verify_partial_bytes(batch, k, vocab), candidates, out_n_match, out_tokens, out_next, out_k,
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 

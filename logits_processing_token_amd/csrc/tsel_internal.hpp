@@ -106,6 +106,15 @@ hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k
                          uint64_t *partials, uint32_t *counters, hipStream_t s);
 int verify_chunks(int32_t V, int32_t dtype);
 
+// tsel_verify_noalloc: scratch of at most this many bytes per device, for
+// device ids below kNoAllocDevices.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+constexpr int kNoAllocDevices = 64;
+hipError_t launch_verify_noalloc(const void *logits, int32_t dtype, int32_t B, int32_t k,
+                                 int32_t V, int64_t row_bytes, int32_t chunks,
+                                 size_t partial_bytes, const int32_t *cand, int32_t *n_match,
+                                 int32_t *tokens, int32_t *next, int32_t *k_out, hipStream_t s);
+
 hipError_t launch_exp2_monotone(uint32_t k0, uint32_t k1, unsigned long long *violations,
                                 hipStream_t s);
 

@@ -28,8 +28,9 @@ TSEL_MAX_EOS = 8
 EXPORTS = (
     "tsel_process_select", "tsel_process_select_workspace_size", "tsel_validate_params",
     "tsel_mask_build", "tsel_verify", "tsel_verify_workspace_size", "tsel_status_string",
-    "tsel_selftest_exp2_monotone", "tsel_finish_step",
+    "tsel_selftest_exp2_monotone", "tsel_finish_step", "tsel_verify_noalloc",
 )
+TSEL_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 
 class TselError(RuntimeError):
@@ -77,6 +78,8 @@ def load() -> C.CDLL:
     lib.tsel_mask_build.argtypes = [i32, vp, i32, vp, vp]
     lib.tsel_verify.restype = i32
     lib.tsel_verify.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tsel_verify_noalloc.restype = i32
+    lib.tsel_verify_noalloc.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]
     lib.tsel_verify_workspace_size.restype = sz
     lib.tsel_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.tsel_status_string.restype = C.c_char_p
@@ -228,4 +231,29 @@ def verify(logits, candidates, workspace, dtype: int, vocab: Optional[int] = Non
                          _ptr(nxt), _ptr(k_next), _ptr(workspace),
                          int(workspace.numel() * workspace.element_size()), _stream(stream))
     _check(st, "tsel_verify")
+    return n_match, tokens, nxt, k_next
+
+
+def verify_noalloc(logits, candidates, dtype: int, vocab: Optional[int] = None,
+                   row_stride: Optional[int] = None, outs: Optional[Sequence] = None,
+                   stream=None):
+    """Run tsel_verify_noalloc (no workspace: the library's per-device
+    scratch array); returns (n_match, tokens, next, k_next)."""
+    import torch
+    lib = load()
+    B, K1, W = logits.shape
+    V = W if vocab is None else vocab
+    k = K1 - 1
+    dev = logits.device
+    if outs is None:
+        outs = (torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty((B, K1), dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+    n_match, tokens, nxt, k_next = outs
+    stride = W if row_stride is None else row_stride
+    st = lib.tsel_verify_noalloc(_ptr(logits), dtype, B, k, V, stride,
+                                 _ptr(candidates) if k > 0 else None, _ptr(n_match),
+                                 _ptr(tokens), _ptr(nxt), _ptr(k_next), _stream(stream))
+    _check(st, "tsel_verify_noalloc")
     return n_match, tokens, nxt, k_next
