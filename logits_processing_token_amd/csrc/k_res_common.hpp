@@ -360,17 +360,24 @@ __device__ __forceinline__ void stage_clear(const Lds &s, RowShared &sh, int kwo
   if (tid == 0) sh.n_coll = 0;
 }
 
-// Staging of a resident row in LDS once stage_clear has run (barriers that
-// order LDS only):
-//   kmask <- ids the registers drop: removed by a processor, or seen
-//   smask <- alive seen ids; list_id <- those ids in id order
-//   woff  <- list offset of every mask word
-// Returns the list length, or -1 when the list does not fit: then the row's
-// token is left pending for the streamed path and the caller returns.
-__device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo &ri, const Lds &s,
-                                     RowShared &sh, const int32_t *h, const Early &e,
-                                     uint16_t *woff) {
-  const int tid = threadIdx.x, V = a.V, mw = a.mw, L = ri.L;
+// Staging of a resident row in LDS once stage_clear has run, in three steps
+// that a kernel may run between the counts of its row's first chunks (each
+// ends in a barrier that orders LDS only):
+//   stage_marks: seen bits, n-gram bans, the eos ban of the minimum lengths;
+//   stage_merge: kmask <- ids the registers drop (removed by a processor, or
+//                seen); smask <- alive seen ids; the list's size and this
+//                thread's offset in it;
+//   stage_list:  list_id <- the alive seen ids in id order; woff <- the list
+//                offset of every mask word.
+struct StageState {
+  uint32_t aq[kMpt];  // this thread's alive seen words
+  int my_off;         // its first list slot
+  int n_list;         // the list's length
+};
+
+__device__ __forceinline__ void stage_marks(const SelectArgs &a, const RowInfo &ri, const Lds &s,
+                                            const int32_t *h, const Early &e) {
+  const int tid = threadIdx.x, V = a.V, L = ri.L;
   lds_barrier();
 #pragma unroll
   for (int k = 0; k < kHpt; ++k) {
@@ -401,11 +408,17 @@ __device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo
     if (q >= 0 && q < V) atomicOr(&s.kmask[q >> 5], 1u << (q & 31));
   }
   lds_barrier();
+}
+
+__device__ __forceinline__ void stage_merge(const SelectArgs &a, const RowInfo &ri, const Lds &s,
+                                            RowShared &sh, const Early &e, StageState &st) {
+  const int tid = threadIdx.x, mw = a.mw;
   // (a thread's four words in one 16-byte read and write per mask; words
   // past mw, inside the masks' rounded-up span, hold no seen id, and their
   // early-loaded words read as 0, so taking them along changes nothing)
-  uint32_t aq[kMpt] = {0u, 0u, 0u, 0u};
   int my_cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kMpt; ++q) st.aq[q] = 0u;
   if (tid * kMpt < mw) {
     const uint4 k4 = reinterpret_cast<const uint4 *>(s.kmask)[tid];
     const uint4 s4 = reinterpret_cast<const uint4 *>(s.smask)[tid];
@@ -414,38 +427,41 @@ __device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo
 #pragma unroll
     for (int q = 0; q < kMpt; ++q) {
       const uint32_t K = kq[q] | e.km[q] | (ri.begin_active ? e.kbeg[q] : 0u);
-      aq[q] = sq[q] & ~K;
+      st.aq[q] = sq[q] & ~K;
       kn[q] = K | sq[q];
-      my_cnt += __popc(aq[q]);
+      my_cnt += __popc(st.aq[q]);
     }
     reinterpret_cast<uint4 *>(s.kmask)[tid] = make_uint4(kn[0], kn[1], kn[2], kn[3]);
-    reinterpret_cast<uint4 *>(s.smask)[tid] = make_uint4(aq[0], aq[1], aq[2], aq[3]);
+    reinterpret_cast<uint4 *>(s.smask)[tid] = make_uint4(st.aq[0], st.aq[1], st.aq[2], st.aq[3]);
   }
-  int n_list = 0;
   // Exclusive prefix of the counts over the workgroup: one barrier (the
   // wave totals' slots were last read before the barrier above), the
   // totals' prefix by row moves, read out of its lanes.
-  int my_off;
-  {
-    constexpr int NW_ = NT / kWave;
-    const int lane = tid & (kWave - 1), wid = tid / kWave;
-    const int incl = wave_incl_scan_i32(my_cnt);
-    if (lane == kWave - 1) sh.red_i32[wid] = incl;
-    lds_barrier();
-    const int wsum = lane < NW_ ? sh.red_i32[lane] : 0;
-    const int wincl = wave_incl_scan_i32(wsum);
-    my_off = __builtin_amdgcn_readlane(wincl - wsum, uni(wid)) + incl - my_cnt;
-    n_list = __builtin_amdgcn_readlane(wincl, NW_ - 1);
-  }
-  if (n_list > a.lcap) {  // too many seen ids for the list: the streamed path decides
+  constexpr int NW_ = NT / kWave;
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const int incl = wave_incl_scan_i32(my_cnt);
+  if (lane == kWave - 1) sh.red_i32[wid] = incl;
+  lds_barrier();
+  const int wsum = lane < NW_ ? sh.red_i32[lane] : 0;
+  const int wincl = wave_incl_scan_i32(wsum);
+  st.my_off = __builtin_amdgcn_readlane(wincl - wsum, uni(wid)) + incl - my_cnt;
+  st.n_list = __builtin_amdgcn_readlane(wincl, NW_ - 1);
+}
+
+// Returns the list length, or -1 when the list does not fit: then the row's
+// token is left pending for the streamed path and the caller returns.
+__device__ __forceinline__ int stage_list(const SelectArgs &a, int row, const Lds &s,
+                                          uint16_t *woff, const StageState &st) {
+  const int tid = threadIdx.x, mw = a.mw;
+  if (st.n_list > a.lcap) {  // too many seen ids for the list: the streamed path decides
     if (tid == 0) a.out_tokens[row] = kPending;
     return -1;
   }
-  int o = my_off;
+  int o = st.my_off;
 #pragma unroll
   for (int q = 0; q < kMpt; ++q) {
     if (tid * kMpt + q < mw) woff[tid * kMpt + q] = (uint16_t)o;
-    uint32_t bits = aq[q];
+    uint32_t bits = st.aq[q];
     while (bits) {
       const int b = __ffs(bits) - 1;
       bits &= bits - 1;
@@ -453,7 +469,17 @@ __device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo
     }
   }
   lds_barrier();
-  return n_list;
+  return st.n_list;
+}
+
+// The three steps in a row.
+__device__ __forceinline__ int stage(const SelectArgs &a, int row, const RowInfo &ri, const Lds &s,
+                                     RowShared &sh, const int32_t *h, const Early &e,
+                                     uint16_t *woff) {
+  stage_marks(a, ri, s, h, e);
+  StageState st;
+  stage_merge(a, ri, s, sh, e, st);
+  return stage_list(a, row, s, woff, st);
 }
 
 }  // namespace res

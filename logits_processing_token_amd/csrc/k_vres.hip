@@ -178,15 +178,18 @@ constexpr int kIndShift = 18;
 constexpr uint32_t kDenseMask = (1u << kIndShift) - 1u;
 
 struct VShared {
-  BinView view;
+  BinView view, view2;  // (view2: the draw's bin when it is known before the boundary's walk)
   WalkResult walk[2];
   float gv[2];
   int gk[2];
   int gi[2], gw[2], gr[2];
   int gid[2];
-  int wtot[2][NW][16];
+  int wtot[16];
   int n_ind_b, n_tie_b, n_above_b;
+  int n_ind_b2, n_tie_b2, n_above_b2;
+  double mbp, mbq, sbase2;
   int tie_id[kTieCap];  // ids of the viewed bin's individuals equal to its value
+  int tie_id2[kTieCap];
   int nz;
   uint32_t kmax[NW];
   float fmax[NW];
@@ -264,6 +267,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   const int len0 = __builtin_nontemporal_load(a.lens + row);
   const int len1 = __builtin_nontemporal_load(a.lens + a.B + row);
   const int len2 = __builtin_nontemporal_load(a.lens + 2 * a.B + row);
+  const float u_row = __builtin_nontemporal_load(a.uniforms + row);  // (read at the draw)
   Early ea;
   early_loads<1>(a, row, rowp, ea);
   const int tail_n = V - NG * EPC;
@@ -332,8 +336,13 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, V * 2, 0x00020000);
   // (a lane past the chunk index's entries asks for an id far past the row:
   // its load reads nothing and returns 0, which no one uses)
-  auto gather_id = [&](int i) {  // the id at list slot lbv[i] + tid
-    return lbv[i] + tid < lbv[i + 1] ? s.list_id[lbv[i] + tid] : 0x3FFFFFFF;
+  // (the list slot this thread takes for chunk index i: successive chunk
+  // indices start a quarter of the workgroup further on, so that the
+  // penalties of the gathered scores spread over every wave)
+  auto slot_of = [&](int i) { return lbv[i] + ((tid + NT - (NT / 4) * (i & 3)) & (NT - 1)); };
+  auto gather_id = [&](int i) {  // the id at list slot slot_of(i)
+    const int k = slot_of(i);
+    return k < lbv[i + 1] ? s.list_id[k] : 0x3FFFFFFF;
   };
   auto gather_at = [&](int id) -> uint32_t {
     return __builtin_amdgcn_raw_buffer_load_b16(rsg, id * 2, 0, 0);
@@ -344,10 +353,11 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   // id; lmax: the seen ids' top)
   float lmax = -INFINITY;
   auto consume = [&](int i, uint32_t raw) {
-    if (lbv[i] + tid < lbv[i + 1]) {
+    const int k = slot_of(i);
+    if (k < lbv[i + 1]) {
       const float y = penalize(__uint_as_float(raw << 16), a.rep);
-      s.list_val[lbv[i] + tid] = y;
-      s.list_id[lbv[i] + tid] |= vbin(vkey_floor(y), vm) << kIdBits;
+      s.list_val[k] = y;
+      s.list_id[k] |= vbin(vkey_floor(y), vm) << kIdBits;
       lmax = fmaxf(lmax, y);
     }
   };
@@ -608,19 +618,28 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   for (int b = tid; b < NB; b += NT) lfix[b] = 0ull;
   if (tid == 0) vs.ovf = 0;
   __syncthreads();
-  for (int k = tid; k < n_ind; k += NT) {
-    const int b = s.list_id[k] >> kIdBits;
-    if (b < 1) continue;
-    atomicAdd(&cnt[b], 1u << kIndShift);
-    const float y = s.list_val[k];
-    const int eu = unit_expo(b);
-    const uint32_t eb = __float_as_uint(mass(y));
-    const int ek = (int)((eb >> 23) & 0xFFu);
-    if (eu == 0 || ek == 0) continue;  // below 2^-126 of the maximum: nothing
-    const int sft = ek - eu;
-    if (sft < 0 || sft > 24) { vs.ovf = 1; continue; }
-    atomicAdd(reinterpret_cast<unsigned long long *>(&lfix[b]),
-              (unsigned long long)((eb & 0x7FFFFFu) | 0x800000u) << sft);
+  // (a thread takes four adjacent entries, read in one 16-byte access per
+  // array; their adds are independent of each other)
+  static_assert(kGatherCap % 4 == 0, "16-byte list rows");
+  for (int k0 = 4 * tid; k0 < n_ind; k0 += 4 * NT) {
+    const int4 i4 = *reinterpret_cast<const int4 *>(s.list_id + k0);
+    const float4 y4 = *reinterpret_cast<const float4 *>(s.list_val + k0);
+    const int iq[4] = {i4.x, i4.y, i4.z, i4.w};
+    const float yq[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = iq[q] >> kIdBits;
+      if (k0 + q >= n_ind || b < 1) continue;
+      atomicAdd(&cnt[b], 1u << kIndShift);
+      const int eu = unit_expo(b);
+      const uint32_t eb = __float_as_uint(mass(yq[q]));
+      const int ek = (int)((eb >> 23) & 0xFFu);
+      if (eu == 0 || ek == 0) continue;  // below 2^-126 of the maximum: nothing
+      const int sft = ek - eu;
+      if (sft < 0 || sft > 24) { vs.ovf = 1; continue; }
+      atomicAdd(reinterpret_cast<unsigned long long *>(&lfix[b]),
+                (unsigned long long)((eb & 0x7FFFFFu) | 0x800000u) << sft);
+    }
   }
   __syncthreads();
   if (uni(vs.ovf) != 0) fallback = true;
@@ -666,6 +685,9 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       vs.n_ind_b = 0;  // (the counters of the first view)
       vs.n_tie_b = 0;
       vs.n_above_b = 0;
+      vs.n_ind_b2 = 0;  // (and of the predicted draw's view)
+      vs.n_tie_b2 = 0;
+      vs.n_above_b2 = 0;
     }
     __syncthreads();
     double after = 0.0;
@@ -685,7 +707,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   above[tid] = incl - part;
   const bool use_top_p = a.top_p < 1.0f;
   const double pw = (double)a.top_p * W;
-  const double u = (double)a.uniforms[row];
+  const double u = (double)uni(u_row);
   if (tid * BPT < NB) {
     double C = above[tid];
     const double2 ma = reinterpret_cast<const double2 *>(bmass)[2 * tid];
@@ -696,12 +718,17 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       const int b = tid * BPT + q;
       const double Cb1 = C;
       C += mq[q];
-      if (use_top_p && Cb1 < pw && C >= pw) { sh.bin_p = b; sh.sbase = Cb1; }
+      if (use_top_p && Cb1 < pw && C >= pw) {
+        sh.bin_p = b;
+        sh.sbase = Cb1;
+        vs.mbp = mq[q];
+      }
     }
   }
   __syncthreads();
   const int bp = uni(sh.bin_p);
   const double C_bp1 = bp >= 0 ? uni(sh.sbase) : 0.0;  // mass above the boundary bin
+  const double m_bp = bp >= 0 ? uni(vs.mbp) : 0.0;     // the boundary bin's own mass
 
   // View of bin b (all threads): its value, its individuals other than the
   // value ordered by key into okey / oval, the tie group's size.  Returns
@@ -775,22 +802,6 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   int cut_pos = 0x7FFFFFFF;
   int bs = -1;
   double bs_start = 0.0;
-  if (!fallback && bp >= 0) {
-    if (!view_bin(bp)) {
-      fallback = true;
-    } else {
-      if (uni(wid) == 0) {
-        wave_walk(true, C_bp1, pw, vs.view, okey, oval, 0x7FFFFFFF, &vs.walk[0]);
-      }
-      __syncthreads();
-      cut_kind = uni(vs.walk[0].kind);
-      if (cut_kind == kFail) fallback = true;
-      Wp = uni(vs.walk[0].acc);
-      cut_pos = uni(vs.walk[0].pos);
-      if (cut_kind == kInd) kcut = uni(vs.walk[0].key);
-    }
-  }
-  const double target = u * Wp;
   // The count pass for the draw's member (all threads), run while wave 0
   // walks the draw's bin: every lane counts the members of the bin's value
   // vv in each of its chunks (a nonzero value by its bf16 pattern, a zero
@@ -819,7 +830,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     }
     return mb;
   };
-  auto count_setup = [&](float v, int ntie) {  // (ntie: the view's individuals equal to v)
+  auto count_setup = [&](float v, int ntie, const int *tie_ids) {  // (ntie: the view's individuals equal to v)
     vv = v;
     ltie_all = ntie > 0;
     if (ltie_all) {
@@ -830,7 +841,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
         atomicOr(&tiew[t >> 1], 1u << ((t & 1) * 16 + ci));
       };
       if (ntie <= kTieCap) {
-        if (tid < ntie) mark(vs.tie_id[tid]);
+        if (tid < ntie) mark(tie_ids[tid]);
       } else {
         for (int k = tid; k < n_list; k += NT)
           if (s.list_val[k] == vv) mark(s.list_id[k] & kIdMask);
@@ -879,17 +890,18 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     }
   };
 
-  // The draw's bin: the bin whose cumulative mass interval holds the target
-  // (bp counts only its kept part); every thread checks its own bins.
-  if (!fallback) {
-    // (the counters of a second view, first counted after the barrier that
-    // ends the search)
-    if (tid == 0) {
-      vs.n_ind_b = 0;
-      vs.n_tie_b = 0;
-      vs.n_above_b = 0;
-    }
-    if (tid * BPT < NB) {
+  // The draw's bin before the boundary's walk: the kept mass lies between
+  // the mass above the boundary bin and that plus the bin's own, so the
+  // draw's target lies between u times either.  When both ends fall inside
+  // one bin above the boundary bin, that bin is the draw's: its view and
+  // the count of its value's members then run beside the boundary's walk.
+  uint64_t *okey2 = reinterpret_cast<uint64_t *>(smem + kVView2Off);
+  float *oval2 = reinterpret_cast<float *>(okey2 + kGatherCap2);
+  uint64_t *gkey2 = reinterpret_cast<uint64_t *>(oval2 + kGatherCap2);
+  float *gval2 = reinterpret_cast<float *>(gkey2 + kGatherCap2);
+  {
+    const double tlo = u * (bp >= 0 ? C_bp1 : W), thi = u * (bp >= 0 ? C_bp1 + m_bp : W);
+    if (!fallback && tid * BPT < NB) {
       double C = above[tid];
       const double2 ma = reinterpret_cast<const double2 *>(bmass)[2 * tid];
       const double2 mb = reinterpret_cast<const double2 *>(bmass)[2 * tid + 1];
@@ -897,36 +909,190 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
 #pragma unroll
       for (int q = BPT - 1; q >= 0; --q) {
         const int b = tid * BPT + q;
-        if (b < 1) continue;
-        const double m = (bp >= 0 && b == bp) ? (Wp - C_bp1) : mq[q];
-        if (m > 0.0 && C <= target && target < C + m && (bp < 0 || b >= bp)) {
+        const double m = mq[q];
+        if (b >= 1 && b > bp && m > 0.0 && C <= tlo && thi < C + m) {
           sh.bin_hi = b;
-          sh.sbase = C;
+          vs.sbase2 = C;
+          vs.mbq = m;
         }
         C += m;
       }
     }
-    __syncthreads();
-    bs = uni(sh.bin_hi);
-    bs_start = uni(sh.sbase);
-    if (bs < 0) {
-      fallback = true;  // rounding left the target outside every bin
+  }
+  __syncthreads();
+  const int bq = fallback ? -1 : uni(sh.bin_hi);
+  bool pred = false;
+  if (bq >= 0) {
+    // both views in one pass over the list
+    const float v0 = bp >= 0 ? bin_value(bp) : 0.0f, v1 = bin_value(bq);
+    const bool need0 = bp >= 0 && (uni(cnt[bp]) >> kIndShift) != 0u;
+    const bool need1 = (uni(cnt[bq]) >> kIndShift) != 0u;
+    if (need0 || need1) {
+      for (int k = tid; k < n_ind; k += NT) {
+        const int tagged = s.list_id[k];
+        const int tb = tagged >> kIdBits;
+        if (tb != bp && tb != bq) continue;
+        const float y = s.list_val[k];
+        const int id = tagged & kIdMask;
+        const bool one = tb == bq;
+        if (y == (one ? v1 : v0)) {
+          const int slot = atomicAdd(one ? &vs.n_tie_b2 : &vs.n_tie_b, 1);
+          if (slot < kTieCap) (one ? vs.tie_id2 : vs.tie_id)[slot] = id;
+        } else {
+          const int slot = atomicAdd(one ? &vs.n_ind_b2 : &vs.n_ind_b, 1);
+          if (slot < (one ? kGatherCap2 : kGatherCap)) {
+            (one ? gkey2 : gkey)[slot] = sel_key(y, (uint32_t)id);
+            (one ? gval2 : gval)[slot] = mass(y);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const int n0 = need0 ? uni(vs.n_ind_b) : 0, n1 = need1 ? uni(vs.n_ind_b2) : 0;
+    const int t0 = need0 ? uni(vs.n_tie_b) : 0, t1 = need1 ? uni(vs.n_tie_b2) : 0;
+    // (each view ordered by one wave: at most 64 individuals each)
+    pred = n0 <= kWave && n1 <= kGatherCap2 && t0 <= kTieCap && t1 <= kTieCap;
+    if (!pred) {
+      if (tid == 0) {  // (the counters start again for the views taken one by one)
+        vs.n_ind_b = 0;
+        vs.n_tie_b = 0;
+        vs.n_above_b = 0;
+      }
+      __syncthreads();
     } else {
-      // (the same bin as the boundary: the view is still in place)
-      const bool same = bs == bp && bp >= 0;
-      if (!same && !view_bin(bs)) {
+      if (wid == 0 && lane < n0) {
+        const uint64_t ki = gkey[lane];
+        int r = 0;
+        for (int j = 0; j < n0; ++j) r += gkey[j] > ki;
+        okey[r] = ki;
+        oval[r] = gval[lane];
+        if (key_score(ki) > v0) atomicAdd(&vs.n_above_b, 1);
+      }
+      if (wid == 1 && lane < n1) {
+        const uint64_t ki = gkey2[lane];
+        int r = 0;
+        for (int j = 0; j < n1; ++j) r += gkey2[j] > ki;
+        okey2[r] = ki;
+        oval2[r] = gval2[lane];
+        if (key_score(ki) > v1) atomicAdd(&vs.n_above_b2, 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        if (bp >= 0) {
+          vs.view.single = 1;
+          vs.view.v = v0;
+          vs.view.e = v0 == -INFINITY ? 0.0f : mass(v0);
+          vs.view.n_ind = n0;
+          vs.view.n_above = need0 ? vs.n_above_b : 0;
+          vs.view.n_group = (int)(cnt[bp] & kDenseMask) + t0;
+        }
+        vs.view2.single = 1;
+        vs.view2.v = v1;
+        vs.view2.e = v1 == -INFINITY ? 0.0f : mass(v1);
+        vs.view2.n_ind = n1;
+        vs.view2.n_above = need1 ? vs.n_above_b2 : 0;
+        vs.view2.n_group = (int)(cnt[bq] & kDenseMask) + t1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      count_setup(v1, t1, vs.tie_id2);
+      const double sb2 = uni(vs.sbase2), mb2 = uni(vs.mbq);
+      if (uni(wid) == 0) {
+        // the boundary's walk gives the kept mass, hence the draw's target,
+        // which must fall in the predicted bin
+        double wp = W;
+        if (bp >= 0) {
+          wave_walk(true, C_bp1, pw, vs.view, okey, oval, 0x7FFFFFFF, &vs.walk[0]);
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          wp = vs.walk[0].acc;
+        }
+        const double tg = u * wp;
+        if (tg >= sb2 && tg < sb2 + mb2) {
+          wave_walk(false, sb2, tg, vs.view2, okey2, oval2, 0x7FFFFFFF, &vs.walk[1]);
+        } else if (lane == 0) {
+          vs.walk[1].kind = kFail;  // (rounding put it elsewhere: the bisection)
+        }
+      }
+      count_rows();  // (wave 0 after its walks, the others meanwhile)
+      __syncthreads();
+      if (bp >= 0) {
+        cut_kind = uni(vs.walk[0].kind);
+        if (cut_kind == kFail) fallback = true;
+        Wp = uni(vs.walk[0].acc);
+        cut_pos = uni(vs.walk[0].pos);
+        if (cut_kind == kInd) kcut = uni(vs.walk[0].key);
+      }
+      bs = bq;
+      bs_start = sb2;
+      draw_kind = uni(vs.walk[1].kind);
+      if (draw_kind == kFail) fallback = true;
+    }
+  }
+  if (!pred) {
+    if (!fallback && bp >= 0) {
+      if (!view_bin(bp)) {
         fallback = true;
       } else {
-        count_setup(bin_value(bs), same ? uni(vs.view_ntie) : uni(vs.n_tie_b));
         if (uni(wid) == 0) {
-          wave_walk(false, bs_start, target, vs.view, okey, oval, same ? cut_pos : 0x7FFFFFFF, &vs.walk[1]);
+          wave_walk(true, C_bp1, pw, vs.view, okey, oval, 0x7FFFFFFF, &vs.walk[0]);
         }
-        count_rows();  // (wave 0 after its walk, the others meanwhile)
         __syncthreads();
-        draw_kind = uni(vs.walk[1].kind);
+        cut_kind = uni(vs.walk[0].kind);
+        if (cut_kind == kFail) fallback = true;
+        Wp = uni(vs.walk[0].acc);
+        cut_pos = uni(vs.walk[0].pos);
+        if (cut_kind == kInd) kcut = uni(vs.walk[0].key);
       }
     }
-    if (draw_kind == kFail) fallback = true;
+    const double target = u * Wp;
+    // The draw's bin: the bin whose cumulative mass interval holds the target
+    // (bp counts only its kept part); every thread checks its own bins.
+    if (!fallback) {
+      // (the counters of a second view, first counted after the barrier that
+      // ends the search)
+      if (tid == 0) {
+        vs.n_ind_b = 0;
+        vs.n_tie_b = 0;
+        vs.n_above_b = 0;
+      }
+      if (tid * BPT < NB) {
+        double C = above[tid];
+        const double2 ma = reinterpret_cast<const double2 *>(bmass)[2 * tid];
+        const double2 mb = reinterpret_cast<const double2 *>(bmass)[2 * tid + 1];
+        const double mq[4] = {ma.x, ma.y, mb.x, mb.y};
+  #pragma unroll
+        for (int q = BPT - 1; q >= 0; --q) {
+          const int b = tid * BPT + q;
+          if (b < 1) continue;
+          const double m = (bp >= 0 && b == bp) ? (Wp - C_bp1) : mq[q];
+          if (m > 0.0 && C <= target && target < C + m && (bp < 0 || b >= bp)) {
+            sh.bin_hi = b;
+            sh.sbase = C;
+          }
+          C += m;
+        }
+      }
+      __syncthreads();
+      bs = uni(sh.bin_hi);
+      bs_start = uni(sh.sbase);
+      if (bs < 0) {
+        fallback = true;  // rounding left the target outside every bin
+      } else {
+        // (the same bin as the boundary: the view is still in place)
+        const bool same = bs == bp && bp >= 0;
+        if (!same && !view_bin(bs)) {
+          fallback = true;
+        } else {
+          count_setup(bin_value(bs), same ? uni(vs.view_ntie) : uni(vs.n_tie_b), vs.tie_id);
+          if (uni(wid) == 0) {
+            wave_walk(false, bs_start, target, vs.view, okey, oval, same ? cut_pos : 0x7FFFFFFF, &vs.walk[1]);
+          }
+          count_rows();  // (wave 0 after its walk, the others meanwhile)
+          __syncthreads();
+          draw_kind = uni(vs.walk[1].kind);
+        }
+      }
+      if (draw_kind == kFail) fallback = true;
+    }
   }
 
   // ---- 5. one pass over the registers: the draw's rank in its tie group -----
@@ -946,7 +1112,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
     if (wid < R) {
       rc = (int)((rsum[lane * 4 + (wid >> 2)] >> ((wid & 3) * 8)) & 0xFFu);
       rinc = wave_incl_scan_i32(rc);
-      if (lane == kWave - 1) vs.wtot[0][0][wid] = rinc;  // the chunk index's total
+      if (lane == kWave - 1) vs.wtot[wid] = rinc;  // the chunk index's total
     }
     __syncthreads();
     // (inclusive sums within a row of 16 lanes by row moves)
@@ -958,7 +1124,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
       return v;
     };
     if (wid == 0) {
-      const int T = lane < R ? vs.wtot[0][0][lane] : 0;
+      const int T = lane < R ? vs.wtot[lane] : 0;
       const int inc = row16_incl_scan(T);
       const int k = vs.gk[1];
       if (lane < 16 && inc - T < k && k <= inc) {

@@ -46,13 +46,16 @@ constexpr int kVCopies = 4;                 // histogram copies, by lane
 constexpr int kZoneExp = 8;                 // scores below 2^-kZoneExp in magnitude share a bin
 constexpr float kDropNats = 36.0f;          // bins start this far below the first chunks' max
 constexpr int kZoneCap = 512;               // near-zero scores listed one by one
+constexpr int kVPipe = 4;                   // chunks in flight per lane while counting
 constexpr int kVHistBytes = kVCopies * kVStride * 4;  // the copies, from LDS byte 0
 constexpr int kVMassOff = kVStride * 4;     // after the fold: per-bin masses (doubles)
 constexpr int kVViewOff = kVMassOff + kVBins * 8;     // then the ordered view of one bin
 constexpr int kVRowSharedBytes = 1024;      // the row's shared scalars, then the kernel's own
 constexpr int kVSharedBytes = 4096;
 constexpr int kVAboveOff = kVViewOff + 24 * kGatherCap;  // then one double per thread
-static_assert(kVAboveOff + 8 * kSelectThreads <= kVHistBytes, "beyond the copies");
+constexpr int kGatherCap2 = 64;            // individuals of a second view (the predicted draw's)
+constexpr int kVView2Off = kVAboveOff + 8 * kSelectThreads;  // then that view
+static_assert(kVView2Off + 24 * kGatherCap2 <= kVHistBytes, "beyond the copies");
 static_assert((kVCopies - 1) * kVStride * 4 + (kVBins - 1) * 4 < 65536,
               "bin offsets are computed in 16 bits");
 
