@@ -82,6 +82,10 @@ typedef struct tsel_params {
   float temperature;            /* > 0 when sampling; 1 = off */
   int32_t top_k;                /* >= 0; 0 = off */
   float top_p;                  /* in (0, 1]; 1 = off */
+
+  int32_t renormalize_logits;   /* nonzero: the log-softmax of the row after the
+                                   processors, before temperature (module doc) */
+  int32_t output_logprobs;      /* nonzero: out_logprobs is given ("Log-probabilities") */
 } tsel_params;
 
 /*
@@ -91,7 +95,8 @@ typedef struct tsel_params {
  * Generation" (module doc; "Lengths"): repetition_penalty,
  * no_repeat_ngram_size, single-token bad words, min_length /
  * min_new_tokens, forced_bos_token_id, forced_eos_token_id, suppress_tokens,
- * begin_suppress_tokens; then, when sampling, temperature, top_k and top_p;
+ * begin_suppress_tokens, renormalize_logits when set; then, when sampling,
+ * temperature, top_k and top_p;
  * then selects the token: the argmax (lowest id among equal scores) when
  * greedy, else the inverse CDF of uniforms[b] over the kept ids taken in
  * (score descending, id ascending) order.  Removed ids score -inf; a forced
@@ -114,21 +119,33 @@ typedef struct tsel_params {
  *  out_processed  device float [B, V] or NULL: the final scores the token is
  *              chosen from (after top_p when sampling).  A debugging and
  *              parity aid: it costs one extra pass over each row.
+ *  out_logprobs   device float [B], given iff params->output_logprobs: the
+ *              log-softmax of those final scores at the selected token, in
+ *              binary64 rounded to binary32; the quiet NaN with sign bit 0
+ *              for a padding row, and NaN for a row whose scores are all
+ *              -inf ("Transmuter.Generation", "Log-probabilities", and the
+ *              function doc of generate/5).  It costs a write and a read of
+ *              the final scores (into the workspace when out_processed is
+ *              NULL).
  *  workspace, workspace_bytes  device scratch of at least
- *              tsel_process_select_workspace_size(params) bytes (NULL/0 when
- *              that is 0).
+ *              tsel_process_select_workspace_size(params) bytes, 256-byte
+ *              aligned (NULL/0 when that is 0): fp32 rows of the
+ *              renormalized scores when renormalize_logits is set, and of
+ *              the final scores when output_logprobs is.
  *
  * Errors: TSEL_ERR_INVALID_ARG for B < 0, V < 1, a stride below V, a
  * hist_stride below 0, penalty <= 0, n < 0, min lengths < 0, n_eos outside
  * [0, TSEL_MAX_EOS], an unknown dtype, temperature <= 0 / top_k < 0 / top_p
- * outside (0, 1] when sampling, or a NULL required pointer;
+ * outside (0, 1] when sampling, a NULL required pointer, or out_logprobs
+ * given without output_logprobs (or the reverse); TSEL_ERR_WORKSPACE when
+ * the workspace is missing or too small;
  * TSEL_ERR_UNSUPPORTED for a misaligned row layout or a vocabulary too large
  * for the on-chip masks (V > 524,288).
  */
 tsel_status tsel_process_select(const void *logits, const int32_t *history,
                                 const int32_t *lens, const tsel_params *params,
                                 const float *uniforms, int32_t *out_tokens,
-                                float *out_processed, void *workspace,
+                                float *out_processed, float *out_logprobs, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
 /* Workspace bytes tsel_process_select needs for these params (0 if none). */

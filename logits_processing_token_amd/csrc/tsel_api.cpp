@@ -194,24 +194,29 @@ tsel_status tsel_validate_params(const tsel_params *params, int32_t sampling_uni
   return check_params(params, sampling_uniforms_given != 0);
 }
 
-size_t tsel_process_select_workspace_size(const tsel_params *params) {
-  (void)params;
-  return 0;
+// Rows of the workspace: the renormalized scores (fp32, a 16-byte aligned
+// stride) when renormalize_logits is on, then the final scores a
+// log-probability is taken over (fp32 [B, V]) when output_logprobs is.
+static size_t renorm_stride(const tsel_params *p) { return ((size_t)p->vocab + 3) & ~size_t(3); }
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+static size_t renorm_bytes(const tsel_params *p) {
+  return p->renormalize_logits ? align256((size_t)p->batch * renorm_stride(p) * 4) : 0;
 }
 
-tsel_status tsel_process_select(const void *logits, const int32_t *history, const int32_t *lens,
-                                const tsel_params *params, const float *uniforms,
-                                int32_t *out_tokens, float *out_processed, void *workspace,
-                                size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  tsel_status st = check_params(params, uniforms != nullptr);
-  if (st != TSEL_OK) return st;
-  if (params->batch == 0) return TSEL_OK;
-  if (!logits || !lens || !out_tokens) return TSEL_ERR_INVALID_ARG;
-  if (!history && params->hist_stride > 0) return TSEL_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
+size_t tsel_process_select_workspace_size(const tsel_params *params) {
+  if (!params || params->batch <= 0 || params->vocab < 1) return 0;
+  size_t n = renorm_bytes(params);
+  if (params->output_logprobs) n += align256((size_t)params->batch * (size_t)params->vocab * 4);
+  return n;
+}
 
+// The kernels for one selection over `logits` with the settings of p (the
+// arguments already checked); hipErrorNotSupported when V does not fit the
+// on-chip layout.
+static hipError_t dispatch_select(const tsel_params *params, const void *logits,
+                                  const int32_t *history, const int32_t *lens,
+                                  const float *uniforms, int32_t *out_tokens, float *out_processed,
+                                  hipStream_t s) {
   tsel::SelectArgs a{};
   const int64_t esize = params->dtype == TSEL_BF16 ? 2 : 4;
   a.logits = static_cast<const char *>(logits);
@@ -240,22 +245,20 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
   a.temperature = params->temperature;
   a.top_k = params->top_k;
   a.top_p = params->top_p;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   size_t lds = 0;
   hipError_t e = hipSuccess;
   if (!a.do_sample) {  // greedy: the warpers do not apply
     a.temperature = 1.0f;
     a.top_k = 0;
     a.top_p = 1.0f;
-    if (!plan_layout(params, SelectKernel::kGreedy, &a, &lds)) return TSEL_ERR_UNSUPPORTED;
+    if (!plan_layout(params, SelectKernel::kGreedy, &a, &lds)) return hipErrorNotSupported;
     e = tsel::launch_greedy(a, lds, s);
   } else {
     tsel::SelectArgs t = a;
     size_t tlds = 0;
     const bool topk = a.top_k > 0 && plan_layout(params, SelectKernel::kTopK, &t, &tlds) &&
                       std::min(a.top_k, a.V) * 4 <= t.tcap;
-    if (!plan_layout(params, SelectKernel::kFull, &a, &lds))
-      return TSEL_ERR_UNSUPPORTED;
+    if (!plan_layout(params, SelectKernel::kFull, &a, &lds)) return hipErrorNotSupported;
     const int res = resident_chunks(params);
     const int epc = params->dtype == TSEL_BF16 ? 8 : 4;
     tsel::SelectArgs r = a;
@@ -286,6 +289,79 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
       e = tsel::launch_full(a, resident_chunks(params), lds, s, 0);
     }
   }
+  return e;
+}
+
+tsel_status tsel_process_select(const void *logits, const int32_t *history, const int32_t *lens,
+                                const tsel_params *params, const float *uniforms,
+                                int32_t *out_tokens, float *out_processed, float *out_logprobs,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  tsel_status st = check_params(params, uniforms != nullptr);
+  if (st != TSEL_OK) return st;
+  if ((out_logprobs != nullptr) != (params->output_logprobs != 0)) return TSEL_ERR_INVALID_ARG;
+  if (params->batch == 0) return TSEL_OK;
+  if (!logits || !lens || !out_tokens) return TSEL_ERR_INVALID_ARG;
+  if (!history && params->hist_stride > 0) return TSEL_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
+  const size_t need = tsel_process_select_workspace_size(params);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TSEL_ERR_WORKSPACE;
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TSEL_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  tsel_params p = *params;
+  const void *src = logits;
+  hipError_t e = hipSuccess;
+  if (params->renormalize_logits) {
+    // the processors and the log-softmax into fp32 rows; the selection then
+    // reads those with every processor switched off (the lengths still mark
+    // padding rows)
+    tsel::SelectArgs ra{};
+    size_t lds = 0;
+    if (!plan_layout(params, SelectKernel::kGreedy, &ra, &lds)) return TSEL_ERR_UNSUPPORTED;
+    const int64_t esize = params->dtype == TSEL_BF16 ? 2 : 4;
+    ra.logits = static_cast<const char *>(logits);
+    ra.row_bytes = params->logits_row_stride * esize;
+    ra.V = params->vocab;
+    ra.B = params->batch;
+    ra.dtype = params->dtype;
+    ra.hist = history;
+    ra.hist_stride = params->hist_stride;
+    ra.lens = lens;
+    ra.bad_mask = params->bad_words_mask;
+    ra.sup_mask = params->suppress_mask;
+    ra.begin_mask = params->begin_suppress_mask;
+    ra.rep = params->repetition_penalty;
+    ra.ngram = params->no_repeat_ngram_size;
+    ra.min_length = params->min_length;
+    ra.min_new = params->min_new_tokens;
+    ra.n_eos = params->n_eos;
+    for (int i = 0; i < TSEL_MAX_EOS; ++i)
+      ra.eos[i] = i < params->n_eos ? params->eos_ids[i] : -1;
+    ra.forced_bos = params->forced_bos_token_id;
+    ra.forced_eos = params->forced_eos_token_id;
+    ra.temperature = 1.0f;
+    ra.top_p = 1.0f;
+    e = tsel::launch_renorm(ra, lds, reinterpret_cast<float *>(ws), (int64_t)renorm_stride(params), s);
+    if (e != hipSuccess) return TSEL_ERR_LAUNCH;
+    src = ws;
+    p.dtype = TSEL_F32;
+    p.logits_row_stride = (int64_t)renorm_stride(params);
+    p.repetition_penalty = 1.0f;
+    p.no_repeat_ngram_size = 0;
+    p.bad_words_mask = p.suppress_mask = p.begin_suppress_mask = nullptr;
+    p.min_length = p.min_new_tokens = 0;
+    p.n_eos = 0;
+    p.forced_bos_token_id = p.forced_eos_token_id = -1;
+    p.renormalize_logits = 0;
+    ws += renorm_bytes(params);
+  }
+  float *proc = out_processed;
+  if (out_logprobs && !proc) proc = reinterpret_cast<float *>(ws);
+  e = dispatch_select(&p, src, history, lens, uniforms, out_tokens, proc, s);
+  if (e == hipErrorNotSupported) return TSEL_ERR_UNSUPPORTED;  // (a layout that does not fit)
+  if (e == hipSuccess && out_logprobs)
+    e = tsel::launch_logprob(proc, params->vocab, params->batch, params->vocab, out_tokens,
+                             out_logprobs, s);
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 

@@ -103,6 +103,11 @@ hipError_t launch_res(const SelectArgs &a, int res, size_t lds, hipStream_t s);
 // the same on bf16 rows with one histogram bin per bf16 value
 hipError_t launch_vres(const SelectArgs &a, int res, size_t lds, hipStream_t s);
 
+hipError_t launch_renorm(const SelectArgs &a, size_t lds, float *dst, int64_t dst_stride,
+                         hipStream_t s);
+hipError_t launch_logprob(const float *proc, int64_t stride, int32_t B, int32_t V,
+                          const int32_t *tokens, float *out, hipStream_t s);
+
 hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
                          int64_t row_bytes, int32_t chunks, const int32_t *cand,
                          int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,

@@ -52,6 +52,7 @@ class Params(C.Structure):
         ("forced_bos_token_id", C.c_int32), ("forced_eos_token_id", C.c_int32),
         ("do_sample", C.c_int32), ("temperature", C.c_float), ("top_k", C.c_int32),
         ("top_p", C.c_float),
+        ("renormalize_logits", C.c_int32), ("output_logprobs", C.c_int32),
     ]
 
 
@@ -69,7 +70,8 @@ def load() -> C.CDLL:
     lib = C.CDLL(LIB_PATH)
     vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     lib.tsel_process_select.restype = i32
-    lib.tsel_process_select.argtypes = [vp, vp, vp, C.POINTER(Params), vp, vp, vp, vp, sz, vp]
+    lib.tsel_process_select.argtypes = [vp, vp, vp, C.POINTER(Params), vp, vp, vp, vp, vp, sz,
+                                        vp]
     lib.tsel_process_select_workspace_size.restype = sz
     lib.tsel_process_select_workspace_size.argtypes = [C.POINTER(Params)]
     lib.tsel_validate_params.restype = i32
@@ -140,6 +142,8 @@ def make_params(batch: int, vocab: int, row_stride: int, dtype: int, hist_stride
     p.temperature = settings.get("temperature", 1.0)
     p.top_k = settings.get("top_k", 0)
     p.top_p = settings.get("top_p", 1.0)
+    p.renormalize_logits = int(bool(settings.get("renormalize_logits", False)))
+    p.output_logprobs = int(bool(settings.get("output_logprobs", False)))
     return p
 
 
@@ -147,17 +151,32 @@ def validate(params: Params, uniforms_given: bool = True) -> int:
     return int(load().tsel_validate_params(C.byref(params), int(uniforms_given)))
 
 
+def process_select_workspace_size(params: Params) -> int:
+    return int(load().tsel_process_select_workspace_size(C.byref(params)))
+
+
 def process_select(logits, history, lens, params: Params, uniforms=None, out_tokens=None,
-                   out_processed=None, stream=None):
-    """Run tsel_process_select; returns out_tokens (allocated if None)."""
+                   out_processed=None, out_logprobs=None, workspace=None, stream=None):
+    """Run tsel_process_select; returns out_tokens (allocated if None).  When
+    params.output_logprobs is set, out_logprobs (float32 [B]) is allocated if
+    None and returned as well: (out_tokens, out_logprobs).  The workspace
+    (a uint8 device tensor) is allocated when None and the call needs one."""
     import torch
     lib = load()
     if out_tokens is None:
         out_tokens = torch.empty(params.batch, dtype=torch.int32, device=logits.device)
+    if params.output_logprobs and out_logprobs is None:
+        out_logprobs = torch.empty(params.batch, dtype=torch.float32, device=logits.device)
+    need = process_select_workspace_size(params)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     st = lib.tsel_process_select(_ptr(logits), _ptr(history), _ptr(lens), C.byref(params),
                                  _ptr(uniforms), _ptr(out_tokens), _ptr(out_processed),
-                                 None, 0, _stream(stream))
+                                 _ptr(out_logprobs), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "tsel_process_select")
+    if params.output_logprobs:
+        return out_tokens, out_logprobs
     return out_tokens
 
 

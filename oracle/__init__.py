@@ -54,6 +54,7 @@ class _Cfg(C.Structure):
         ("begin_ids", C.POINTER(C.c_int32)), ("n_begin", C.c_int32),
         ("do_sample", C.c_int32), ("temperature", C.c_float),
         ("top_k", C.c_int32), ("top_p", C.c_float),
+        ("renormalize_logits", C.c_int32),
     ]
 
 
@@ -64,6 +65,7 @@ class _Res(C.Structure):
         ("greedy_margin", C.c_double), ("n_admissible", C.c_int32),
         ("admissible", C.c_int32 * MAX_ADMISSIBLE),
         ("keep_min", C.c_int32), ("keep_max", C.c_int32),
+        ("logprob", C.c_float),
     ]
 
 
@@ -116,6 +118,7 @@ class Config:
     temperature: float = 1.0
     top_k: int = 0
     top_p: float = 1.0
+    renormalize_logits: bool = False
 
 
 def _ids(seq) -> np.ndarray:
@@ -145,7 +148,8 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
     Returns a dict of numpy arrays indexed like ``rows``: token, n_finite,
     topk_threshold, margin, greedy_margin, admissible (list of arrays),
     keep_min and keep_max (the kept counts top_p allows under the margin
-    policy's perturbation) and, when asked, processed [len(rows), V] float32.
+    policy's perturbation), logprob (the token's log-probability, NaN for a
+    padding row) and, when asked, processed [len(rows), V] float32.
     """
     lib = _load()
     logits = np.ascontiguousarray(logits)
@@ -167,7 +171,8 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
         begin_ids=_ptr(keep["begin_suppress_tokens"]),
         n_begin=keep["begin_suppress_tokens"].size,
         do_sample=int(bool(cfg.do_sample)), temperature=cfg.temperature,
-        top_k=cfg.top_k, top_p=cfg.top_p)
+        top_k=cfg.top_k, top_p=cfg.top_p,
+        renormalize_logits=int(bool(cfg.renormalize_logits)))
     if cfg.do_sample and uniforms is None:
         raise ValueError("sampling needs one uniform per row")
     u = (np.zeros(B, np.float32) if uniforms is None
@@ -178,6 +183,7 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
         "topk_threshold": np.empty(n, np.float32), "margin": np.empty(n, np.float64),
         "greedy_margin": np.empty(n, np.float64), "admissible": [None] * n,
         "keep_min": np.empty(n, np.int32), "keep_max": np.empty(n, np.int32),
+        "logprob": np.empty(n, np.float32),
     }
     processed = np.empty((n, V), np.float32) if want_processed else None
     esize = logits.itemsize
@@ -203,6 +209,7 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
         out["admissible"][i] = np.array(res.admissible[:res.n_admissible], np.int32)
         out["keep_min"][i] = res.keep_min
         out["keep_max"][i] = res.keep_max
+        out["logprob"][i] = res.logprob
 
     if threads > 1 and n > 1:
         with ThreadPoolExecutor(max_workers=threads) as ex:

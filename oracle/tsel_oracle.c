@@ -59,6 +59,7 @@ typedef struct {
   float temperature;             /* 1.0 = identity */
   int32_t top_k;                 /* 0 = off */
   float top_p;                   /* >= 1.0 = off */
+  int32_t renormalize_logits;    /* 0 = off */
 } oracle_cfg;
 
 typedef struct {
@@ -72,6 +73,8 @@ typedef struct {
   int32_t keep_min, keep_max;    /* ids top_p keeps for sure / may keep when
                                     each normalized mass before an id moves
                                     by at most eps (sampling; else n_finite) */
+  float logprob;                 /* log-softmax of the final scores at the token
+                                    (quiet NaN for a row with no token) */
 } oracle_row_result;
 
 /* ------------------------------------------------------------------ */
@@ -133,6 +136,44 @@ static int32_t argmax_lowest(const float *x, int32_t V) {
   for (int32_t v = 1; v < V; ++v)
     if (x[v] > x[best]) best = v;
   return best;
+}
+
+/* log(sum over the finite scores of exp(x - m)), m the largest finite
+ * score, in binary64; returns -inf (and m = -inf) when none is finite. */
+static double log_sum_exp_shifted(const float *x, int32_t V, double *m_out) {
+  double m = -INFINITY;
+  for (int32_t v = 0; v < V; ++v)
+    if ((double)x[v] > m) m = (double)x[v];
+  *m_out = m;
+  if (m == -INFINITY) return -INFINITY;
+  double sum = 0.0;
+  for (int32_t v = 0; v < V; ++v)
+    if (x[v] > -INFINITY) sum += exp((double)x[v] - m);
+  return log(sum);
+}
+
+/* [T] module doc, renormalize_logits (after the processors of the task,
+ * before temperature): the log-softmax of the row.  Reading: the largest
+ * score m and ls = log(sum exp(x - m)) rounded once to binary32, then two
+ * binary32 subtractions, (x - m) - ls; -inf stays -inf; a row with no finite
+ * score is left as it is. */
+static void renormalize(float *x, int32_t V) {
+  double m;
+  const double ls = log_sum_exp_shifted(x, V, &m);
+  if (m == -INFINITY) return;
+  const float mf = (float)m, lsf = (float)ls;
+  for (int32_t v = 0; v < V; ++v)
+    if (x[v] > -INFINITY) x[v] = (x[v] - mf) - lsf;
+}
+
+/* [T] "Log-probabilities": the log-softmax of the scores the step selects
+ * from, at the token: x[t] - m - log(sum exp(x - m)) in binary64, rounded
+ * once to binary32 (all scores -inf: NaN, as the arithmetic gives). */
+static float token_logprob(const float *x, int32_t V, int32_t t) {
+  double m;
+  const double ls = log_sum_exp_shifted(x, V, &m);
+  if (m == -INFINITY) return NAN;
+  return (float)(((double)x[t] - m) - ls);
 }
 
 static int cmp_float_desc(const void *a, const void *b) {
@@ -261,6 +302,7 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
    * token, reported as -1. */
   if (L == 0) {
     res->token = -1;
+    res->logprob = NAN;
     if (x_out)
       for (int32_t v = 0; v < V; ++v) x_out[v] = -INFINITY;
     return 0;
@@ -294,6 +336,7 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
     int32_t begin = (cfg->forced_bos >= 0 && P == 1) ? 1 : 0;
     if (new_tokens == begin) ban_ids(x, V, cfg->begin_ids, cfg->n_begin);
   }
+  if (cfg->renormalize_logits) renormalize(x, V);
 
   if (!cfg->do_sample) {
     int32_t t = argmax_lowest(x, V);
@@ -305,6 +348,7 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
     res->greedy_margin = (x1 > -INFINITY) ? ((double)x1 - (double)x2) / den : 0.0;
     for (int32_t v = 0; v < V; ++v) res->n_finite += x[v] > -INFINITY;
     res->keep_min = res->keep_max = res->n_finite;
+    res->logprob = token_logprob(x, V, t);
     if (x_out) memcpy(x_out, x, sizeof(float) * (size_t)V);
     free(x); free(order); free(buf);
     return 0;
@@ -392,6 +436,7 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
     res->n_admissible = na;
   }
   free(pre);
+  res->logprob = token_logprob(x, V, t);
   if (x_out) memcpy(x_out, x, sizeof(float) * (size_t)V);
   free(x); free(order); free(buf);
   return 0;

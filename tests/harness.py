@@ -30,7 +30,7 @@ def torch_mod():
 
 
 def run_gpu_select(w: synth.SelectWorkload, want_processed: bool = False,
-                   stride_pad: int = 0) -> dict:
+                   stride_pad: int = 0, want_logprobs: bool = False) -> dict:
     from logits_processing_token_amd import tsel
     torch = torch_mod()
     d = upload_select(w, stride_pad)
@@ -39,9 +39,13 @@ def run_gpu_select(w: synth.SelectWorkload, want_processed: bool = False,
     proc = None
     if want_processed:
         proc = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda:0")
-    tsel.process_select(d["logits"], d["hist"], d["lens"], d["params"], d["u"], out, proc)
+    params = d["params"]
+    params.output_logprobs = int(want_logprobs)
+    r = tsel.process_select(d["logits"], d["hist"], d["lens"], params, d["u"], out, proc)
     torch.cuda.synchronize()
     res = {"token": out.cpu().numpy()}
+    if want_logprobs:
+        res["logprob"] = r[1].cpu().numpy()
     if want_processed:
         res["processed"] = proc.cpu().numpy()
     return res
@@ -60,7 +64,8 @@ def compare_select(w: synth.SelectWorkload, gpu: dict, ora: dict, rows=None,
     rows = list(range(w.batch)) if rows is None else list(rows)
     sampling = bool(w.settings.get("do_sample"))
     rep = dict(rows=len(rows), exact=0, low_margin=0, low_margin_mismatch=0,
-               high_margin_mismatch=[], not_admissible=[], processed_mismatch=[])
+               high_margin_mismatch=[], not_admissible=[], processed_mismatch=[],
+               logprob_mismatch=[])
     for i, b in enumerate(rows):
         g, o = int(gpu["token"][b]), int(ora["token"][i])
         low = sampling and ora["margin"][i] < MARGIN
@@ -77,6 +82,15 @@ def compare_select(w: synth.SelectWorkload, gpu: dict, ora: dict, rows=None,
                 rep["exact"] += 1
             else:
                 rep["high_margin_mismatch"].append((b, g, o))
+        if "logprob" in gpu and g == o and not logprobs_agree(gpu["logprob"][b], ora["logprob"][i]):
+            # a low-margin row may keep a different top_p set (see the kept
+            # sets below); its log-probability must then be the log-softmax
+            # of the GPU's own kept scores at the token
+            own = (low and check_processed
+                   and logprobs_agree(gpu["logprob"][b], logprob_of(gpu["processed"][b], g)))
+            if not own:
+                rep["logprob_mismatch"].append((b, float(gpu["logprob"][b]),
+                                                float(ora["logprob"][i])))
         if check_processed and g == o:
             gp, op = gpu["processed"][b], ora["processed"][i]
             if low:
@@ -86,6 +100,28 @@ def compare_select(w: synth.SelectWorkload, gpu: dict, ora: dict, rows=None,
             if not ok:
                 rep["processed_mismatch"].append(b)
     return rep
+
+
+def logprob_of(row: np.ndarray, t: int) -> np.float32:
+    """The log-softmax of a row of final scores at t, in binary64."""
+    x = row.astype(np.float64)
+    fin = np.isfinite(x)
+    if not fin.any():
+        return np.float32(np.nan)
+    m = x[fin].max()
+    return np.float32((x[t] - m) - np.log(np.sum(np.exp(x[fin] - m))))
+
+
+def logprobs_agree(g: float, o: float) -> bool:
+    """Both sides take the log-sum-exp in binary64 and round once: the same
+    binary32 value up to a rounding boundary the two sums straddle (2 ulp
+    allowed); NaN must meet NaN with the same bits."""
+    g, o = np.float32(g), np.float32(o)
+    if np.isnan(o) or np.isnan(g):
+        return bool(np.isnan(o) and np.isnan(g) and g.view(np.uint32) == o.view(np.uint32))
+    if np.isinf(o) or np.isinf(g):
+        return bool(g == o)
+    return bool(abs(float(g) - float(o)) <= 2 * float(np.spacing(np.abs(o))))
 
 
 def kept_sets_agree(gp: np.ndarray, op: np.ndarray, keep_min: int, keep_max: int) -> bool:

@@ -78,23 +78,43 @@ def test_sampling_needs_uniforms():
     assert tsel.validate(p, uniforms_given=True) == tsel.TSEL_OK
 
 
+def ws_fake():
+    return C.c_void_p(0x4000)
+
+
 def test_entry_points_reject_before_any_gpu_call():
     """Invalid or empty calls return from the host checks; no pointer is
     dereferenced (the fake addresses would fault) and nothing is launched."""
     lib = tsel.load()
     fake = C.c_void_p(0x1000)
     p = _params(batch=0)
-    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, None, 0,
-                                   None) == tsel.TSEL_OK
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, None, None,
+                                   0, None) == tsel.TSEL_OK
     p = _params()
-    assert lib.tsel_process_select(None, fake, fake, C.byref(p), None, fake, None, None, 0,
+    assert lib.tsel_process_select(None, fake, fake, C.byref(p), None, fake, None, None, None, 0,
                                    None) == tsel.TSEL_ERR_INVALID_ARG
     p = _params(do_sample=True)
-    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, None, 0,
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, None, None, 0,
                                    None) == tsel.TSEL_ERR_INVALID_ARG
     p = _params()
     assert lib.tsel_process_select(C.c_void_p(0x1004), fake, fake, C.byref(p), None, fake, None,
-                                   None, 0, None) == tsel.TSEL_ERR_UNSUPPORTED
+                                   None, None, 0, None) == tsel.TSEL_ERR_UNSUPPORTED
+    # log-probabilities: the flag and the output go together; the workspace
+    # holds the final scores (and the renormalized rows when asked for)
+    p = _params()
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, fake, None, 0,
+                                   None) == tsel.TSEL_ERR_INVALID_ARG
+    p = _params(output_logprobs=True)
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, None, None, 0,
+                                   None) == tsel.TSEL_ERR_INVALID_ARG
+    need = lib.tsel_process_select_workspace_size(C.byref(p))
+    assert need >= 4 * p.batch * p.vocab
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, fake, None, 0,
+                                   None) == tsel.TSEL_ERR_WORKSPACE
+    assert lib.tsel_process_select(fake, fake, fake, C.byref(p), None, fake, None, fake, ws_fake(),
+                                   need - 1, None) == tsel.TSEL_ERR_WORKSPACE
+    p2 = _params(output_logprobs=True, renormalize_logits=True)
+    assert lib.tsel_process_select_workspace_size(C.byref(p2)) >= 8 * p.batch * p.vocab
     assert lib.tsel_mask_build(0, fake, 1, fake, None) == tsel.TSEL_ERR_INVALID_ARG
     assert lib.tsel_mask_build(10, None, 3, fake, None) == tsel.TSEL_ERR_INVALID_ARG
     assert lib.tsel_mask_build(10, fake, -1, fake, None) == tsel.TSEL_ERR_INVALID_ARG

@@ -1,0 +1,77 @@
+"""GPU parity of the token log-probability and renormalize_logits against
+the oracle ("Transmuter.Generation (transmuter v2.0.0)": "Log-probabilities"
+and the module doc's processor order), through every selection kernel:
+greedy, the top_k candidate buffer, the streamed full path, and the two
+kernels that hold the row in registers; padding, forced and all-removed
+rows among them."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from logits_processing_token_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+sys.path.insert(0, os.path.dirname(__file__))
+from test_gpu_parity import _assert_select, _gpu  # noqa: E402,F401
+
+B = 10
+LENS = np.array([40, 0, 1, 40, 39, 40, 2, 40, 40, 40], np.int32)
+PROMPT = np.array([40, 0, 1, 38, 39, 1, 1, 40, 30, 40], np.int32)
+MAXL = np.full(B, 1 << 30, np.int32)
+MAXL[3] = 41  # forced eos
+SUPPRESS_ALL_BUT_NONE = None
+
+PATHS = [
+    # greedy
+    ("f32", 5000, dict()),
+    ("bf16", 50273, dict()),
+    # top_k candidate buffer
+    ("f32", 32000, dict(do_sample=True, top_k=50, top_p=0.9, temperature=0.7)),
+    ("bf16", 32000, dict(do_sample=True, top_k=3, temperature=1.3)),
+    # streamed full path (temperature != 1, no top_k)
+    ("f32", 70001, dict(do_sample=True, top_p=0.95, temperature=0.8)),
+    # rows in registers: bf16 (value bins) and fp32 (mass bins), T = 1
+    ("bf16", 128256, dict(do_sample=True, top_p=0.95)),
+    ("bf16", 4099, dict(do_sample=True, top_p=1.0)),
+    ("f32", 65536, dict(do_sample=True, top_p=0.9)),
+]
+COMMON = dict(repetition_penalty=1.2, suppress_tokens=[13, 21], forced_bos_token_id=9,
+              forced_eos_token_id=7, no_repeat_ngram_size=2)
+
+
+def _work(seed, dtype, V, s):
+    w = synth.random_select(seed, B, V, 64, dtype="f32", settings=dict(COMMON, **s),
+                            lens=LENS, prompt_lens=PROMPT, max_lengths=MAXL, sigma=2.0,
+                            id_range=min(V, 200), plant_n=1)
+    if dtype == "bf16":
+        w.logits = synth.bf16_bits(w.logits)
+    return w
+
+
+@pytest.mark.parametrize("dtype,V,s", PATHS)
+def test_logprobs_every_path(dtype, V, s):
+    _assert_select(_work(600 + V, dtype, V, s), logprobs=True)
+
+
+@pytest.mark.parametrize("dtype,V,s", PATHS)
+def test_renormalize_every_path(dtype, V, s):
+    """The renormalized scores (processed rows) bit for bit, the tokens, and
+    the log-probabilities over them."""
+    _assert_select(_work(700 + V, dtype, V, dict(s, renormalize_logits=True)), logprobs=True)
+
+
+def test_logprob_all_removed_row():
+    """Every id suppressed: token 0 and NaN, in greedy and sampling mode."""
+    for s in (dict(), dict(do_sample=True, top_p=0.8)):
+        w = synth.random_select(5, 3, 500, 16, settings=dict(s, suppress_tokens=list(range(500))))
+        _assert_select(w, logprobs=True)
+
+
+def test_logprobs_benchmark_batch():
+    """All 256 rows of the B=256, V=128256 bf16 batch with log-probabilities
+    (and the final scores, against which a row whose top_p set may differ
+    from the oracle's at its boundary is checked)."""
+    _assert_select(synth.c3_select(), processed=True, logprobs=True)

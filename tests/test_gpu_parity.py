@@ -31,15 +31,17 @@ def _say(*a):
 
 
 def _assert_select(w, rows=None, processed=True, max_low_mismatch_frac=0.0,
-                   stride_pad=0):
+                   stride_pad=0, logprobs=False):
     _say(f"case {w.name}: B={w.batch} V={w.vocab} {w.dtype} settings={w.settings}")
-    gpu = harness.run_gpu_select(w, want_processed=processed, stride_pad=stride_pad)
+    gpu = harness.run_gpu_select(w, want_processed=processed, stride_pad=stride_pad,
+                                 want_logprobs=logprobs)
     ora = harness.run_oracle_select(w, rows=rows, want_processed=processed)
     rep = harness.compare_select(w, gpu, ora, rows=rows, check_processed=processed)
     _say("  report:", {k: (v if not isinstance(v, list) else v[:5]) for k, v in rep.items()})
     assert rep["high_margin_mismatch"] == [], rep
     assert rep["not_admissible"] == [], rep
     assert rep["processed_mismatch"] == [], rep
+    assert rep["logprob_mismatch"] == [], rep
     if rep["low_margin"]:
         assert rep["low_margin_mismatch"] <= max_low_mismatch_frac * rep["low_margin"], rep
     return rep

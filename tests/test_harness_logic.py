@@ -46,3 +46,22 @@ def test_kept_sets_value_mismatch():
     o = _row([3.0, NI, 1.0, 2.0])
     g = _row([3.0, NI, 1.0000001, 2.0])
     assert not harness.kept_sets_agree(g, o, 3, 3)
+
+
+def test_logprobs_agree_rule():
+    one = np.float32(-1.25)
+    assert harness.logprobs_agree(one, one)
+    assert harness.logprobs_agree(np.nextafter(one, np.float32(0)), one)
+    assert not harness.logprobs_agree(np.float32(-1.2501), one)
+    qnan = np.array([0x7FC00000], np.uint32).view(np.float32)[0]
+    assert harness.logprobs_agree(qnan, qnan)
+    assert not harness.logprobs_agree(np.array([0xFFC00000], np.uint32).view(np.float32)[0], qnan)
+    assert not harness.logprobs_agree(np.float32(0.0), qnan)
+
+
+def test_logprob_of_row():
+    row = np.log(np.array([1.0, 2.0, 3.0, 4.0], np.float32)).astype(np.float32)
+    assert abs(float(harness.logprob_of(row, 3)) - np.log(0.4)) < 3e-7
+    row[0] = -np.inf  # kept set 2:3:4
+    assert abs(float(harness.logprob_of(row, 1)) - np.log(2 / 9)) < 3e-7
+    assert np.isnan(harness.logprob_of(np.full(3, -np.inf, np.float32), 0))
