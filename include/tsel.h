@@ -231,6 +231,48 @@ tsel_status tsel_verify_noalloc(const void *logits, int32_t dtype, int32_t batch
                                 int32_t *out_k, void *stream);
 
 /*
+ * tsel_verify_select -- verification of k assistant drafts per row with the
+ * token selection method of the step ("Assisted Generation: a new direction
+ * toward low-latency text generation", "Greedy decoding with assisted
+ * generation", step 3: ".argmax() for greedy search or .multinomial() for
+ * sampling"; "Sample with assisted generation").  Position j of row b was
+ * computed after the row's history and the drafts 0..j-1; its token is
+ * tsel_process_select's selection of that position row, whose history is
+ * the row's history followed by candidates[b][0..j-1] and whose length is
+ * lens[b] + j (prompt length and max_length unchanged; a padding row stays
+ * one), drawing with uniforms[b * (k+1) + j] when sampling.  The matches,
+ * kept tokens, next token and next draft count then follow as in
+ * tsel_verify: drafts are accepted left to right while they equal the
+ * selected token.
+ *
+ *  logits      device [B, k+1, params->logits_row_stride] of params->dtype
+ *              (16-byte aligned rows); params->batch is B.
+ *  history, lens  as tsel_process_select (history [B, params->hist_stride],
+ *              lens [3 * B]).
+ *  params      the selection settings (processors, warpers,
+ *              renormalize_logits); output_logprobs must be 0.
+ *  candidates  device int32 [B, k] (NULL when k == 0).
+ *  uniforms    device float [B * (k+1)], required iff sampling.
+ *  out_n_match, out_tokens [B, k+1], out_next, out_k  as tsel_verify.
+ *  workspace   device, 256-byte aligned, at least
+ *              tsel_verify_select_workspace_size(params, k) bytes: the
+ *              position rows' histories, lengths and tokens (and what the
+ *              selection itself needs).
+ * Errors: those of tsel_process_select for the settings; TSEL_ERR_INVALID_ARG
+ * for k < 0, output_logprobs set, or NULL required pointers;
+ * TSEL_ERR_WORKSPACE for a missing or small workspace; TSEL_ERR_UNSUPPORTED
+ * for k > 1023 or rows the selection's on-chip layout cannot hold.
+ */
+tsel_status tsel_verify_select(const void *logits, const int32_t *history, const int32_t *lens,
+                               const tsel_params *params, int32_t k, const int32_t *candidates,
+                               const float *uniforms, int32_t *out_n_match, int32_t *out_tokens,
+                               int32_t *out_next, int32_t *out_k, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Workspace bytes tsel_verify_select needs. */
+size_t tsel_verify_select_workspace_size(const tsel_params *params, int32_t k);
+
+/*
  * tsel_finish_step -- the end of one decode step for every row, on the
  * device, so that a decode loop needs no host read per step
  * ("Transmuter.Generation (transmuter v2.0.0)", function doc of generate/5:

@@ -365,6 +365,74 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 
+// tsel_verify_select: the position rows' histories, lengths and tokens,
+// then the selection's own workspace.
+static tsel_params vsel_params(const tsel_params *p, int32_t k) {
+  tsel_params q = *p;
+  q.batch = p->batch * (k + 1);
+  q.hist_stride = std::max(p->hist_stride, 0) + k;
+  return q;
+}
+static size_t vsel_rows_bytes(const tsel_params *p, int32_t k) {
+  const size_t R = (size_t)p->batch * (size_t)(k + 1);
+  const size_t H2 = (size_t)std::max(p->hist_stride, 0) + (size_t)k;
+  return align256(R * H2 * 4) + align256(R * 3 * 4) + align256(R * 4);
+}
+
+size_t tsel_verify_select_workspace_size(const tsel_params *params, int32_t k) {
+  if (!params || params->batch <= 0 || params->vocab < 1 || k < 0) return 0;
+  const tsel_params q = vsel_params(params, k);
+  return vsel_rows_bytes(params, k) + tsel_process_select_workspace_size(&q);
+}
+
+tsel_status tsel_verify_select(const void *logits, const int32_t *history, const int32_t *lens,
+                               const tsel_params *params, int32_t k, const int32_t *candidates,
+                               const float *uniforms, int32_t *out_n_match, int32_t *out_tokens,
+                               int32_t *out_next, int32_t *out_k, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (k < 0) return TSEL_ERR_INVALID_ARG;
+  tsel_status st = check_params(params, uniforms != nullptr);
+  if (st != TSEL_OK) return st;
+  if (params->output_logprobs) return TSEL_ERR_INVALID_ARG;
+  if (params->batch == 0) return TSEL_OK;
+  if (!logits || !lens || !out_n_match || !out_tokens || !out_next || !out_k)
+    return TSEL_ERR_INVALID_ARG;
+  if (k > 0 && !candidates) return TSEL_ERR_INVALID_ARG;
+  if (!history && params->hist_stride > 0) return TSEL_ERR_INVALID_ARG;
+  if (k > tsel::kMaxVerifyK) return TSEL_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
+  if ((int64_t)params->batch * (k + 1) > (int64_t)INT32_MAX / 4) return TSEL_ERR_UNSUPPORTED;
+  const size_t need = tsel_verify_select_workspace_size(params, k);
+  if (!workspace || workspace_bytes < need) return TSEL_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TSEL_ERR_UNSUPPORTED;
+  const tsel_params q = vsel_params(params, k);
+  {  // (the position rows must fit the selection too)
+    tsel::SelectArgs probe{};
+    size_t lds = 0;
+    if (!plan_layout(&q, params->do_sample ? SelectKernel::kFull : SelectKernel::kGreedy, &probe,
+                     &lds))
+      return TSEL_ERR_UNSUPPORTED;
+  }
+  const size_t R = (size_t)q.batch;
+  char *ws = static_cast<char *>(workspace);
+  int32_t *hist2 = reinterpret_cast<int32_t *>(ws);
+  ws += align256(R * (size_t)q.hist_stride * 4);
+  int32_t *lens2 = reinterpret_cast<int32_t *>(ws);
+  ws += align256(R * 3 * 4);
+  int32_t *sel = reinterpret_cast<int32_t *>(ws);
+  ws += align256(R * 4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = tsel::launch_vsel_expand(history, params->hist_stride, lens, params->batch, k,
+                                          candidates, hist2, q.hist_stride, lens2, s);
+  if (e != hipSuccess) return TSEL_ERR_LAUNCH;
+  st = tsel_process_select(logits, hist2, lens2, &q, uniforms, sel, nullptr, nullptr, ws,
+                           workspace_bytes - (size_t)(ws - static_cast<char *>(workspace)), stream);
+  if (st != TSEL_OK) return st;
+  e = tsel::launch_vsel_match(sel, params->batch, k, candidates, out_n_match, out_tokens, out_next,
+                              out_k, s);
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
 tsel_status tsel_mask_build(int32_t vocab, const int32_t *ids, int32_t n_ids, uint32_t *out_mask,
                             void *stream) {
   if (vocab < 1 || n_ids < 0 || !out_mask || (n_ids > 0 && !ids)) return TSEL_ERR_INVALID_ARG;

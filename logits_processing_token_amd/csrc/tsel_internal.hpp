@@ -108,6 +108,13 @@ hipError_t launch_renorm(const SelectArgs &a, size_t lds, float *dst, int64_t ds
 hipError_t launch_logprob(const float *proc, int64_t stride, int32_t B, int32_t V,
                           const int32_t *tokens, float *out, hipStream_t s);
 
+hipError_t launch_vsel_expand(const int32_t *hist, int32_t hist_stride, const int32_t *lens,
+                              int32_t B, int32_t k, const int32_t *cand, int32_t *hist2,
+                              int32_t hist2_stride, int32_t *lens2, hipStream_t s);
+hipError_t launch_vsel_match(const int32_t *sel, int32_t B, int32_t k, const int32_t *cand,
+                             int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,
+                             hipStream_t s);
+
 hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
                          int64_t row_bytes, int32_t chunks, const int32_t *cand,
                          int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,

@@ -29,6 +29,7 @@ EXPORTS = (
     "tsel_process_select", "tsel_process_select_workspace_size", "tsel_validate_params",
     "tsel_mask_build", "tsel_verify", "tsel_verify_workspace_size", "tsel_status_string",
     "tsel_selftest_exp2_monotone", "tsel_finish_step", "tsel_verify_noalloc",
+    "tsel_verify_select", "tsel_verify_select_workspace_size",
 )
 TSEL_NOALLOC_SCRATCH_BYTES = 1 << 20
 
@@ -82,6 +83,11 @@ def load() -> C.CDLL:
     lib.tsel_verify.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tsel_verify_noalloc.restype = i32
     lib.tsel_verify_noalloc.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]
+    lib.tsel_verify_select.restype = i32
+    lib.tsel_verify_select.argtypes = [vp, vp, vp, C.POINTER(Params), i32, vp, vp, vp, vp, vp,
+                                       vp, vp, sz, vp]
+    lib.tsel_verify_select_workspace_size.restype = sz
+    lib.tsel_verify_select_workspace_size.argtypes = [C.POINTER(Params), i32]
     lib.tsel_verify_workspace_size.restype = sz
     lib.tsel_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.tsel_status_string.restype = C.c_char_p
@@ -275,4 +281,32 @@ def verify_noalloc(logits, candidates, dtype: int, vocab: Optional[int] = None,
                                  _ptr(candidates) if k > 0 else None, _ptr(n_match),
                                  _ptr(tokens), _ptr(nxt), _ptr(k_next), _stream(stream))
     _check(st, "tsel_verify_noalloc")
+    return n_match, tokens, nxt, k_next
+
+
+def verify_select(logits, history, lens, params: Params, candidates, uniforms=None,
+                  workspace=None, outs: Optional[Sequence] = None, stream=None):
+    """Run tsel_verify_select on logits [B, k+1, stride] (params.batch = B,
+    params.logits_row_stride = stride); returns (n_match, tokens, next,
+    k_next)."""
+    import torch
+    lib = load()
+    B, K1 = logits.shape[0], logits.shape[1]
+    k = K1 - 1
+    dev = logits.device
+    if outs is None:
+        outs = (torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty((B, K1), dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+    n_match, tokens, nxt, k_next = outs
+    need = int(lib.tsel_verify_select_workspace_size(C.byref(params), k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.tsel_verify_select(_ptr(logits), _ptr(history), _ptr(lens), C.byref(params), k,
+                                _ptr(candidates) if k > 0 else None, _ptr(uniforms),
+                                _ptr(n_match), _ptr(tokens), _ptr(nxt), _ptr(k_next),
+                                _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                _stream(stream))
+    _check(st, "tsel_verify_select")
     return n_match, tokens, nxt, k_next

@@ -84,6 +84,11 @@ def bind(path: str):
     lib.oracle_verify_row.argtypes = [
         C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_void_p,
         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.oracle_verify_select_row.restype = C.c_int
+    lib.oracle_verify_select_row.argtypes = [
+        C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+        C.POINTER(_Cfg), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+        C.c_void_p]
     lib.oracle_finish_row.restype = C.c_int32
     lib.oracle_finish_row.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                       C.c_int32, C.c_void_p]
@@ -137,6 +142,28 @@ def _dtype_code(logits: np.ndarray) -> int:
     raise TypeError("logits must be float32 or uint16 (bf16 bits)")
 
 
+def _c_cfg(cfg: Config, V: int, dcode: int):
+    """The C struct of cfg (and the id arrays it points into, which must
+    outlive it)."""
+    keep = {k: _ids(getattr(cfg, k)) for k in (
+        "bad_words_ids", "eos_token_ids", "suppress_tokens", "begin_suppress_tokens")}
+    ccfg = _Cfg(
+        vocab=V, dtype=dcode, repetition_penalty=cfg.repetition_penalty,
+        no_repeat_ngram_size=cfg.no_repeat_ngram_size,
+        bad_ids=_ptr(keep["bad_words_ids"]), n_bad=keep["bad_words_ids"].size,
+        min_length=cfg.min_length, min_new_tokens=cfg.min_new_tokens,
+        eos_ids=_ptr(keep["eos_token_ids"]), n_eos=keep["eos_token_ids"].size,
+        forced_bos=cfg.forced_bos_token_id, forced_eos=cfg.forced_eos_token_id,
+        suppress_ids=_ptr(keep["suppress_tokens"]),
+        n_suppress=keep["suppress_tokens"].size,
+        begin_ids=_ptr(keep["begin_suppress_tokens"]),
+        n_begin=keep["begin_suppress_tokens"].size,
+        do_sample=int(bool(cfg.do_sample)), temperature=cfg.temperature,
+        top_k=cfg.top_k, top_p=cfg.top_p,
+        renormalize_logits=int(bool(cfg.renormalize_logits)))
+    return ccfg, keep
+
+
 def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
            prompt_lens: np.ndarray, max_lengths: np.ndarray, cfg: Config,
            uniforms: Optional[np.ndarray] = None, rows: Optional[Sequence[int]] = None,
@@ -157,22 +184,7 @@ def select(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
     B, V = logits.shape
     rows = list(range(B)) if rows is None else [int(r) for r in rows]
     dcode = _dtype_code(logits)
-    keep = {k: _ids(getattr(cfg, k)) for k in (
-        "bad_words_ids", "eos_token_ids", "suppress_tokens", "begin_suppress_tokens")}
-    ccfg = _Cfg(
-        vocab=V, dtype=dcode, repetition_penalty=cfg.repetition_penalty,
-        no_repeat_ngram_size=cfg.no_repeat_ngram_size,
-        bad_ids=_ptr(keep["bad_words_ids"]), n_bad=keep["bad_words_ids"].size,
-        min_length=cfg.min_length, min_new_tokens=cfg.min_new_tokens,
-        eos_ids=_ptr(keep["eos_token_ids"]), n_eos=keep["eos_token_ids"].size,
-        forced_bos=cfg.forced_bos_token_id, forced_eos=cfg.forced_eos_token_id,
-        suppress_ids=_ptr(keep["suppress_tokens"]),
-        n_suppress=keep["suppress_tokens"].size,
-        begin_ids=_ptr(keep["begin_suppress_tokens"]),
-        n_begin=keep["begin_suppress_tokens"].size,
-        do_sample=int(bool(cfg.do_sample)), temperature=cfg.temperature,
-        top_k=cfg.top_k, top_p=cfg.top_p,
-        renormalize_logits=int(bool(cfg.renormalize_logits)))
+    ccfg, keep = _c_cfg(cfg, V, dcode)
     if cfg.do_sample and uniforms is None:
         raise ValueError("sampling needs one uniform per row")
     u = (np.zeros(B, np.float32) if uniforms is None
@@ -284,3 +296,52 @@ def finish_step(tokens, lens, max_lengths, eos_ids, finished):
         out[b] = lib.oracle_finish_row(int(t[b]), int(L[b]), int(M[b]), e.ctypes.data, e.size,
                                        fin[b:].ctypes.data)
     return out, fin
+
+
+def verify_select(logits: np.ndarray, candidates: np.ndarray, history: np.ndarray,
+                  lens: np.ndarray, prompt_lens: np.ndarray, max_lengths: np.ndarray,
+                  cfg: Config, uniforms: Optional[np.ndarray] = None, threads: int = 1) -> dict:
+    """Verification of k drafts per row with the full selection at each
+    position (the processors over the history extended by the drafts before
+    it, and for sampling the warpers and a draw from uniforms[b, j]).
+
+    logits: [B, k+1, V] float32 or uint16 (bf16 bits); candidates: [B, k];
+    history: [B, H] (row b uses its first lens[b] ids); uniforms: [B, k+1]
+    when sampling.  Returns n_match [B], tokens [B, k+1], next [B], k_next [B].
+    """
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    candidates = np.ascontiguousarray(candidates, dtype=np.int32)
+    history = np.ascontiguousarray(history, dtype=np.int32)
+    B, K1, V = logits.shape
+    k = K1 - 1
+    dcode = _dtype_code(logits)
+    ccfg, keep = _c_cfg(cfg, V, dcode)
+    if cfg.do_sample and uniforms is None:
+        raise ValueError("sampling needs one uniform per position")
+    u = None if uniforms is None else np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, K1)
+    cand2 = candidates.reshape(B, max(k, 0)) if k > 0 else np.zeros((B, 1), np.int32)
+    n_match = np.empty(B, np.int32)
+    tokens = np.empty((B, K1), np.int32)
+    nxt = np.empty(B, np.int32)
+    k_next = np.empty(B, np.int32)
+    esize = logits.itemsize
+
+    def one(b):
+        rc = lib.oracle_verify_select_row(
+            logits.ctypes.data + b * K1 * V * esize, k, V, history[b].ctypes.data,
+            int(lens[b]), int(prompt_lens[b]), int(max_lengths[b]), C.byref(ccfg),
+            None if u is None else u[b].ctypes.data, cand2[b].ctypes.data,
+            n_match[b:].ctypes.data, tokens[b].ctypes.data, nxt[b:].ctypes.data,
+            k_next[b:].ctypes.data)
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+
+    if threads > 1 and B > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(B)))
+    else:
+        for b in range(B):
+            one(b)
+    _ = keep
+    return {"n_match": n_match, "tokens": tokens, "next": nxt, "k_next": k_next}

@@ -443,6 +443,21 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
 }
 
 /* ------------------------------------------------------------------ */
+/* [A] "Greedy decoding with assisted generation", steps 4-6: the selected
+ * tokens sel[0..k] against the k drafts. */
+static void match_drafts(int32_t k, const int32_t *cand, const int32_t *sel, int32_t *n_match,
+                         int32_t *tokens, int32_t *next, int32_t *k_next) {
+  /* step 4: left to right, stop at the first mismatch */
+  int32_t n = 0;
+  while (n < k && cand[n] == sel[n]) ++n;
+  /* step 5: keep the matches plus the first divergent token */
+  for (int32_t j = 0; j <= k; ++j) tokens[j] = j <= n ? sel[j] : -1;
+  *n_match = n;
+  *next = sel[n];
+  /* step 6: +2 when every candidate matched, else -1 (floor 1) */
+  *k_next = (n == k) ? k + 2 : (k - 1 > 1 ? k - 1 : 1);
+}
+
 /* [A] "Greedy decoding with assisted generation", steps 3-6, for one
  * batch row.  logits: (k+1) rows of V logits, row stride `stride` elements;
  * cand: the k draft ids.  Outputs: the match count, the kept tokens
@@ -460,17 +475,43 @@ void oracle_verify_row(const void *logits, int32_t dtype, int32_t k, int32_t V,
     for (int32_t v = 0; v < V; ++v) x[v] = load_logit(row, dtype, v);
     sel[j] = argmax_lowest(x, V); /* step 3: .argmax() per position */
   }
-  /* step 4: left to right, stop at the first mismatch */
-  int32_t n = 0;
-  while (n < k && cand[n] == sel[n]) ++n;
-  /* step 5: keep the matches plus the first divergent token */
-  for (int32_t j = 0; j <= k; ++j) tokens[j] = j <= n ? sel[j] : -1;
-  *n_match = n;
-  *next = sel[n];
-  /* step 6: +2 when every candidate matched, else -1 (floor 1) */
-  *k_next = (n == k) ? k + 2 : (k - 1 > 1 ? k - 1 : 1);
+  match_drafts(k, cand, sel, n_match, tokens, next, k_next);
   free(x);
   free(sel);
+}
+
+/* [A] steps 3-6 with the token selection method of the step (the
+ * processors, and for sampling the warpers and a draw: ".multinomial() for
+ * sampling"; "Sample with assisted generation").  Position j was computed
+ * by the model after the history h[0..L) and the drafts cand[0..j), so its
+ * selection sees that extended history and the length L + j (the length
+ * rules of [T] "Lengths" move with it); its draw takes the uniform u[j].  A
+ * padding row (L == 0) stays one at every position.  Returns 0, or -1 on
+ * allocation failure. */
+int oracle_verify_select_row(const void *logits, int32_t k, int64_t stride, const int32_t *h,
+                             int32_t L, int32_t P, int32_t M, const oracle_cfg *cfg,
+                             const float *u, const int32_t *cand, int32_t *n_match,
+                             int32_t *tokens, int32_t *next, int32_t *k_next) {
+  const size_t esize = cfg->dtype == 0 ? 4 : 2;
+  int32_t *hx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(L + k + 1));
+  int32_t *sel = (int32_t *)calloc((size_t)(k + 1), sizeof(int32_t));
+  if (!hx || !sel) { free(hx); free(sel); return -1; }
+  for (int32_t i = 0; i < L; ++i) hx[i] = h[i];
+  for (int32_t i = 0; i < k; ++i) hx[L + i] = cand[i];
+  for (int32_t j = 0; j <= k; ++j) {
+    const char *row = (const char *)logits + (size_t)j * (size_t)stride * esize;
+    oracle_row_result r;
+    if (oracle_select_row(row, hx, L == 0 ? 0 : L + j, P, M, cfg, u ? u[j] : 0.0f, NULL, &r) != 0) {
+      free(hx);
+      free(sel);
+      return -1;
+    }
+    sel[j] = r.token;
+  }
+  match_drafts(k, cand, sel, n_match, tokens, next, k_next);
+  free(hx);
+  free(sel);
+  return 0;
 }
 
 /* Bitmask of an id list (ids outside [0, V) are ignored): bit v of word
