@@ -1,7 +1,7 @@
 /*
  * tsel.h -- C ABI of libtsel.so: batched token selection over the logits of
- * one decode step, and greedy verification of assistant drafts, on AMD
- * Instinct MI355X (gfx950).
+ * one decode step, one step of beam search, and verification of assistant
+ * drafts, on AMD Instinct MI355X (gfx950).
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" point to GPU memory; everything else is host.
@@ -271,6 +271,58 @@ tsel_status tsel_verify_select(const void *logits, const int32_t *history, const
 
 /* Workspace bytes tsel_verify_select needs. */
 size_t tsel_verify_select_workspace_size(const tsel_params *params, int32_t k);
+
+/*
+ * tsel_beam_step -- one step of beam search ("Transmuter.Generation
+ * (transmuter v2.0.0)", the beam paragraph under "Log-probabilities").  The
+ * batch holds P prompts of num_beams rows each (row p * num_beams + j is
+ * beam j of prompt p).  Each beam row takes the log-softmax of its logits
+ * ((x - m) - ls in binary32, m the row's largest logit, ls =
+ * log(sum exp(x - m)) from binary64; -inf stays -inf), then the processors
+ * of tsel_process_select in their order with removed ids at -FLT_MAX (the
+ * smallest finite value) instead of -inf and a forced id at 0, then adds the
+ * beam's score; a candidate's score is raised to -FLT_MAX when below it.
+ * Candidate (beam j, id v) has the flattened index j * V + v.  Of each
+ * prompt's candidates the best K = tsel_beam_width(num_beams, n_eos) are
+ * kept, by score descending and, among equal scores, by flattened index
+ * ascending.  On the first step only beam 0 of a prompt gives candidates
+ * (its beams are all alike); a padding beam row (lens[r] == 0) gives none.
+ * Slots past a prompt's candidates hold score -inf, beam -1, id -1.
+ *
+ *  logits       device, params->batch = P * num_beams rows as in
+ *               tsel_process_select (16-byte aligned rows).
+ *  history, lens  as tsel_process_select, one row per beam.
+ *  params       the processors' settings; the warpers are not used
+ *               (do_sample must be 0), nor are renormalize_logits and
+ *               output_logprobs (both 0).
+ *  num_beams    beams per prompt, 1 .. 64; params->batch a multiple of it.
+ *  beam_scores  device float [P * num_beams]: each beam's running score
+ *               (-inf for a dead beam).
+ *  first_step   nonzero on the first step of the search.
+ *  out_scores   device float [P, K]; out_beams, out_tokens device int32
+ *               [P, K]: the kept candidates, best first.
+ *  workspace    device, 256-byte aligned, at least
+ *               tsel_beam_step_workspace_size(params, num_beams) bytes: each
+ *               beam row's best K candidates.
+ * Errors: those of tsel_process_select for the params; TSEL_ERR_INVALID_ARG
+ * for do_sample, renormalize_logits or output_logprobs set, num_beams < 1,
+ * a batch that is not a multiple of num_beams, or NULL required pointers;
+ * TSEL_ERR_WORKSPACE for a missing or small workspace; TSEL_ERR_UNSUPPORTED
+ * for num_beams > 64, num_beams * V >= 2^32, or V beyond the on-chip masks
+ * of this path (V > 409,600).
+ */
+tsel_status tsel_beam_step(const void *logits, const int32_t *history, const int32_t *lens,
+                           const tsel_params *params, int32_t num_beams,
+                           const float *beam_scores, int32_t first_step, float *out_scores,
+                           int32_t *out_beams, int32_t *out_tokens, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* K, the candidates a prompt keeps per beam step: max(2, 1 + n_eos) *
+ * num_beams (0 for num_beams < 1 or n_eos < 0). */
+int32_t tsel_beam_width(int32_t num_beams, int32_t n_eos);
+
+/* Workspace bytes tsel_beam_step needs. */
+size_t tsel_beam_step_workspace_size(const tsel_params *params, int32_t num_beams);
 
 /*
  * tsel_finish_step -- the end of one decode step for every row, on the

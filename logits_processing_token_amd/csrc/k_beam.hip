@@ -1,0 +1,295 @@
+// k_beam.hip -- one step of beam search over the logits of num_beams rows
+// per prompt ("Transmuter.Generation (transmuter v2.0.0)", the beam
+// paragraph under "Log-probabilities"): each beam row takes the log-softmax
+// of its logits, the processors act on that with removed ids at the
+// smallest finite value, and the beam's score is added, a score never going
+// below the smallest finite value; of a prompt's num_beams * V candidates
+// the best K = max(2, 1 + eos ids) * num_beams are kept.  On the first step
+// only beam 0 of a prompt counts; a padding beam row (length 0) gives none.
+//
+// A candidate (beam j, id v) of a prompt has the flattened index
+// e = j * V + v and the 64-bit key (ordered score << 32) | (2^32 - 1 - e):
+// keys are unique and order candidates as the step does (score descending,
+// then e ascending), so the best K are the K largest keys.  No key is 0, which
+// marks "no candidate".
+//
+//  * k_beam_rows, one workgroup per beam row: the row's largest logit m and
+//    log(sum exp(x - m)) in binary64 (a running pair per lane, joined at the
+//    row's maximum); the seen and removed ids as two bitmasks in LDS; then the
+//    row's best K keys, scores recomputed from the logits on every pass (the
+//    row stays in L2 and nothing of size V is written).
+//  * k_beam_merge, one workgroup per prompt: the best K of its num_beams * K
+//    row keys, written as score, beam and id.
+//
+// Both select with the same routine: a radix select over the keys, 12 bits
+// then 13 at a time from the top, stopping as soon as the keys at or above
+// the current prefix number at most kSelCap; those are gathered into LDS and
+// each one's rank is the count of larger keys among them.
+
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <stdint.h>
+
+#include "tsel_device.hpp"
+#include "tsel_internal.hpp"
+
+namespace tsel {
+namespace {
+
+constexpr int kBT = kBeamThreads;
+
+struct SelShared {
+  int wsum[kBT / kWave];
+  int total, digit, above, cnt, nc;
+};
+
+__device__ __forceinline__ uint32_t ordered32(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ bool has_bit(const uint32_t *m, int v) {
+  return (m[v >> 5] >> (v & 31)) & 1u;
+}
+
+// The largest min(K, present keys) of key(0..n) (0 = absent), each passed to
+// emit(rank, key), rank 0 the largest; returns how many.  Every thread of
+// the workgroup calls.  hist: kBeamSelBins words; cand: kSelCap keys.
+template <class KeyFn, class EmitFn>
+__device__ int select_top(int64_t n, int K, KeyFn key, EmitFn emit, uint32_t *hist,
+                          uint64_t *cand, SelShared &ss) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0ull, pmask = 0ull;
+  int need = 0, above = 0, keff = 0;
+  for (int pass = 0; pass < 5; ++pass) {
+    const int width = pass == 0 ? 12 : 13;
+    const int shift = 52 - 13 * pass;
+    const int nbins = 1 << width;
+    for (int d = tid; d < nbins; d += kBT) hist[d] = 0u;
+    __syncthreads();
+    for (int64_t e = tid; e < n; e += kBT) {
+      const uint64_t k = key(e);
+      if (k != 0ull && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (nbins - 1)], 1u);
+    }
+    __syncthreads();
+    // thread t holds bins top, top-1, ..., the t-th group from the top
+    const int per = nbins / kBT;
+    const int top = nbins - 1 - tid * per;
+    int s = 0;
+    for (int i = 0; i < per; ++i) s += (int)hist[top - i];
+    int total = 0;
+    const int excl = block_excl_scan_i32<kBT>(s, ss.wsum, &total);
+    if (pass == 0) {
+      keff = total < K ? total : K;
+      if (keff == 0) return 0;
+      need = keff;
+    }
+    if (excl < need && need <= excl + s) {  // (exactly one thread)
+      int acc = excl;
+      for (int i = 0; i < per; ++i) {
+        const int c = (int)hist[top - i];
+        if (acc + c >= need) {
+          ss.digit = top - i;
+          ss.above = acc;
+          ss.cnt = c;
+          break;
+        }
+        acc += c;
+      }
+    }
+    if (tid == 0) ss.nc = 0;
+    __syncthreads();
+    above += ss.above;
+    need -= ss.above;
+    prefix |= (uint64_t)ss.digit << shift;
+    pmask |= (uint64_t)(nbins - 1) << shift;
+    const int cnt = ss.cnt;
+    __syncthreads();  // (ss is written again on the next pass)
+    if (above + cnt <= kSelCap) break;  // (after the last pass: above + cnt = keff)
+  }
+  // the keys at or above the prefix: `above` with a larger prefix, then the
+  // ones sharing it, the keff-th largest among them
+  for (int64_t e = tid; e < n; e += kBT) {
+    const uint64_t k = key(e);
+    if (k != 0ull && (k & pmask) >= prefix) {
+      const int slot = atomicAdd(&ss.nc, 1);
+      if (slot < kSelCap) cand[slot] = k;
+    }
+  }
+  __syncthreads();
+  const int nc = ss.nc < kSelCap ? ss.nc : kSelCap;
+  for (int j = tid; j < nc; j += kBT) {
+    const uint64_t kj = cand[j];
+    int r = 0;
+    for (int q = 0; q < nc; ++q) r += cand[q] > kj;
+    if (r < keff) emit(r, kj);
+  }
+  return keff;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
+  extern __shared__ __align__(16) uint32_t bsm[];
+  __shared__ float rmax[kBT / kWave];
+  __shared__ double rsum[kBT / kWave];
+  __shared__ SelShared ss;
+  const SelectArgs &s = a.s;
+  const int r = blockIdx.x, tid = threadIdx.x, V = s.V, K = a.width;
+  const int beam = r % a.nb;
+  uint64_t *keys_out = a.row_keys + (int64_t)r * K;
+  const int L = s.lens[r], P = s.lens[s.B + r], M = s.lens[2 * s.B + r];
+  if ((a.first_step && beam > 0) || L <= 0) {  // no candidates
+    for (int i = tid; i < K; i += kBT) keys_out[i] = 0ull;
+    return;
+  }
+  const char *rowp = s.logits + (int64_t)r * s.row_bytes;
+  const bool bf16 = s.dtype == 1;
+  auto load = [&](int v) -> float {
+    return bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
+                : reinterpret_cast<const float *>(rowp)[v];
+  };
+  const int mw = (V + 31) / 32;
+  uint32_t *seen = bsm, *kill = bsm + mw;
+  uint32_t *hist = bsm + ((2 * mw + 3) & ~3);
+  uint64_t *cand = reinterpret_cast<uint64_t *>(hist + kBeamSelBins);
+  for (int w = tid; w < 2 * mw; w += kBT) bsm[w] = 0u;
+  // the log-softmax's shift and sum, in binary64
+  double m = -INFINITY, sum = 0.0;
+  for (int v = tid; v < V; v += kBT) {
+    const double x = (double)load(v);
+    if (!(x > -INFINITY)) continue;
+    if (x > m) {
+      sum = sum * exp(m - x) + 1.0;
+      m = x;
+    } else {
+      sum += exp(x - m);
+    }
+  }
+  const float Mx = block_max_f32<kBT>((float)m, rmax);
+  const double S = block_sum_f64<kBT>(m > -INFINITY ? sum * exp(m - (double)Mx) : 0.0, rsum);
+  // (the reductions' barriers order the clearing of the masks)
+  const int new_tokens = L - P;
+  const bool begin_active =
+      s.begin_mask != nullptr && new_tokens == ((s.forced_bos >= 0 && P == 1) ? 1 : 0);
+  int forced = -1;
+  if (s.forced_bos >= 0 && L == 1) forced = s.forced_bos;
+  if (s.forced_eos >= 0 && L == M - 1) forced = s.forced_eos;
+  const int32_t *h = s.hist + (int64_t)r * s.hist_stride;
+  const int Lh = L < s.hist_stride ? L : s.hist_stride;  // (ids past the stride are not the row's)
+  if (forced < 0) {
+    for (int i = tid; i < Lh; i += kBT) {
+      const int v = h[i];
+      if (v >= 0 && v < V) atomicOr(&seen[v >> 5], 1u << (v & 31));
+    }
+    const int n = s.ngram;
+    if (n > 0 && Lh >= n) {  // window i bans its last id when its head is the history's tail
+      const int32_t *tl = h + (Lh - n + 1);
+      for (int i = tid; i + n <= Lh; i += kBT) {
+        bool match = true;
+        for (int j = 0; j < n - 1; ++j)
+          if (h[i + j] != tl[j]) { match = false; break; }
+        const int t = h[i + n - 1];
+        if (match && t >= 0 && t < V) atomicOr(&kill[t >> 5], 1u << (t & 31));
+      }
+    }
+    const bool minlen_active =
+        s.min_new > 0 ? (new_tokens < s.min_new) : (s.min_length > 0 && L < s.min_length);
+    if (minlen_active && tid < s.n_eos) {
+      const int e = s.eos[tid];
+      if (e >= 0 && e < V) atomicOr(&kill[e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+  bool forced_alive = forced >= 0 && forced < V;
+  if (forced_alive && s.sup_mask && has_bit(s.sup_mask, forced)) forced_alive = false;
+  if (forced_alive && begin_active && has_bit(s.begin_mask, forced)) forced_alive = false;
+  for (int w = tid; w < mw; w += kBT) {
+    uint32_t k = kill[w];
+    if (s.bad_mask) k |= s.bad_mask[w];
+    if (s.sup_mask) k |= s.sup_mask[w];
+    if (begin_active) k |= s.begin_mask[w];
+    kill[w] = k;
+  }
+  __syncthreads();
+  const bool any = Mx > -INFINITY;
+  const float lsf = any ? (float)log(S) : 0.0f;
+  const float s_beam = a.beam_scores[r];
+  const uint32_t flat0 = (uint32_t)beam * (uint32_t)V;
+  auto key = [&](int64_t e) -> uint64_t {
+    const int v = (int)e;
+    float y;
+    if (forced >= 0) {
+      y = (forced_alive && v == forced) ? 0.0f : -FLT_MAX;
+    } else {
+      const float x = load(v);
+      y = (any && x > -INFINITY) ? (x - Mx) - lsf : x;
+      if (has_bit(kill, v)) {
+        y = -FLT_MAX;
+      } else if (s.rep != 1.0f && has_bit(seen, v)) {
+        y = penalize(y, s.rep);
+      }
+    }
+    float c = y + s_beam;
+    if (!(c >= -FLT_MAX)) c = -FLT_MAX;  // never below the smallest finite value
+    if (c == 0.0f) c = 0.0f;             // (-0 and +0 are one score)
+    return ((uint64_t)ordered32(c) << 32) | (uint64_t)(0xFFFFFFFFu - (flat0 + (uint32_t)v));
+  };
+  const int keff = select_top(
+      (int64_t)V, K, key, [&](int rank, uint64_t k) { keys_out[rank] = k; }, hist, cand, ss);
+  for (int i = keff + tid; i < K; i += kBT) keys_out[i] = 0ull;
+}
+
+__global__ __launch_bounds__(kBT, 1) void k_beam_merge(BeamArgs a) {
+  extern __shared__ __align__(16) uint32_t bsm[];
+  __shared__ SelShared ss;
+  const int p = blockIdx.x, tid = threadIdx.x, V = a.s.V, K = a.width;
+  const uint64_t *keys = a.row_keys + (int64_t)p * a.nb * K;
+  uint32_t *hist = bsm;
+  uint64_t *cand = reinterpret_cast<uint64_t *>(hist + kBeamSelBins);
+  float *sc = a.out_scores + (int64_t)p * K;
+  int32_t *bm = a.out_beams + (int64_t)p * K, *tk = a.out_tokens + (int64_t)p * K;
+  const int keff = select_top(
+      (int64_t)a.nb * K, K, [&](int64_t e) { return keys[e]; },
+      [&](int rank, uint64_t k) {
+        const uint32_t e = 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu);
+        sc[rank] = unordered32((uint32_t)(k >> 32));
+        bm[rank] = (int32_t)(e / (uint32_t)V);
+        tk[rank] = (int32_t)(e % (uint32_t)V);
+      },
+      hist, cand, ss);
+  for (int i = keff + tid; i < K; i += kBT) {  // fewer candidates than slots
+    sc[i] = -INFINITY;
+    bm[i] = -1;
+    tk[i] = -1;
+  }
+}
+
+size_t beam_rows_lds(int32_t V) {
+  const size_t mw = ((size_t)V + 31) / 32;
+  return (((2 * mw + 3) & ~size_t(3)) + kBeamSelBins) * 4 + (size_t)kSelCap * 8;
+}
+
+hipError_t launch_beam(const BeamArgs &a, hipStream_t st) {
+  if (a.s.B <= 0) return hipSuccess;
+  const size_t lds = beam_rows_lds(a.s.V);
+  const size_t mlds = (size_t)kBeamSelBins * 4 + (size_t)kSelCap * 8;
+  static std::atomic<uint64_t> rows_set{0}, merge_set{0};  // devices where the limit is raised
+  if (hipError_t e = ensure_dyn_lds(reinterpret_cast<const void *>(&k_beam_rows),
+                                    (int)kSelectMaxDynLds, rows_set);
+      e != hipSuccess)
+    return e;
+  if (hipError_t e = ensure_dyn_lds(reinterpret_cast<const void *>(&k_beam_merge),
+                                    (int)kSelectMaxDynLds, merge_set);
+      e != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(k_beam_rows, dim3(a.s.B), dim3(kBT), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_beam_merge, dim3(a.s.B / a.nb), dim3(kBT), mlds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace tsel

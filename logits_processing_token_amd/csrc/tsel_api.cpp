@@ -210,13 +210,10 @@ size_t tsel_process_select_workspace_size(const tsel_params *params) {
   return n;
 }
 
-// The kernels for one selection over `logits` with the settings of p (the
-// arguments already checked); hipErrorNotSupported when V does not fit the
-// on-chip layout.
-static hipError_t dispatch_select(const tsel_params *params, const void *logits,
-                                  const int32_t *history, const int32_t *lens,
-                                  const float *uniforms, int32_t *out_tokens, float *out_processed,
-                                  hipStream_t s) {
+// The rows and the processors' settings of p as kernel arguments (the
+// warpers off).
+static tsel::SelectArgs proc_args(const tsel_params *params, const void *logits,
+                                  const int32_t *history, const int32_t *lens) {
   tsel::SelectArgs a{};
   const int64_t esize = params->dtype == TSEL_BF16 ? 2 : 4;
   a.logits = static_cast<const char *>(logits);
@@ -227,9 +224,6 @@ static hipError_t dispatch_select(const tsel_params *params, const void *logits,
   a.hist = history;
   a.hist_stride = params->hist_stride;
   a.lens = lens;
-  a.uniforms = uniforms;
-  a.out_tokens = out_tokens;
-  a.out_processed = out_processed;
   a.bad_mask = params->bad_words_mask;
   a.sup_mask = params->suppress_mask;
   a.begin_mask = params->begin_suppress_mask;
@@ -241,6 +235,22 @@ static hipError_t dispatch_select(const tsel_params *params, const void *logits,
   for (int i = 0; i < TSEL_MAX_EOS; ++i) a.eos[i] = i < params->n_eos ? params->eos_ids[i] : -1;
   a.forced_bos = params->forced_bos_token_id;
   a.forced_eos = params->forced_eos_token_id;
+  a.temperature = 1.0f;
+  a.top_p = 1.0f;
+  return a;
+}
+
+// The kernels for one selection over `logits` with the settings of p (the
+// arguments already checked); hipErrorNotSupported when V does not fit the
+// on-chip layout.
+static hipError_t dispatch_select(const tsel_params *params, const void *logits,
+                                  const int32_t *history, const int32_t *lens,
+                                  const float *uniforms, int32_t *out_tokens, float *out_processed,
+                                  hipStream_t s) {
+  tsel::SelectArgs a = proc_args(params, logits, history, lens);
+  a.uniforms = uniforms;
+  a.out_tokens = out_tokens;
+  a.out_processed = out_processed;
   a.do_sample = params->do_sample ? 1 : 0;
   a.temperature = params->temperature;
   a.top_k = params->top_k;
@@ -315,32 +325,9 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
     // the processors and the log-softmax into fp32 rows; the selection then
     // reads those with every processor switched off (the lengths still mark
     // padding rows)
-    tsel::SelectArgs ra{};
+    tsel::SelectArgs ra = proc_args(params, logits, history, lens);
     size_t lds = 0;
     if (!plan_layout(params, SelectKernel::kGreedy, &ra, &lds)) return TSEL_ERR_UNSUPPORTED;
-    const int64_t esize = params->dtype == TSEL_BF16 ? 2 : 4;
-    ra.logits = static_cast<const char *>(logits);
-    ra.row_bytes = params->logits_row_stride * esize;
-    ra.V = params->vocab;
-    ra.B = params->batch;
-    ra.dtype = params->dtype;
-    ra.hist = history;
-    ra.hist_stride = params->hist_stride;
-    ra.lens = lens;
-    ra.bad_mask = params->bad_words_mask;
-    ra.sup_mask = params->suppress_mask;
-    ra.begin_mask = params->begin_suppress_mask;
-    ra.rep = params->repetition_penalty;
-    ra.ngram = params->no_repeat_ngram_size;
-    ra.min_length = params->min_length;
-    ra.min_new = params->min_new_tokens;
-    ra.n_eos = params->n_eos;
-    for (int i = 0; i < TSEL_MAX_EOS; ++i)
-      ra.eos[i] = i < params->n_eos ? params->eos_ids[i] : -1;
-    ra.forced_bos = params->forced_bos_token_id;
-    ra.forced_eos = params->forced_eos_token_id;
-    ra.temperature = 1.0f;
-    ra.top_p = 1.0f;
     e = tsel::launch_renorm(ra, lds, reinterpret_cast<float *>(ws), (int64_t)renorm_stride(params), s);
     if (e != hipSuccess) return TSEL_ERR_LAUNCH;
     src = ws;
@@ -430,6 +417,54 @@ tsel_status tsel_verify_select(const void *logits, const int32_t *history, const
   if (st != TSEL_OK) return st;
   e = tsel::launch_vsel_match(sel, params->batch, k, candidates, out_n_match, out_tokens, out_next,
                               out_k, s);
+  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
+}
+
+int32_t tsel_beam_width(int32_t num_beams, int32_t n_eos) {
+  if (num_beams < 1 || n_eos < 0) return 0;
+  const int64_t k = (int64_t)std::max<int64_t>(2, 1 + (int64_t)n_eos) * num_beams;
+  return k > INT32_MAX ? 0 : (int32_t)k;
+}
+
+size_t tsel_beam_step_workspace_size(const tsel_params *params, int32_t num_beams) {
+  if (!params || params->batch <= 0 || num_beams < 1) return 0;
+  const int32_t K = tsel_beam_width(num_beams, std::max(params->n_eos, 0));
+  return align256((size_t)params->batch * (size_t)K * 8);
+}
+
+tsel_status tsel_beam_step(const void *logits, const int32_t *history, const int32_t *lens,
+                           const tsel_params *params, int32_t num_beams,
+                           const float *beam_scores, int32_t first_step, float *out_scores,
+                           int32_t *out_beams, int32_t *out_tokens, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  tsel_status st = check_params(params, false);
+  if (st != TSEL_OK) return st;
+  if (params->do_sample || params->renormalize_logits || params->output_logprobs)
+    return TSEL_ERR_INVALID_ARG;
+  if (num_beams < 1 || params->batch % num_beams != 0) return TSEL_ERR_INVALID_ARG;
+  if (num_beams > tsel::kMaxBeams) return TSEL_ERR_UNSUPPORTED;
+  if ((int64_t)num_beams * params->vocab > (int64_t)UINT32_MAX) return TSEL_ERR_UNSUPPORTED;
+  if (tsel::beam_rows_lds(params->vocab) > (size_t)tsel::kSelectMaxDynLds)
+    return TSEL_ERR_UNSUPPORTED;
+  if (params->batch == 0) return TSEL_OK;
+  if (!logits || !lens || !beam_scores || !out_scores || !out_beams || !out_tokens)
+    return TSEL_ERR_INVALID_ARG;
+  if (!history && params->hist_stride > 0) return TSEL_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
+  const size_t need = tsel_beam_step_workspace_size(params, num_beams);
+  if (!workspace || workspace_bytes < need) return TSEL_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TSEL_ERR_UNSUPPORTED;
+  tsel::BeamArgs a{};
+  a.s = proc_args(params, logits, history, lens);
+  a.nb = num_beams;
+  a.width = tsel_beam_width(num_beams, params->n_eos);
+  a.first_step = first_step ? 1 : 0;
+  a.beam_scores = beam_scores;
+  a.row_keys = static_cast<uint64_t *>(workspace);
+  a.out_scores = out_scores;
+  a.out_beams = out_beams;
+  a.out_tokens = out_tokens;
+  hipError_t e = tsel::launch_beam(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 

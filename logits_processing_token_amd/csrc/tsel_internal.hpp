@@ -94,6 +94,25 @@ struct SelectArgs {
   uint32_t off_sh;          // value-bin path: its shared scalars (no static LDS)
 };
 
+// One beam-search step: SelectArgs carries the processors' settings, B the
+// beam rows (prompts * nb).
+constexpr int kBeamThreads = 1024;
+constexpr int kBeamSelBins = 8192;  // radix-select histogram (13-bit digits)
+constexpr int kSelCap = 2048;       // keys ranked on chip at once
+constexpr int kMaxBeams = 64;
+struct BeamArgs {
+  SelectArgs s;
+  int32_t nb;                 // beams per prompt
+  int32_t width;              // K, the candidates kept per prompt
+  int32_t first_step;
+  const float *beam_scores;   // [B]
+  uint64_t *row_keys;         // workspace [B, K]: each row's best keys
+  float *out_scores;          // [B / nb, K]
+  int32_t *out_beams, *out_tokens;
+};
+size_t beam_rows_lds(int32_t V);
+hipError_t launch_beam(const BeamArgs &a, hipStream_t s);
+
 hipError_t launch_greedy(const SelectArgs &a, size_t lds, hipStream_t s);
 hipError_t launch_topk(const SelectArgs &a, size_t lds, hipStream_t s);
 // pending != 0: only rows whose token an earlier kernel left as pending

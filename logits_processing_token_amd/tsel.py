@@ -29,7 +29,8 @@ EXPORTS = (
     "tsel_process_select", "tsel_process_select_workspace_size", "tsel_validate_params",
     "tsel_mask_build", "tsel_verify", "tsel_verify_workspace_size", "tsel_status_string",
     "tsel_selftest_exp2_monotone", "tsel_finish_step", "tsel_verify_noalloc",
-    "tsel_verify_select", "tsel_verify_select_workspace_size",
+    "tsel_verify_select", "tsel_verify_select_workspace_size", "tsel_beam_step",
+    "tsel_beam_width", "tsel_beam_step_workspace_size",
 )
 TSEL_NOALLOC_SCRATCH_BYTES = 1 << 20
 
@@ -88,6 +89,13 @@ def load() -> C.CDLL:
                                        vp, vp, sz, vp]
     lib.tsel_verify_select_workspace_size.restype = sz
     lib.tsel_verify_select_workspace_size.argtypes = [C.POINTER(Params), i32]
+    lib.tsel_beam_step.restype = i32
+    lib.tsel_beam_step.argtypes = [vp, vp, vp, C.POINTER(Params), i32, vp, i32, vp, vp, vp, vp,
+                                   sz, vp]
+    lib.tsel_beam_width.restype = i32
+    lib.tsel_beam_width.argtypes = [i32, i32]
+    lib.tsel_beam_step_workspace_size.restype = sz
+    lib.tsel_beam_step_workspace_size.argtypes = [C.POINTER(Params), i32]
     lib.tsel_verify_workspace_size.restype = sz
     lib.tsel_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.tsel_status_string.restype = C.c_char_p
@@ -310,3 +318,34 @@ def verify_select(logits, history, lens, params: Params, candidates, uniforms=No
                                 _stream(stream))
     _check(st, "tsel_verify_select")
     return n_match, tokens, nxt, k_next
+
+
+def beam_width(num_beams: int, n_eos: int) -> int:
+    """tsel_beam_width: the candidates a prompt keeps per beam step."""
+    return int(load().tsel_beam_width(int(num_beams), int(n_eos)))
+
+
+def beam_step(logits, history, lens, params: Params, num_beams: int, beam_scores,
+              first_step: bool = False, workspace=None, outs: Optional[Sequence] = None,
+              stream=None):
+    """Run tsel_beam_step over params.batch = prompts * num_beams beam rows;
+    returns (scores [P, K] fp32, beams [P, K] int32, tokens [P, K] int32)."""
+    import torch
+    lib = load()
+    dev = logits.device
+    P = params.batch // max(int(num_beams), 1)
+    K = beam_width(num_beams, params.n_eos)
+    if outs is None:
+        outs = (torch.empty((P, K), dtype=torch.float32, device=dev),
+                torch.empty((P, K), dtype=torch.int32, device=dev),
+                torch.empty((P, K), dtype=torch.int32, device=dev))
+    scores, beams, tokens = outs
+    need = int(lib.tsel_beam_step_workspace_size(C.byref(params), int(num_beams)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.tsel_beam_step(_ptr(logits), _ptr(history), _ptr(lens), C.byref(params),
+                            int(num_beams), _ptr(beam_scores), 1 if first_step else 0,
+                            _ptr(scores), _ptr(beams), _ptr(tokens), _ptr(workspace),
+                            int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(st, "tsel_beam_step")
+    return scores, beams, tokens

@@ -89,6 +89,11 @@ def bind(path: str):
         C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
         C.POINTER(_Cfg), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
         C.c_void_p]
+    lib.oracle_beam_step.restype = C.c_int
+    lib.oracle_beam_step.argtypes = [
+        C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+        C.c_void_p, C.POINTER(_Cfg), C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+        C.c_void_p]
     lib.oracle_finish_row.restype = C.c_int32
     lib.oracle_finish_row.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                       C.c_int32, C.c_void_p]
@@ -345,3 +350,58 @@ def verify_select(logits: np.ndarray, candidates: np.ndarray, history: np.ndarra
             one(b)
     _ = keep
     return {"n_match": n_match, "tokens": tokens, "next": nxt, "k_next": k_next}
+
+
+def beam_width(num_beams: int, n_eos: int) -> int:
+    """Candidates kept per prompt and step: max(2, 1 + eos ids) * num_beams."""
+    return max(2, 1 + n_eos) * num_beams
+
+
+def beam_step(logits: np.ndarray, history: np.ndarray, lens: np.ndarray,
+              prompt_lens: np.ndarray, max_lengths: np.ndarray, cfg: Config, num_beams: int,
+              beam_scores: np.ndarray, first_step: bool = False, threads: int = 1,
+              width: Optional[int] = None) -> dict:
+    """One beam-search step for B = rows / num_beams prompts (prompt i owns
+    rows i * num_beams .. i * num_beams + num_beams - 1).
+
+    logits: [rows, V] float32 or uint16 (bf16 bits); history: [rows, H];
+    lens, prompt_lens, max_lengths, beam_scores: [rows].  Returns scores
+    [B, K] float32, beams [B, K] int32 (the beam within its prompt) and
+    tokens [B, K] int32, K = max(2, 1 + eos ids) * num_beams (or `width`,
+    to see the candidates just past the kept ones)."""
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    history = np.ascontiguousarray(history, dtype=np.int32)
+    rows, V = logits.shape
+    nb = int(num_beams)
+    B = rows // nb
+    K = beam_width(nb, len(list(cfg.eos_token_ids))) if width is None else int(width)
+    ccfg, keep = _c_cfg(cfg, V, _dtype_code(logits))
+    L = np.ascontiguousarray(lens, dtype=np.int32)
+    P = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    M = np.ascontiguousarray(max_lengths, dtype=np.int32)
+    bs = np.ascontiguousarray(beam_scores, dtype=np.float32)
+    scores = np.empty((B, K), np.float32)
+    beams = np.empty((B, K), np.int32)
+    tokens = np.empty((B, K), np.int32)
+    esize = logits.itemsize
+    H = history.shape[1]
+
+    def one(i):
+        r0 = i * nb
+        rc = lib.oracle_beam_step(
+            logits.ctypes.data + r0 * V * esize, V, nb, history.ctypes.data + r0 * H * 4, H,
+            L[r0:].ctypes.data, P[r0:].ctypes.data, M[r0:].ctypes.data, C.byref(ccfg),
+            bs[r0:].ctypes.data, int(bool(first_step)), K, scores[i].ctypes.data,
+            beams[i].ctypes.data, tokens[i].ctypes.data)
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+
+    if threads > 1 and B > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(B)))
+    else:
+        for i in range(B):
+            one(i)
+    _ = keep
+    return {"scores": scores, "beams": beams, "tokens": tokens}

@@ -31,6 +31,7 @@
  * order; greedy ties go to the lowest index; an all-removed row selects id 0;
  * the next draft count is floored at 1.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -108,25 +109,27 @@ static void repetition_penalty(float *x, int32_t V, const int32_t *h, int32_t L,
  * occur only once.  The next id t is banned when the last n-1 ids followed
  * by t form an n-gram that already occurs in the history. */
 static void no_repeat_ngram(float *x, int32_t V, const int32_t *h, int32_t L,
-                            int32_t n) {
+                            int32_t n, float removed) {
   if (n <= 0 || L < n) return;
   const int32_t *tail = h + (L - n + 1); /* the last n-1 ids */
   for (int32_t i = 0; i + n <= L; ++i) {
     int match = 1;
     for (int32_t j = 0; j < n - 1; ++j)
       if (h[i + j] != tail[j]) { match = 0; break; }
-    if (match && in_vocab(h[i + n - 1], V)) x[h[i + n - 1]] = -INFINITY;
+    if (match && in_vocab(h[i + n - 1], V)) x[h[i + n - 1]] = removed;
   }
 }
 
-static void ban_ids(float *x, int32_t V, const int32_t *ids, int32_t n) {
+/* Removed ids take `removed`: -inf for selection; the smallest finite
+ * value in beam search ([T], the beam paragraph under "Log-probabilities"). */
+static void ban_ids(float *x, int32_t V, const int32_t *ids, int32_t n, float removed) {
   for (int32_t i = 0; i < n; ++i)
-    if (in_vocab(ids[i], V)) x[ids[i]] = -INFINITY;
+    if (in_vocab(ids[i], V)) x[ids[i]] = removed;
 }
 
 /* [T] "Lengths", forced_bos_token_id / forced_eos_token_id. */
-static void force_token(float *x, int32_t V, int32_t id) {
-  for (int32_t v = 0; v < V; ++v) x[v] = -INFINITY;
+static void force_token(float *x, int32_t V, int32_t id, float removed) {
+  for (int32_t v = 0; v < V; ++v) x[v] = removed;
   if (in_vocab(id, V)) x[id] = 0.0f;
 }
 
@@ -284,6 +287,35 @@ static int32_t sample_inverse_cdf(const float *x, int32_t V, float u,
   return order[pick];
 }
 
+/* The processors of [T] module doc, in its order, over one row of scores
+ * (from the repetition penalty to begin_suppress_tokens); removed ids take
+ * `removed`. */
+static void apply_processors(float *x, int32_t V, const int32_t *h, int32_t L, int32_t P,
+                             int32_t M, const oracle_cfg *cfg, float removed) {
+  const int32_t new_tokens = L - P;
+  if (cfg->repetition_penalty != 1.0f)
+    repetition_penalty(x, V, h, L, cfg->repetition_penalty);
+  if (cfg->no_repeat_ngram_size > 0)
+    no_repeat_ngram(x, V, h, L, cfg->no_repeat_ngram_size, removed);
+  ban_ids(x, V, cfg->bad_ids, cfg->n_bad, removed);
+  {
+    /* [T] "Lengths": min_new_tokens replaces min_length when both are set. */
+    int active = 0;
+    if (cfg->min_new_tokens > 0) active = new_tokens < cfg->min_new_tokens;
+    else if (cfg->min_length > 0) active = L < cfg->min_length;
+    if (active) ban_ids(x, V, cfg->eos_ids, cfg->n_eos, removed);
+  }
+  if (cfg->forced_bos >= 0 && L == 1) force_token(x, V, cfg->forced_bos, removed);
+  if (cfg->forced_eos >= 0 && L == M - 1) force_token(x, V, cfg->forced_eos, removed);
+  ban_ids(x, V, cfg->suppress_ids, cfg->n_suppress, removed);
+  {
+    /* [T] "Lengths", begin_suppress_tokens: at the first new token, or at
+     * the second when a forced bos followed a one-token prompt. */
+    int32_t begin = (cfg->forced_bos >= 0 && P == 1) ? 1 : 0;
+    if (new_tokens == begin) ban_ids(x, V, cfg->begin_ids, cfg->n_begin, removed);
+  }
+}
+
 /* ------------------------------------------------------------------ */
 /* The whole selection for one row.  logits_row: V logits of dtype;
  * h: L history ids (prompt then new tokens, chronological); P: prompt
@@ -313,29 +345,7 @@ int oracle_select_row(const void *logits_row, const int32_t *h, int32_t L,
   if (!x || !order || !buf) { free(x); free(order); free(buf); return -1; }
   for (int32_t v = 0; v < V; ++v) x[v] = load_logit(logits_row, cfg->dtype, v);
 
-  const int32_t new_tokens = L - P;
-  /* Processor order of [T] module doc. */
-  if (cfg->repetition_penalty != 1.0f)
-    repetition_penalty(x, V, h, L, cfg->repetition_penalty);
-  if (cfg->no_repeat_ngram_size > 0)
-    no_repeat_ngram(x, V, h, L, cfg->no_repeat_ngram_size);
-  ban_ids(x, V, cfg->bad_ids, cfg->n_bad);
-  {
-    /* [T] "Lengths": min_new_tokens replaces min_length when both are set. */
-    int active = 0;
-    if (cfg->min_new_tokens > 0) active = new_tokens < cfg->min_new_tokens;
-    else if (cfg->min_length > 0) active = L < cfg->min_length;
-    if (active) ban_ids(x, V, cfg->eos_ids, cfg->n_eos);
-  }
-  if (cfg->forced_bos >= 0 && L == 1) force_token(x, V, cfg->forced_bos);
-  if (cfg->forced_eos >= 0 && L == M - 1) force_token(x, V, cfg->forced_eos);
-  ban_ids(x, V, cfg->suppress_ids, cfg->n_suppress);
-  {
-    /* [T] "Lengths", begin_suppress_tokens: at the first new token, or at
-     * the second when a forced bos followed a one-token prompt. */
-    int32_t begin = (cfg->forced_bos >= 0 && P == 1) ? 1 : 0;
-    if (new_tokens == begin) ban_ids(x, V, cfg->begin_ids, cfg->n_begin);
-  }
+  apply_processors(x, V, h, L, P, M, cfg, -INFINITY);
   if (cfg->renormalize_logits) renormalize(x, V);
 
   if (!cfg->do_sample) {
@@ -511,6 +521,74 @@ int oracle_verify_select_row(const void *logits, int32_t k, int64_t stride, cons
   match_drafts(k, cand, sel, n_match, tokens, next, k_next);
   free(hx);
   free(sel);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* [T] the beam paragraph under "Log-probabilities": one step of beam
+ * search for one prompt of nb beams.  Each beam row takes the log-softmax
+ * of its logits (read as renormalize_logits above: (x - m) - ls in binary32
+ * with ls from binary64), then the processors with removed ids at the
+ * smallest finite value, then adds the beam's score; a score never goes
+ * below the smallest finite value.  Of the nb * V candidates (beam j, id v)
+ * at flattened index j * V + v, the best K are kept, by score descending
+ * and, among equal scores, by flattened index ascending.  On the first step
+ * only beam 0 counts (all beams of a prompt are equal); a padding beam row
+ * (L == 0) gives no candidates.  Slots past the candidates there are take
+ * score -inf, beam -1 and id -1.
+ *
+ * logits: nb rows of V logits at `stride` elements; h: nb histories at
+ * `hstride`; L, P, M: per beam.  Returns 0, or -1 on allocation failure. */
+typedef struct {
+  float score;
+  int64_t flat;
+} beam_cand;
+
+static int cmp_beam_cand(const void *a, const void *b) {
+  const beam_cand *x = (const beam_cand *)a, *y = (const beam_cand *)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->flat > y->flat) - (x->flat < y->flat);
+}
+
+int oracle_beam_step(const void *logits, int64_t stride, int32_t nb, const int32_t *h,
+                     int64_t hstride, const int32_t *L, const int32_t *P, const int32_t *M,
+                     const oracle_cfg *cfg, const float *beam_scores, int32_t first_step,
+                     int32_t K, float *out_scores, int32_t *out_beams, int32_t *out_tokens) {
+  const int32_t V = cfg->vocab;
+  const size_t esize = cfg->dtype == 0 ? 4 : 2;
+  float *x = (float *)malloc(sizeof(float) * (size_t)V);
+  beam_cand *c = (beam_cand *)malloc(sizeof(beam_cand) * (size_t)nb * (size_t)V);
+  if (!x || !c) { free(x); free(c); return -1; }
+  int64_t n = 0;
+  for (int32_t j = 0; j < nb; ++j) {
+    if ((first_step && j > 0) || L[j] == 0) continue;
+    const char *row = (const char *)logits + (size_t)j * (size_t)stride * esize;
+    for (int32_t v = 0; v < V; ++v) x[v] = load_logit(row, cfg->dtype, v);
+    renormalize(x, V);  /* the log-softmax of the logits */
+    apply_processors(x, V, h + (size_t)j * (size_t)hstride, L[j], P[j], M[j], cfg, -FLT_MAX);
+    for (int32_t v = 0; v < V; ++v) {
+      float sc = x[v] + beam_scores[j];
+      if (!(sc >= -FLT_MAX)) sc = -FLT_MAX;  /* never below the smallest finite value */
+      c[n].score = sc;
+      c[n].flat = (int64_t)j * V + v;
+      ++n;
+    }
+  }
+  qsort(c, (size_t)n, sizeof(beam_cand), cmp_beam_cand);
+  for (int32_t q = 0; q < K; ++q) {
+    if (q < n) {
+      out_scores[q] = c[q].score;
+      out_beams[q] = (int32_t)(c[q].flat / V);
+      out_tokens[q] = (int32_t)(c[q].flat % V);
+    } else {
+      out_scores[q] = -INFINITY;
+      out_beams[q] = -1;
+      out_tokens[q] = -1;
+    }
+  }
+  free(x);
+  free(c);
   return 0;
 }
 

@@ -144,6 +144,37 @@ def test_entry_points_reject_before_any_gpu_call():
 
 
 
+def test_beam_step_rejects_before_any_gpu_call():
+    """One beam-search step: the width rule, the workspace query, and the
+    host checks (settings, beams per prompt, vocabulary, workspace)."""
+    lib = tsel.load()
+    f = C.c_void_p(0x1000)
+    ws = C.c_void_p(0x2000)
+    assert [lib.tsel_beam_width(nb, e) for nb, e in [(1, 0), (4, 0), (4, 1), (4, 2), (3, 8)]] == \
+        [2, 8, 8, 12, 27]
+    assert lib.tsel_beam_width(0, 1) == 0 and lib.tsel_beam_width(2, -1) == 0
+
+    def call(p, nb, logits=f, wsp=ws, nbytes=1 << 30):
+        return lib.tsel_beam_step(logits, f, f, C.byref(p), nb, f, 0, f, f, f, wsp, nbytes, None)
+
+    p = _params(batch=8, eos_token_ids=[3])
+    need = lib.tsel_beam_step_workspace_size(C.byref(p), 4)
+    assert need >= 8 * 8 * 8  # each row's best K = 8 keys of 8 bytes
+    assert call(_params(batch=0), 4, logits=None) == tsel.TSEL_OK
+    assert call(p, 0) == tsel.TSEL_ERR_INVALID_ARG
+    assert call(p, 3) == tsel.TSEL_ERR_INVALID_ARG            # 8 rows are not prompts of 3
+    assert call(_params(batch=130), 65) == tsel.TSEL_ERR_UNSUPPORTED
+    assert call(_params(batch=8, do_sample=True), 4) == tsel.TSEL_ERR_INVALID_ARG
+    assert call(_params(batch=8, renormalize_logits=True), 4) == tsel.TSEL_ERR_INVALID_ARG
+    assert call(_params(batch=8, output_logprobs=True), 4) == tsel.TSEL_ERR_INVALID_ARG
+    assert call(_params(batch=8, vocab=409632, row_stride=409632), 4) == tsel.TSEL_ERR_UNSUPPORTED
+    assert call(p, 4, logits=None) == tsel.TSEL_ERR_INVALID_ARG
+    assert call(p, 4, wsp=None, nbytes=0) == tsel.TSEL_ERR_WORKSPACE
+    assert call(p, 4, nbytes=need - 1) == tsel.TSEL_ERR_WORKSPACE
+    assert call(p, 4, wsp=C.c_void_p(0x2010), nbytes=need) == tsel.TSEL_ERR_UNSUPPORTED
+    assert call(p, 4, logits=C.c_void_p(0x1004)) == tsel.TSEL_ERR_UNSUPPORTED
+
+
 def test_finish_step_rejects_before_any_gpu_call():
     """The end-of-step call: an empty batch does nothing; bad sizes, missing
     pointers and too many stop ids are refused on the host."""

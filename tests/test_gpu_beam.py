@@ -1,0 +1,230 @@
+"""GPU parity of one beam-search step (tsel_beam_step) with the oracle
+("Transmuter.Generation (transmuter v2.0.0)", the beam paragraph under
+"Log-probabilities").
+
+Both sides compute every candidate score with the same binary32 operations
+((x - m) - ls, the penalty, the beam score, the clamp), ls rounded once from
+binary64, so the kept candidates, their order and their scores are compared
+bit for bit.  The cases cover the processors with removed ids at the
+smallest finite value, forced rows, dead and padding beams, the first step,
+fewer candidates than slots, rows of equal scores (the select's deeper
+passes, in the rows and in the merge of 64 beams) and a 151,936-id
+vocabulary."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from logits_processing_token_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+sys.path.insert(0, os.path.dirname(__file__))
+from test_gpu_parity import _gpu  # noqa: E402,F401
+
+FMAX = float(np.finfo(np.float32).max)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gpu_run(w, first_step=False):
+    import torch
+    from logits_processing_token_amd import tsel
+    x = w["x"]
+    rows, V = x.shape
+    epc = 8 if x.dtype == np.uint16 else 4
+    stride = ((V + epc - 1) // epc) * epc
+    host = np.zeros((rows, stride), x.dtype)
+    host[:, :V] = x
+    dev = torch.device("cuda:0")
+    logits = torch.from_numpy(host.view(np.int16) if host.dtype == np.uint16 else host).to(dev)
+    dt = tsel.TSEL_BF16 if host.dtype == np.uint16 else tsel.TSEL_F32
+    masks = {}
+    for name in ("bad_words_ids", "suppress_tokens", "begin_suppress_tokens"):
+        if w["s"].get(name):
+            masks[name] = tsel.mask_build(V, torch.tensor(list(w["s"][name]), dtype=torch.int32,
+                                                          device=dev))
+    params = tsel.make_params(rows, V, stride, dt, w["hist"].shape[1], w["s"], masks)
+    lens = torch.from_numpy(np.concatenate([w["L"], w["P"], w["M"]]).astype(np.int32)).to(dev)
+    bs = torch.from_numpy(np.ascontiguousarray(w["bs"], np.float32)).to(dev)
+    sc, bm, tk = tsel.beam_step(logits, torch.from_numpy(w["hist"]).to(dev), lens, params,
+                                w["nb"], bs, first_step=first_step)
+    torch.cuda.synchronize()
+    return {"scores": sc.cpu().numpy(), "beams": bm.cpu().numpy(), "tokens": tk.cpu().numpy()}
+
+
+def _check(w, first_step=False):
+    rows, V = w["x"].shape
+    nb = w["nb"]
+    _say(f"  beam step: {rows // nb} prompts x {nb} beams, V {V}, {w['x'].dtype}, "
+         f"first {first_step}")
+    gpu = _gpu_run(w, first_step)
+    cfg = oracle.Config(**w["s"])
+    K = oracle.beam_width(nb, len(w["s"].get("eos_token_ids", [])))
+    ora = oracle.beam_step(w["x"], w["hist"], w["L"], w["P"], w["M"], cfg, nb, w["bs"],
+                           first_step=first_step, threads=16, width=K + 4)
+    for p in range(rows // nb):
+        want = {k: v[p, :K] for k, v in ora.items()}
+        got = {k: v[p] for k, v in gpu.items()}
+        same = (np.array_equal(got["beams"], want["beams"]) and
+                np.array_equal(got["tokens"], want["tokens"]) and
+                np.array_equal(got["scores"].view(np.uint32), want["scores"].view(np.uint32)))
+        assert same, (p, got, want, "next:", ora["scores"][p, K:], ora["beams"][p, K:],
+                      ora["tokens"][p, K:])
+    return gpu
+
+
+def _workload(seed, P, nb, V, dtype, settings, hist_len=24, scale=2.0, hot_hist=True):
+    g = np.random.default_rng(seed)
+    rows = P * nb
+    x = (g.standard_normal((rows, V)) * scale).astype(np.float32)
+    if hot_hist:  # history ids among each row's top ids, so the rules decide
+        top = np.argsort(-x, axis=1)[:, :12]
+        hist = np.take_along_axis(top, g.integers(0, 12, (rows, hist_len)), axis=1)
+    else:
+        hist = g.integers(0, V, (rows, hist_len))
+    hist = hist.astype(np.int32)
+    L = np.full(rows, hist_len, np.int32)
+    bs = (-6.0 * g.random(rows)).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.bf16_bits(x)
+    return dict(x=x, hist=hist, L=L, P=L.copy(), M=np.full(rows, 1 << 30, np.int32), bs=bs,
+                nb=nb, s=settings)
+
+
+@pytest.mark.parametrize("dtype,V,nb,eos", [
+    ("bf16", 32000, 4, []),
+    ("f32", 32000, 4, [2]),
+    ("bf16", 50272, 1, []),
+    ("f32", 50272, 8, [5, 6, 7]),
+])
+def test_beam_random(dtype, V, nb, eos):
+    w = _workload(2000 + V + nb, 8, nb, V, dtype, dict(eos_token_ids=eos), hot_hist=False)
+    _check(w)
+
+
+RULES = dict(repetition_penalty=1.3, no_repeat_ngram_size=2, bad_words_ids=[17, 4000],
+             suppress_tokens=[13], begin_suppress_tokens=[11, 12], min_new_tokens=3,
+             eos_token_ids=[3, 5], forced_bos_token_id=2, forced_eos_token_id=7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beam_processors(dtype):
+    """Every processor, with ids of the history among each row's best, and
+    rows at the length rules' edges: forced bos (length 1), forced eos
+    (length max_length - 1), the begin suppression, min_new_tokens, dead
+    beams (score -inf) and padding beams (length 0)."""
+    P, nb, V = 6, 4, 5000
+    w = _workload(31, P, nb, V, dtype, RULES)
+    rows = P * nb
+    g = np.random.default_rng(5)
+    L = np.full(rows, 24, np.int32)
+    Pl = np.full(rows, 20, np.int32)  # 4 new tokens: min_new_tokens off
+    M = np.full(rows, 1 << 30, np.int32)
+    L[0:4] = 1                        # prompt 0: forced bos on every beam
+    Pl[0:4] = 1
+    M[5] = 25                         # prompt 1, beam 1: forced eos
+    Pl[6] = 24                        # beam 2: no new token yet: begin suppression, eos banned
+    Pl[9] = 22                        # prompt 2: two new tokens: eos banned
+    L[13] = 0                         # prompt 3, beam 1: padding
+    w["bs"][14] = -np.inf             # beam 2 dead
+    Pl[16:20] = 1                     # prompt 4: a one-token prompt, forced bos then ...
+    L[16:20] = 2                      # ... the first free token: begin suppression
+    w["L"], w["P"], w["M"] = L, Pl, M
+    # put the banned and forced ids among the best scores of their rows
+    x = w["x"]
+    for r in range(rows):
+        for t in (2, 3, 5, 7, 11, 12, 13, 17):
+            if dtype == "bf16":  # (bit patterns: the row's best value itself)
+                vals = (x[r].astype(np.uint32) << 16).view(np.float32)
+                x[r, t] = x[r, np.argmax(vals)]
+            else:
+                x[r, t] = x[r].max() - 0.01 * g.random()
+    _check(w)
+
+
+def test_beam_first_step_and_short_vocab():
+    w = _workload(41, 5, 4, 9000, "bf16", dict(repetition_penalty=1.2, eos_token_ids=[1]))
+    _check(w, first_step=True)
+    # V = 3 ids, two beams, two eos ids: K = 6 slots for 3 (first step) or 6
+    # candidates
+    w = _workload(42, 3, 2, 3, "f32", dict(eos_token_ids=[0, 1]), hist_len=4, hot_hist=False)
+    g = _check(w, first_step=True)
+    assert (g["beams"][:, 3:] == -1).all() and (g["tokens"][:, 3:] == -1).all()
+    assert np.isneginf(g["scores"][:, 3:]).all()
+    _check(w)
+
+
+def test_beam_equal_scores_take_the_deep_select():
+    """Rows of one value: the row select cannot stop before its last pass,
+    and 64 beams x 576 slots overflow the merge's on-chip list the same way."""
+    rows = 3 * 4
+    x = np.zeros((rows, 32000), np.float32)
+    w = dict(x=synth.bf16_bits(x), hist=np.zeros((rows, 4), np.int32) + 5,
+             L=np.full(rows, 4, np.int32), P=np.full(rows, 4, np.int32),
+             M=np.full(rows, 1 << 30, np.int32), nb=4,
+             bs=np.array([0, 0, 0, 0, 0, -1, 0, -1, -2, -2, -2, -2], np.float32),
+             s=dict(repetition_penalty=2.0))
+    _check(w)
+    rows = 2 * 64
+    g = np.random.default_rng(7)
+    w = dict(x=np.zeros((rows, 3000), np.float32), hist=np.zeros((rows, 2), np.int32),
+             L=np.full(rows, 2, np.int32), P=np.full(rows, 2, np.int32),
+             M=np.full(rows, 1 << 30, np.int32), nb=64,
+             bs=g.choice(np.array([0.0, -1.0], np.float32), rows),
+             s=dict(eos_token_ids=list(range(8))))
+    _check(w)
+
+
+def test_beam_scores_clamp_at_the_smallest_finite_value():
+    """Candidates of dead beams, of beams whose score is -FLT_MAX and removed
+    ids all sit at -FLT_MAX and go by flattened index."""
+    P, nb, V = 4, 8, 10
+    g = np.random.default_rng(9)
+    x = (g.standard_normal((P * nb, V))).astype(np.float32)
+    bs = np.full(P * nb, -np.inf, np.float32)
+    bs[0::nb] = 0.0          # beam 0 live
+    bs[3::nb] = -FMAX        # beam 3 at the smallest finite value
+    bs[8 + 5] = -3e38        # prompt 1, beam 5: finite, between the two
+    w = dict(x=x, hist=np.zeros((P * nb, 2), np.int32), L=np.full(P * nb, 2, np.int32),
+             P=np.full(P * nb, 2, np.int32), M=np.full(P * nb, 1 << 30, np.int32), nb=nb,
+             bs=bs, s=dict(suppress_tokens=[4]))
+    g2 = _check(w)
+    assert (g2["scores"][[0, 2, 3], 9:] == -FMAX).all()
+    assert (g2["beams"][1, 9:] == 5).all() and (g2["scores"][1, 9:] > -FMAX).all()
+
+
+def test_beam_large_vocab():
+    """The 151,936-id bf16 vocabulary, 8 prompts x 4 beams, with the penalty
+    and an n-gram ban on histories of 256 ids."""
+    w = _workload(61, 8, 4, 151936, "bf16",
+                  dict(repetition_penalty=1.1, no_repeat_ngram_size=3, eos_token_ids=[0]),
+                  hist_len=256)
+    _check(w)
+
+
+def test_beam_strided_rows_and_stream():
+    """Rows at a padded stride, on a side stream."""
+    import torch
+    from logits_processing_token_amd import tsel
+    w = _workload(71, 4, 2, 1000, "f32", dict())
+    rows, V = w["x"].shape
+    dev = torch.device("cuda:0")
+    host = np.full((rows, 1024), 99.0, np.float32)  # padding that must not be read as ids
+    host[:, :V] = w["x"]
+    logits = torch.from_numpy(host).to(dev)
+    params = tsel.make_params(rows, V, 1024, tsel.TSEL_F32, w["hist"].shape[1], w["s"])
+    lens = torch.from_numpy(np.concatenate([w["L"], w["P"], w["M"]]).astype(np.int32)).to(dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        sc, bm, tk = tsel.beam_step(logits, torch.from_numpy(w["hist"]).to(dev), lens, params,
+                                    2, torch.from_numpy(w["bs"]).to(dev), stream=s.cuda_stream)
+    s.synchronize()
+    ora = oracle.beam_step(w["x"], w["hist"], w["L"], w["P"], w["M"], oracle.Config(), 2, w["bs"])
+    assert np.array_equal(tk.cpu().numpy(), ora["tokens"])
+    assert np.array_equal(bm.cpu().numpy(), ora["beams"])
+    assert np.array_equal(sc.cpu().numpy(), ora["scores"])
