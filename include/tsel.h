@@ -191,13 +191,14 @@ tsel_status tsel_mask_build(int32_t vocab, const int32_t *ids, int32_t n_ids,
  *  out_tokens   device int32 [B, k+1]: kept tokens, then -1.
  *  out_next     device int32 [B]: next[n_match].
  *  out_k        device int32 [B]: the next draft count.
- *  workspace    device, >= tsel_verify_workspace_size(B, k, V) bytes.  It
- *               must hold zeros before its first use (e.g. hipMemset once
- *               after allocation); every call leaves it that way again.
+ *  workspace    device, 8-byte aligned, >= tsel_verify_workspace_size(B, k,
+ *               V) bytes: the argmax of every chunk of every position row.
+ *               Its contents before a call do not matter (each call writes
+ *               what it reads); two calls in flight at once need two.
  * Errors: TSEL_ERR_INVALID_ARG for B < 0, k < 0, V < 1, a stride below V,
  * an unknown dtype, or NULL required pointers; TSEL_ERR_WORKSPACE when the
  * workspace is missing or too small; TSEL_ERR_UNSUPPORTED for misaligned
- * rows, k > 1023 or B * (k+1) > 65535.
+ * rows or workspace, k > 1023 or B * (k+1) > 65535.
  */
 tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_t k,
                         int32_t vocab, int64_t row_stride, const int32_t *candidates,
@@ -212,11 +213,11 @@ size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab);
  * tsel_verify_noalloc -- tsel_verify for callers that cannot allocate device
  * memory (code under HIP graph capture, serving loops that forbid
  * allocation).  Same arguments, results and checks as tsel_verify, without
- * the workspace: its partial maxima and per-row counters live in a
- * file-scope device array of TSEL_NOALLOC_SCRATCH_BYTES that each GPU holds
- * from its first call until the process ends.  The first call on a device
- * (device ids below 64) takes the array's address and clears it with a small
- * kernel on `stream`; no call allocates or frees memory.  Every call on one
+ * the workspace: its partial maxima live in a file-scope device array of
+ * TSEL_NOALLOC_SCRATCH_BYTES that each GPU holds from its first call until
+ * the process ends.  The first call on a device (device ids below 64) takes
+ * the array's address; no call allocates or frees memory, and nothing in the
+ * array needs to start at zero.  Every call on one
  * GPU shares that GPU's array, so calls that overlap in time on one GPU race
  * and give wrong results: the caller orders them (e.g. one stream).
  * Errors: as tsel_verify; TSEL_ERR_UNSUPPORTED when

@@ -24,37 +24,6 @@
 #include "k_select_common.hpp"
 
 namespace tsel {
-namespace {
-
-// Running (max, sum of exp(x - max)) of one thread's finite scores.
-struct LseAcc {
-  double m = -INFINITY;
-  double s = 0.0;
-  __device__ __forceinline__ void add(float xf) {
-    const double x = (double)xf;
-    if (!(x > -INFINITY)) return;
-    if (x > m) {
-      s = s * exp(m - x) + 1.0;  // (exp(-inf) = 0 on the first score)
-      m = x;
-    } else {
-      s += exp(x - m);
-    }
-  }
-};
-
-// The row's largest finite score M (-inf if none) and S = sum exp(x - M).
-template <int NT_>
-__device__ __forceinline__ void lse_join(const LseAcc &acc, float *rmax, double *rsum, float *M_out,
-                                         double *S_out) {
-  const float M = block_max_f32<NT_>((float)acc.m, rmax);
-  double part = 0.0;
-  if (acc.m > -INFINITY) part = acc.s * exp(acc.m - (double)M);
-  const double S = block_sum_f64<NT_>(part, rsum);
-  *M_out = M;
-  *S_out = S;
-}
-
-}  // namespace
 
 // =========================================================================
 // k_renorm: processors, then the log-softmax of the row, into dst (fp32 rows
@@ -114,7 +83,7 @@ __global__ __launch_bounds__(kLpThreads) void k_logprob(const float *proc, int64
   __shared__ double rsum[kLpThreads / kWave];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int t = tokens[row];
-  const float qnan = __uint_as_float(0x7FC00000u);
+  const float qnan = lp_none();
   if (t < 0 || t >= V) {  // no token (a padding row)
     if (tid == 0) out[row] = qnan;
     return;

@@ -100,6 +100,39 @@ __device__ __forceinline__ double mass_key_ge(const SelectArgs &a, int row, cons
   return block_sum_f64<NT>(m, sh.red_f64);
 }
 
+// The token's log-probability over the final scores of its row
+// ("Transmuter.Generation (transmuter v2.0.0)", "Log-probabilities"): the
+// kept scores are those >= t_y whose selection key is >= kcut, each after
+// temperature; the result is y_t - M - log(sum exp(y - M)) over them in
+// binary64, rounded once (NaN when nothing is kept).  One more pass over
+// the row (PLAIN: visit_plain rather than the chunk stream) and the list;
+// the token's own final score is picked up on the way.
+template <int DT, bool PLAIN = false>
+__device__ __forceinline__ float kept_logprob(const SelectArgs &a, int row, const Lds &s,
+                                              RowShared &sh, float t_y, uint64_t kcut,
+                                              int token) {
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  const float T = a.temperature;
+  const int n_list = sh.n_list;
+  LseAcc acc;
+  float yt = -INFINITY;
+  auto body = [&](int v, float y) {
+    if (v == token) yt = y;
+    if (y > -INFINITY && y >= t_y && sel_key(y, (uint32_t)v) >= kcut) acc.add(y);
+  };
+  if (PLAIN) visit_plain<DT>(a, rowp, s, [&](int v, float x) { body(v, (T != 1.0f) ? x / T : x); });
+  else stream_row<DT>(a, rowp, s, sh.dense_pen != 0,
+                      [&](int v, float x) { body(v, (T != 1.0f) ? x / T : x); });
+  for (int i = threadIdx.x; i < n_list; i += NT)
+    body(s.list_id[i], (T != 1.0f) ? s.list_val[i] / T : s.list_val[i]);
+  float M;
+  double S;
+  lse_join<NT>(acc, sh.red_f32, sh.red_f64, &M, &S);
+  yt = block_max_f32<NT>(yt, sh.red_f32);
+  if (!(M > -INFINITY) || !(yt > -INFINITY)) return lp_none();
+  return (float)(((double)yt - (double)M) - log(S));
+}
+
 // Top_p cut and inverse-CDF draw by bisection over 64-bit selection keys.
 // Returns the token; *kcut_out = smallest kept key.
 template <int DT, bool PLAIN = false>

@@ -18,6 +18,39 @@ constexpr uint32_t kNoDigit = 0xFFFFFFFFu;
 constexpr int kPending = -2;         // token marker: row left for k_full
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The log-probability of a row without a token, or whose scores are all
+// -inf: the quiet NaN with sign bit 0.
+__device__ __forceinline__ float lp_none() { return __uint_as_float(0x7FC00000u); }
+
+// Running (max, sum of exp(x - max)) of one thread's finite scores in
+// binary64; the sum is rescaled when the maximum moves.
+struct LseAcc {
+  double m = -INFINITY;
+  double s = 0.0;
+  __device__ __forceinline__ void add(float xf) {
+    const double x = (double)xf;
+    if (!(x > -INFINITY)) return;
+    if (x > m) {
+      s = s * exp(m - x) + 1.0;  // (exp(-inf) = 0 on the first score)
+      m = x;
+    } else {
+      s += exp(x - m);
+    }
+  }
+};
+
+// The largest finite score M over the workgroup (-inf if none) and S = sum
+// exp(x - M), joining every thread's pair at M.  Every thread calls.
+template <int NT_>
+__device__ __forceinline__ void lse_join(const LseAcc &acc, float *rmax, double *rsum,
+                                         float *M_out, double *S_out) {
+  const float M = block_max_f32<NT_>((float)acc.m, rmax);
+  double part = 0.0;
+  if (acc.m > -INFINITY) part = acc.s * exp(acc.m - (double)M);
+  *S_out = block_sum_f64<NT_>(part, rsum);
+  *M_out = M;
+}
+
 template <int DT>
 struct Elem;
 template <>
@@ -214,7 +247,10 @@ __device__ __forceinline__ bool row_prologue_after_lens(const SelectArgs &a, int
       a.begin_mask != nullptr && ri.new_tokens == ((a.forced_bos >= 0 && ri.P == 1) ? 1 : 0);
   float *outp = a.out_processed ? a.out_processed + (int64_t)row * V : nullptr;
   if (ri.L <= 0) {
-    if (tid == 0) a.out_tokens[row] = -1;
+    if (tid == 0) {
+      a.out_tokens[row] = -1;
+      if (a.out_logprobs) a.out_logprobs[row] = lp_none();
+    }
     if (outp)
       for (int v = tid; v < V; v += NT) outp[v] = -INFINITY;
     return true;
@@ -226,7 +262,11 @@ __device__ __forceinline__ bool row_prologue_after_lens(const SelectArgs &a, int
     bool alive = forced < V;
     if (alive && a.sup_mask && bit_of(a.sup_mask, forced)) alive = false;
     if (alive && ri.begin_active && bit_of(a.begin_mask, forced)) alive = false;
-    if (tid == 0) a.out_tokens[row] = alive ? forced : 0;
+    if (tid == 0) {
+      a.out_tokens[row] = alive ? forced : 0;
+      // (the lone score 0 has log-probability 0)
+      if (a.out_logprobs) a.out_logprobs[row] = alive ? 0.0f : lp_none();
+    }
     if (outp)
       for (int v = tid; v < V; v += NT) outp[v] = (alive && v == forced) ? 0.0f : -INFINITY;
     return true;

@@ -3,14 +3,17 @@
 // toward low-latency text generation", section "Greedy decoding with assisted
 // generation", steps 3-6).
 //
-// Every (position row, vocabulary chunk) pair is one workgroup of 256
-// threads that streams its chunk once (16 bytes per lane per load) and
-// reduces a (score, id) argmax; the partial maxima go to the workspace.  The
-// last workgroup to finish a batch row (an atomic counter per row) merges the
-// partials of its k+1 positions, counts the left-to-right matches, writes the
-// kept tokens and the next draft count, and clears the counter for the next
-// call.  Chunks keep the grid well above the 256 compute units even when
-// B * (k+1) is small.
+// Two launches.  k_verify_part: every (position row, vocabulary chunk) pair
+// is one workgroup of 256 threads that streams its chunk once (16 bytes per
+// lane per load) and writes the (score, id) argmax key of the chunk to the
+// workspace.  k_verify_merge: one wave per batch row merges the chunk keys of
+// its k+1 positions, counts the left-to-right matches, and writes the kept
+// tokens, the next token and the next draft count.  The launch boundary
+// orders the partial keys before the merge, so no workgroup needs a
+// device-wide fence (on this GPU one writes back and invalidates the L2), and
+// nothing in the workspace carries over from one call to the next.  Chunks
+// keep the grid well above the 256 compute units even when B * (k+1) is
+// small.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,19 +29,14 @@ constexpr int VT = 256;   // threads per workgroup
 constexpr int VCH = 8;    // 16-byte chunks per lane per workgroup
 
 template <int DT>
-__global__ __launch_bounds__(VT) void k_verify(const char *logits, int64_t row_bytes, int V,
-                                               int k, int S, const int32_t *cand,
-                                               int32_t *n_match, int32_t *tokens, int32_t *next,
-                                               int32_t *k_out, uint64_t *partials,
-                                               uint32_t *counters) {
+__global__ __launch_bounds__(VT) void k_verify_part(const char *logits, int64_t row_bytes,
+                                                    int V, int S, uint64_t *partials) {
   constexpr int EPC = DT == 1 ? 8 : 4;
   constexpr int CHUNK = VT * VCH * EPC;  // elements per workgroup
   __shared__ uint64_t red[VT / kWave];
-  __shared__ int last;
   const int tid = threadIdx.x;
   const int s = blockIdx.x;       // chunk of the row
   const int r = blockIdx.y;       // position row b * (k+1) + j
-  const int b = r / (k + 1);
   const char *rowp = logits + (int64_t)r * row_bytes;
   const int NG = V / EPC;
   const int e0 = s * CHUNK;
@@ -82,38 +80,32 @@ __global__ __launch_bounds__(VT) void k_verify(const char *logits, int64_t row_b
     uint64_t m = red[0];
     for (int i = 1; i < VT / kWave; ++i) m = red[i] > m ? red[i] : m;
     partials[(int64_t)r * S + s] = m;
-    __threadfence();  // publish the partial before counting this workgroup
-    const uint32_t done = atomicAdd(&counters[b], 1u);
-    last = done == (uint32_t)((k + 1) * S - 1);
   }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // Epilogue for batch row b: merge the partials of each position, then the
-  // left-to-right comparison (it stops at the first mismatch).
+}
+
+// One wave per batch row b: merge each position's chunk keys, then the
+// left-to-right comparison (it stops at the first mismatch).
+__global__ __launch_bounds__(kWave) void k_verify_merge(int k, int S, const int32_t *cand,
+                                                        const uint64_t *partials,
+                                                        int32_t *n_match, int32_t *tokens,
+                                                        int32_t *next, int32_t *k_out) {
   __shared__ int sel[kMaxVerifyK + 1];
-  __shared__ int nm_s;
-  for (int j = tid; j <= k; j += VT) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int j = lane; j <= k; j += kWave) {
     uint64_t m = 0ull;
     const uint64_t *p = partials + ((int64_t)b * (k + 1) + j) * S;
-    for (int q = 0; q < S; ++q) {
-      const uint64_t v = __hip_atomic_load(p + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      m = v > m ? v : m;
-    }
+    for (int q = 0; q < S; ++q) m = p[q] > m ? p[q] : m;
     sel[j] = m == 0ull ? 0 : (int)key_index(m);  // every score -inf: the lowest id
   }
   __syncthreads();
-  if (tid == 0) {
-    int nm = 0;
-    while (nm < k && cand[(int64_t)b * k + nm] == sel[nm]) ++nm;
-    nm_s = nm;
+  int nm = 0;
+  while (nm < k && cand[(int64_t)b * k + nm] == sel[nm]) ++nm;  // (every lane alike)
+  if (lane == 0) {
     n_match[b] = nm;
     next[b] = sel[nm];
     k_out[b] = nm == k ? k + 2 : (k - 1 > 1 ? k - 1 : 1);
-    counters[b] = 0u;  // ready for the next call
   }
-  __syncthreads();
-  for (int j = tid; j <= k; j += VT) tokens[(int64_t)b * (k + 1) + j] = j <= nm_s ? sel[j] : -1;
+  for (int j = lane; j <= k; j += kWave) tokens[(int64_t)b * (k + 1) + j] = j <= nm ? sel[j] : -1;
 }
 
 // ---- the variant that allocates nothing -------------------------------------
@@ -129,40 +121,30 @@ std::mutex g_scratch_mu;
 void *g_scratch_at[kNoAllocDevices];  // per device id: the array's address, once set up
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_clear_words(uint32_t *p, int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
-}
-
 hipError_t launch_verify_noalloc(const void *logits, int32_t dtype, int32_t B, int32_t k,
                                  int32_t V, int64_t row_bytes, int32_t chunks,
-                                 size_t partial_bytes, const int32_t *cand, int32_t *n_match,
-                                 int32_t *tokens, int32_t *next, int32_t *k_out, hipStream_t s) {
+                                 const int32_t *cand, int32_t *n_match, int32_t *tokens,
+                                 int32_t *next, int32_t *k_out, hipStream_t s) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kNoAllocDevices) return hipErrorInvalidDevice;
-  char *base = nullptr;
+  void *base = nullptr;
   {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_at[dev]) {
-      // set-up on this device (it is current): the array's address, then its
-      // counters cleared once; every call leaves them at zero again
+      // set-up on this device (it is current): the array's address; nothing
+      // in it needs to start at zero (every call writes the keys it reads)
       void *p = nullptr;
       e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
       if (e != hipSuccess) return e;
       if (!p) return hipErrorInvalidSymbol;
-      constexpr int n = (int)(kNoAllocScratchBytes / 4);
-      hipLaunchKernelGGL(k_clear_words, dim3(64), dim3(256), 0, s, static_cast<uint32_t *>(p), n);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
       g_scratch_at[dev] = p;
     }
-    base = static_cast<char *>(g_scratch_at[dev]);
+    base = g_scratch_at[dev];
   }
-  uint64_t *partials = reinterpret_cast<uint64_t *>(base);
-  uint32_t *counters = reinterpret_cast<uint32_t *>(base + ((partial_bytes + 15) & ~size_t(15)));
   return launch_verify(logits, dtype, B, k, V, row_bytes, chunks, cand, n_match, tokens, next,
-                       k_out, partials, counters, s);
+                       k_out, static_cast<uint64_t *>(base), s);
 }
 
 int verify_chunks(int32_t V, int32_t dtype) {
@@ -173,15 +155,19 @@ int verify_chunks(int32_t V, int32_t dtype) {
 hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
                          int64_t row_bytes, int32_t chunks, const int32_t *cand,
                          int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,
-                         uint64_t *partials, uint32_t *counters, hipStream_t s) {
+                         uint64_t *partials, hipStream_t s) {
   if (B == 0) return hipSuccess;
   dim3 grid(chunks, B * (k + 1));
   if (dtype == 1)
-    hipLaunchKernelGGL(k_verify<1>, grid, dim3(VT), 0, s, (const char *)logits, row_bytes, V, k,
-                       chunks, cand, n_match, tokens, next, k_out, partials, counters);
+    hipLaunchKernelGGL(k_verify_part<1>, grid, dim3(VT), 0, s, (const char *)logits, row_bytes,
+                       V, chunks, partials);
   else
-    hipLaunchKernelGGL(k_verify<0>, grid, dim3(VT), 0, s, (const char *)logits, row_bytes, V, k,
-                       chunks, cand, n_match, tokens, next, k_out, partials, counters);
+    hipLaunchKernelGGL(k_verify_part<0>, grid, dim3(VT), 0, s, (const char *)logits, row_bytes,
+                       V, chunks, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_verify_merge, dim3(B), dim3(kWave), 0, s, k, chunks, cand,
+                     (const uint64_t *)partials, n_match, tokens, next, k_out);
   return hipGetLastError();
 }
 

@@ -518,7 +518,10 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   uint64_t kcut = 0ull;
   int token = 0;
   if (mx == -INFINITY) {  // every id removed: id 0, nothing kept
-    if (tid == 0) a.out_tokens[row] = 0;
+    if (tid == 0) {
+      a.out_tokens[row] = 0;
+      if (a.out_logprobs) a.out_logprobs[row] = lp_none();
+    }
     if (a.out_processed) {
       untag(n_list);
       res_processed<1>(a, row, s, INFINITY, ~0ull, n_list);
@@ -800,6 +803,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   double Wp = W;
   int cut_kind = kNone, draw_kind = kNone;
   int cut_pos = 0x7FFFFFFF;
+  int cut_rank = -1;  // kGroup cut: the boundary group's members kept, less one
   int bs = -1;
   double bs_start = 0.0;
   // The count pass for the draw's member (all threads), run while wave 0
@@ -1019,6 +1023,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
         if (cut_kind == kFail) fallback = true;
         Wp = uni(vs.walk[0].acc);
         cut_pos = uni(vs.walk[0].pos);
+        cut_rank = uni(vs.walk[0].rank);
         if (cut_kind == kInd) kcut = uni(vs.walk[0].key);
       }
       bs = bq;
@@ -1040,6 +1045,7 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
         if (cut_kind == kFail) fallback = true;
         Wp = uni(vs.walk[0].acc);
         cut_pos = uni(vs.walk[0].pos);
+        cut_rank = uni(vs.walk[0].rank);
         if (cut_kind == kInd) kcut = uni(vs.walk[0].key);
       }
     }
@@ -1181,9 +1187,65 @@ __global__ __launch_bounds__(NT, 1) void k_vres(SelectArgs a) {
   if (!fallback && draw_kind == kGroup) token = vs.gid[1];
   if (!fallback && draw_kind == kInd) token = (int)key_index(vs.walk[1].key);
 
-  if (fallback || a.out_processed) untag(n_ind);
+  // ---- 6. the token's log-probability ("Log-probabilities") --------------
+  // The log-softmax of the kept scores at the token, in binary64 from the
+  // counts: every bin above the boundary's keeps its dense members (one
+  // value: count * exp(v - mx)); the boundary bin keeps (cut_rank + 1)
+  // members of its tie group, or, cut at an individual, its group when the
+  // value lies above the cut; individuals are kept by bin and by key.  mx
+  // bounds the row's scores from above (any shift gives the same value).
+  // A row whose kept set reaches the dropped scores (no boundary, and some
+  // scores below the bins), or that took the bisection, sums over the row
+  // from memory instead.
+  float lp = 0.0f;
+  bool lp_row = fallback;
+  if (a.out_logprobs && !fallback) {
+    if (bp < 0 && (uni(cnt[0]) & kDenseMask) != 0u) {
+      lp_row = true;
+    } else {
+      const double M = (double)mx;
+      const float yt = draw_kind == kGroup ? bin_value(bs) : key_score(vs.walk[1].key);
+      const float vcut = bp >= 0 ? bin_value(bp) : 0.0f;
+      const float scut = cut_kind == kInd ? key_score(kcut) : 0.0f;
+      double acc = 0.0;
+      if (tid * BPT < NB) {
+        const uint4 n4 = reinterpret_cast<const uint4 *>(cnt)[tid];
+        const uint32_t nq[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+          const int b = tid * BPT + q;
+          const uint32_t n = nq[q] & kDenseMask;
+          if (b < 1 || n == 0u) continue;
+          const float v = bin_value(b);
+          if (!(v > -INFINITY)) continue;
+          if (bp < 0 || b > bp || (b == bp && cut_kind == kInd && v > scut))
+            acc += (double)n * exp((double)v - M);
+        }
+      }
+      for (int k = tid; k < n_ind; k += NT) {
+        const int tagged = s.list_id[k];
+        const float y = s.list_val[k];
+        if (!(y > -INFINITY)) continue;
+        const int b = tagged >> kIdBits;
+        const bool kept =
+            bp < 0 || b > bp ||
+            (b == bp && (cut_kind == kGroup ? y > vcut
+                                            : sel_key(y, (uint32_t)(tagged & kIdMask)) >= kcut));
+        if (kept) acc += exp((double)y - M);
+      }
+      if (tid == 0 && cut_kind == kGroup) acc += (double)(cut_rank + 1) * exp((double)vcut - M);
+      const double Wk = block_sum_f64<NT>(acc, sh.red_f64);
+      lp = (float)(((double)yt - M) - log(Wk));
+    }
+  }
+
+  if (fallback || a.out_processed || lp_row) untag(n_ind);
   if (fallback) token = bisect_select<1, true>(a, row, s, sh, -INFINITY, cref, &kcut);
-  if (tid == 0) a.out_tokens[row] = token;
+  if (a.out_logprobs && lp_row) lp = kept_logprob<1, true>(a, row, s, sh, -INFINITY, kcut, token);
+  if (tid == 0) {
+    a.out_tokens[row] = token;
+    if (a.out_logprobs) a.out_logprobs[row] = lp;
+  }
   if (a.out_processed) res_processed<1>(a, row, s, -INFINITY, kcut, n_list);
 }
 

@@ -194,22 +194,6 @@ tsel_status tsel_validate_params(const tsel_params *params, int32_t sampling_uni
   return check_params(params, sampling_uniforms_given != 0);
 }
 
-// Rows of the workspace: the renormalized scores (fp32, a 16-byte aligned
-// stride) when renormalize_logits is on, then the final scores a
-// log-probability is taken over (fp32 [B, V]) when output_logprobs is.
-static size_t renorm_stride(const tsel_params *p) { return ((size_t)p->vocab + 3) & ~size_t(3); }
-static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-static size_t renorm_bytes(const tsel_params *p) {
-  return p->renormalize_logits ? align256((size_t)p->batch * renorm_stride(p) * 4) : 0;
-}
-
-size_t tsel_process_select_workspace_size(const tsel_params *params) {
-  if (!params || params->batch <= 0 || params->vocab < 1) return 0;
-  size_t n = renorm_bytes(params);
-  if (params->output_logprobs) n += align256((size_t)params->batch * (size_t)params->vocab * 4);
-  return n;
-}
-
 // The rows and the processors' settings of p as kernel arguments (the
 // warpers off).
 static tsel::SelectArgs proc_args(const tsel_params *params, const void *logits,
@@ -240,64 +224,129 @@ static tsel::SelectArgs proc_args(const tsel_params *params, const void *logits,
   return a;
 }
 
+// The kernel path one selection takes for the settings of p.  kTopK and
+// kFull also finish the rows whose candidates overflow or whose history
+// outgrows the resident list; every path but kGreedy and kRes computes the
+// log-probabilities itself (the other two leave them to a pass over the
+// final scores).
+enum class Path { kGreedy, kVres, kRes, kTopK, kFull, kNone };
+
+static Path select_path(const tsel_params *p) {
+  tsel::SelectArgs probe{};
+  size_t lds = 0;
+  if (!p->do_sample)
+    return plan_layout(p, SelectKernel::kGreedy, &probe, &lds) ? Path::kGreedy : Path::kNone;
+  if (!plan_layout(p, SelectKernel::kFull, &probe, &lds)) return Path::kNone;
+  const int res = resident_chunks(p);
+  const int epc = p->dtype == TSEL_BF16 ? 8 : 4;
+  const bool simple = p->top_k <= 0 && p->temperature == 1.0f && res > 0 && p->vocab >= epc;
+  if (simple && p->dtype == TSEL_BF16 && plan_vres(p, res, &probe, &lds)) return Path::kVres;
+  if (simple && plan_layout(p, SelectKernel::kRes, &probe, &lds)) return Path::kRes;
+  if (p->top_k > 0 && plan_layout(p, SelectKernel::kTopK, &probe, &lds) &&
+      std::min(p->top_k, p->vocab) * 4 <= probe.tcap)
+    return Path::kTopK;
+  return Path::kFull;
+}
+
+static bool fused_logprobs(Path path) { return path != Path::kGreedy && path != Path::kRes; }
+
+// Rows of the workspace: the renormalized scores (fp32, a 16-byte aligned
+// stride) when renormalize_logits is on, then the final scores a
+// log-probability is taken over (fp32 [B, V]) when output_logprobs is and the
+// selection's path leaves it to a pass over them.
+static size_t renorm_stride(const tsel_params *p) { return ((size_t)p->vocab + 3) & ~size_t(3); }
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+static size_t renorm_bytes(const tsel_params *p) {
+  return p->renormalize_logits ? align256((size_t)p->batch * renorm_stride(p) * 4) : 0;
+}
+
+// The params the selection itself sees: after renormalize_logits, fp32 rows
+// with every processor switched off (the lengths still mark padding rows).
+static tsel_params selection_params(const tsel_params *params) {
+  tsel_params p = *params;
+  if (!params->renormalize_logits) return p;
+  p.dtype = TSEL_F32;
+  p.logits_row_stride = (int64_t)renorm_stride(params);
+  p.repetition_penalty = 1.0f;
+  p.no_repeat_ngram_size = 0;
+  p.bad_words_mask = p.suppress_mask = p.begin_suppress_mask = nullptr;
+  p.min_length = p.min_new_tokens = 0;
+  p.n_eos = 0;
+  p.forced_bos_token_id = p.forced_eos_token_id = -1;
+  p.renormalize_logits = 0;
+  return p;
+}
+
+size_t tsel_process_select_workspace_size(const tsel_params *params) {
+  if (!params || params->batch <= 0 || params->vocab < 1) return 0;
+  size_t n = renorm_bytes(params);
+  if (params->output_logprobs) {
+    const tsel_params q = selection_params(params);
+    if (!fused_logprobs(select_path(&q)))
+      n += align256((size_t)params->batch * (size_t)params->vocab * 4);
+  }
+  return n;
+}
+
 // The kernels for one selection over `logits` with the settings of p (the
 // arguments already checked); hipErrorNotSupported when V does not fit the
-// on-chip layout.
+// on-chip layout.  out_logprobs is written only on the paths that compute it.
 static hipError_t dispatch_select(const tsel_params *params, const void *logits,
                                   const int32_t *history, const int32_t *lens,
                                   const float *uniforms, int32_t *out_tokens, float *out_processed,
-                                  hipStream_t s) {
+                                  float *out_logprobs, hipStream_t s) {
+  const Path path = select_path(params);
+  if (path == Path::kNone) return hipErrorNotSupported;
   tsel::SelectArgs a = proc_args(params, logits, history, lens);
   a.uniforms = uniforms;
   a.out_tokens = out_tokens;
   a.out_processed = out_processed;
+  a.out_logprobs = fused_logprobs(path) ? out_logprobs : nullptr;
   a.do_sample = params->do_sample ? 1 : 0;
   a.temperature = params->temperature;
   a.top_k = params->top_k;
   a.top_p = params->top_p;
   size_t lds = 0;
-  hipError_t e = hipSuccess;
-  if (!a.do_sample) {  // greedy: the warpers do not apply
+  if (path == Path::kGreedy) {  // greedy: the warpers do not apply
     a.temperature = 1.0f;
     a.top_k = 0;
     a.top_p = 1.0f;
-    if (!plan_layout(params, SelectKernel::kGreedy, &a, &lds)) return hipErrorNotSupported;
-    e = tsel::launch_greedy(a, lds, s);
-  } else {
-    tsel::SelectArgs t = a;
-    size_t tlds = 0;
-    const bool topk = a.top_k > 0 && plan_layout(params, SelectKernel::kTopK, &t, &tlds) &&
-                      std::min(a.top_k, a.V) * 4 <= t.tcap;
-    if (!plan_layout(params, SelectKernel::kFull, &a, &lds)) return hipErrorNotSupported;
-    const int res = resident_chunks(params);
-    const int epc = params->dtype == TSEL_BF16 ? 8 : 4;
-    tsel::SelectArgs r = a;
-    size_t rlds = 0;
-    if (a.top_k <= 0 && a.temperature == 1.0f && res > 0 && a.V >= epc &&
-        a.dtype == TSEL_BF16 && plan_vres(params, res, &r, &rlds)) {
+    plan_layout(params, SelectKernel::kGreedy, &a, &lds);
+    return tsel::launch_greedy(a, lds, s);
+  }
+  plan_layout(params, SelectKernel::kFull, &a, &lds);
+  const int res = resident_chunks(params);
+  const int64_t most_seen = std::min<int64_t>(std::max(params->hist_stride, 0), a.V);
+  tsel::SelectArgs r = a;
+  size_t rlds = 0;
+  hipError_t e = hipSuccess;
+  switch (path) {
+    case Path::kVres:
       // bf16 row held in registers, one histogram bin per bf16 value; rows
       // with more distinct seen ids than the list holds are left pending
       // for the streamed path
+      plan_vres(params, res, &r, &rlds);
       e = tsel::launch_vres(r, res, rlds, s);
-      const int64_t most_seen = std::min<int64_t>(std::max(params->hist_stride, 0), a.V);
-      if (e == hipSuccess && r.lcap < most_seen)
-        e = tsel::launch_full(a, res, lds, s, 1);
-    } else if (a.top_k <= 0 && a.temperature == 1.0f && res > 0 && a.V >= epc &&
-        plan_layout(params, SelectKernel::kRes, &r, &rlds)) {
+      if (e == hipSuccess && r.lcap < most_seen) e = tsel::launch_full(a, res, lds, s, 1);
+      break;
+    case Path::kRes:
       // Row held in registers.  A row with more distinct seen ids than the
       // on-chip list holds is left pending for the streamed path.
+      plan_layout(params, SelectKernel::kRes, &r, &rlds);
       e = tsel::launch_res(r, res, rlds, s);
-      const int64_t most_seen = std::min<int64_t>(std::max(params->hist_stride, 0), a.V);
-      if (e == hipSuccess && r.lcap < most_seen)
-        e = tsel::launch_full(a, res, lds, s, 1);
-    } else if (topk) {
-      // Candidate-buffer pass; rows whose ties overflow it are marked and
-      // finished by the full path right after, on the same stream.
-      e = tsel::launch_topk(t, tlds, s);
-      if (e == hipSuccess) e = tsel::launch_full(a, resident_chunks(params), lds, s, 1);
-    } else {
-      e = tsel::launch_full(a, resident_chunks(params), lds, s, 0);
+      if (e == hipSuccess && r.lcap < most_seen) e = tsel::launch_full(a, res, lds, s, 1);
+      break;
+    case Path::kTopK: {
+      // Candidate-buffer pass; a row whose ties overflow it runs the full
+      // path in the same workgroup, with that path's layout.
+      tsel::SelectArgs t = a;
+      size_t tlds = 0;
+      plan_layout(params, SelectKernel::kTopK, &t, &tlds);
+      e = tsel::launch_topk(t, a, std::max(tlds, lds), s);
+      break;
     }
+    default:
+      e = tsel::launch_full(a, res, lds, s, 0);
   }
   return e;
 }
@@ -318,7 +367,7 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TSEL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
-  tsel_params p = *params;
+  const tsel_params p = selection_params(params);
   const void *src = logits;
   hipError_t e = hipSuccess;
   if (params->renormalize_logits) {
@@ -331,22 +380,16 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
     e = tsel::launch_renorm(ra, lds, reinterpret_cast<float *>(ws), (int64_t)renorm_stride(params), s);
     if (e != hipSuccess) return TSEL_ERR_LAUNCH;
     src = ws;
-    p.dtype = TSEL_F32;
-    p.logits_row_stride = (int64_t)renorm_stride(params);
-    p.repetition_penalty = 1.0f;
-    p.no_repeat_ngram_size = 0;
-    p.bad_words_mask = p.suppress_mask = p.begin_suppress_mask = nullptr;
-    p.min_length = p.min_new_tokens = 0;
-    p.n_eos = 0;
-    p.forced_bos_token_id = p.forced_eos_token_id = -1;
-    p.renormalize_logits = 0;
     ws += renorm_bytes(params);
   }
+  // log-probabilities: from the selection kernels, or from a pass over the
+  // final scores (into the workspace when the caller does not want them)
+  const bool post = out_logprobs && !fused_logprobs(select_path(&p));
   float *proc = out_processed;
-  if (out_logprobs && !proc) proc = reinterpret_cast<float *>(ws);
-  e = dispatch_select(&p, src, history, lens, uniforms, out_tokens, proc, s);
+  if (post && !proc) proc = reinterpret_cast<float *>(ws);
+  e = dispatch_select(&p, src, history, lens, uniforms, out_tokens, proc, out_logprobs, s);
   if (e == hipErrorNotSupported) return TSEL_ERR_UNSUPPORTED;  // (a layout that does not fit)
-  if (e == hipSuccess && out_logprobs)
+  if (e == hipSuccess && post)
     e = tsel::launch_logprob(proc, params->vocab, params->batch, params->vocab, out_tokens,
                              out_logprobs, s);
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
@@ -507,7 +550,7 @@ static size_t verify_partial_bytes(int32_t batch, int32_t k, int32_t vocab);
 
 size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab) {
   if (batch <= 0 || k < 0 || vocab < 1) return 0;
-  return align16(verify_partial_bytes(batch, k, vocab)) + align16((size_t)batch * 4);
+  return align16(verify_partial_bytes(batch, k, vocab));
 }
 
 // Host checks shared by both verify entry points (TSEL_OK to go on).
@@ -543,14 +586,12 @@ tsel_status tsel_verify(const void *logits, int32_t dtype, int32_t batch, int32_
   const size_t need = tsel_verify_workspace_size(batch, k, vocab);
   if (!workspace || workspace_bytes < need) return TSEL_ERR_WORKSPACE;
   const int64_t esize = dtype == TSEL_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0) return TSEL_ERR_UNSUPPORTED;
   const int S = tsel::verify_chunks(vocab, dtype);
-  char *ws = static_cast<char *>(workspace);
-  uint64_t *partials = reinterpret_cast<uint64_t *>(ws);
-  uint32_t *counters =
-      reinterpret_cast<uint32_t *>(ws + align16(verify_partial_bytes(batch, k, vocab)));
   hipError_t e = tsel::launch_verify(logits, dtype, batch, k, vocab, row_stride * esize, S,
                                      candidates, out_n_match, out_tokens, out_next, out_k,
-                                     partials, counters, static_cast<hipStream_t>(stream));
+                                     static_cast<uint64_t *>(workspace),
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 
@@ -566,8 +607,7 @@ tsel_status tsel_verify_noalloc(const void *logits, int32_t dtype, int32_t batch
   const int64_t esize = dtype == TSEL_BF16 ? 2 : 4;
   hipError_t e = tsel::launch_verify_noalloc(
       logits, dtype, batch, k, vocab, row_stride * esize, tsel::verify_chunks(vocab, dtype),
-      verify_partial_bytes(batch, k, vocab), candidates, out_n_match, out_tokens, out_next, out_k,
-      static_cast<hipStream_t>(stream));
+      candidates, out_n_match, out_tokens, out_next, out_k, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 

@@ -71,6 +71,7 @@ struct SelectArgs {
   const float *uniforms;
   int32_t *out_tokens;
   float *out_processed;
+  float *out_logprobs;      // the token's log-probability, when the kernel computes it
   const uint32_t *bad_mask, *sup_mask, *begin_mask;
   float rep;
   int32_t ngram;
@@ -114,7 +115,9 @@ size_t beam_rows_lds(int32_t V);
 hipError_t launch_beam(const BeamArgs &a, hipStream_t s);
 
 hipError_t launch_greedy(const SelectArgs &a, size_t lds, hipStream_t s);
-hipError_t launch_topk(const SelectArgs &a, size_t lds, hipStream_t s);
+// af: the full path's layout of the same call, for rows whose ties
+// overflow the candidate buffer; lds covers both layouts
+hipError_t launch_topk(const SelectArgs &a, const SelectArgs &af, size_t lds, hipStream_t s);
 // pending != 0: only rows whose token an earlier kernel left as pending
 hipError_t launch_full(const SelectArgs &a, int res, size_t lds, hipStream_t s, int pending);
 // sampling without top_k at temperature 1, row held in `res` chunks per lane
@@ -137,7 +140,7 @@ hipError_t launch_vsel_match(const int32_t *sel, int32_t B, int32_t k, const int
 hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k, int32_t V,
                          int64_t row_bytes, int32_t chunks, const int32_t *cand,
                          int32_t *n_match, int32_t *tokens, int32_t *next, int32_t *k_out,
-                         uint64_t *partials, uint32_t *counters, hipStream_t s);
+                         uint64_t *partials, hipStream_t s);
 int verify_chunks(int32_t V, int32_t dtype);
 
 // tsel_verify_noalloc: scratch of at most this many bytes per device, for
@@ -146,8 +149,8 @@ constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
 constexpr int kNoAllocDevices = 64;
 hipError_t launch_verify_noalloc(const void *logits, int32_t dtype, int32_t B, int32_t k,
                                  int32_t V, int64_t row_bytes, int32_t chunks,
-                                 size_t partial_bytes, const int32_t *cand, int32_t *n_match,
-                                 int32_t *tokens, int32_t *next, int32_t *k_out, hipStream_t s);
+                                 const int32_t *cand, int32_t *n_match, int32_t *tokens,
+                                 int32_t *next, int32_t *k_out, hipStream_t s);
 
 hipError_t launch_exp2_monotone(uint32_t k0, uint32_t k1, unsigned long long *violations,
                                 hipStream_t s);

@@ -220,6 +220,65 @@ def c5_select(seed: int = 1005, batch: int = 1024) -> SelectWorkload:
                           uniforms(g_u, B))
 
 
+@dataclass
+class BeamWorkload:
+    """One beam-search step: num_beams rows per prompt, prompt p owning rows
+    p * num_beams .. (p + 1) * num_beams - 1."""
+    name: str
+    logits: np.ndarray            # [P * num_beams, V] float32, or uint16 bf16 bits
+    history: np.ndarray           # [P * num_beams, H] int32
+    lens: np.ndarray
+    prompt_lens: np.ndarray
+    max_lengths: np.ndarray
+    settings: Dict
+    num_beams: int
+    beam_scores: np.ndarray       # [P * num_beams] float32
+
+
+def c3_beam(seed: int = 1006, num_beams: int = 4) -> BeamWorkload:
+    """The C3 batch read as 64 prompts x 4 beams: the same logits, histories
+    and static masks, one eos id (so K = 8 candidates per prompt), and beam
+    scores uniform in [-8, 0)."""
+    w = c3_select(seed)
+    (g_b,) = _streams(seed + 100, 1)
+    settings = {k: v for k, v in w.settings.items()
+                if k in ("repetition_penalty", "suppress_tokens", "bad_words_ids")}
+    settings["eos_token_ids"] = [2]
+    bs = (-8.0 * g_b.random(w.batch)).astype(np.float32)
+    return BeamWorkload("C3-beam", w.logits, w.history, w.lens, w.prompt_lens, w.max_lengths,
+                        settings, num_beams, bs)
+
+
+@dataclass
+class VerifySelectWorkload:
+    """Verification with the selection of the step at every position."""
+    name: str
+    logits: np.ndarray            # [B, k+1, V] float32 or uint16 bf16 bits
+    candidates: np.ndarray        # [B, k] int32
+    history: np.ndarray           # [B, H] int32
+    lens: np.ndarray
+    prompt_lens: np.ndarray
+    max_lengths: np.ndarray
+    settings: Dict
+    uniforms: Optional[np.ndarray]  # [B, k+1] float32, sampling only
+
+
+def c4_verify_select(seed: int = 1007) -> VerifySelectWorkload:
+    """The C4 shape ([32, 9, 151936] bf16 ~N(0,3), drafts planted as the
+    position's argmax with probability 0.8) sampled at temperature 0.7 with
+    top_p 0.9 and repetition penalty 1.1 over 256 uniform history ids."""
+    v = c4_verify(seed)
+    g_h, g_u = _streams(seed + 100, 2)
+    B, K1, V = v.logits.shape
+    L = 256
+    h = g_h.integers(0, V, size=(B, L)).astype(np.int32)
+    settings = dict(repetition_penalty=1.1, do_sample=True, temperature=0.7, top_p=0.9)
+    return VerifySelectWorkload("C4-sampled", v.logits, v.candidates, h,
+                                np.full(B, L, np.int32), np.full(B, L, np.int32),
+                                np.full(B, LARGE_MAX_LENGTH, np.int32), settings,
+                                uniforms(g_u, B * K1).reshape(B, K1))
+
+
 # --------------------------------------------------------------------------
 # Small random cases for rule and edge coverage.
 

@@ -70,6 +70,6 @@ def upload_verify(w: synth.VerifyWorkload):
         logits = torch.from_numpy(host).to(dev)
         dtype = tsel.TSEL_F32
     cand = torch.from_numpy(np.ascontiguousarray(w.candidates, dtype=np.int32)).to(dev)
-    ws = torch.zeros(max(tsel.verify_workspace_size(B, K1 - 1, V), 16), dtype=torch.uint8,
+    ws = torch.empty(max(tsel.verify_workspace_size(B, K1 - 1, V), 16), dtype=torch.uint8,
                      device=dev)
     return dict(logits=logits, cand=cand, ws=ws, dtype=dtype, V=V, stride=stride)

@@ -86,8 +86,11 @@ def compare_select(w: synth.SelectWorkload, gpu: dict, ora: dict, rows=None,
             # a low-margin row may keep a different top_p set (see the kept
             # sets below); its log-probability must then be the log-softmax
             # of the GPU's own kept scores at the token
-            own = (low and check_processed
-                   and logprobs_agree(gpu["logprob"][b], logprob_of(gpu["processed"][b], g)))
+            if check_processed:
+                own = low and logprobs_agree(gpu["logprob"][b], logprob_of(gpu["processed"][b], g))
+            else:  # (without the GPU's kept set: any count the margin allows)
+                own = low and any(logprobs_agree(gpu["logprob"][b], c) for c in logprob_over_prefixes(
+                    w, b, g, int(ora["keep_min"][i]), int(ora["keep_max"][i])))
             if not own:
                 rep["logprob_mismatch"].append((b, float(gpu["logprob"][b]),
                                                 float(ora["logprob"][i])))
@@ -110,6 +113,29 @@ def logprob_of(row: np.ndarray, t: int) -> np.float32:
         return np.float32(np.nan)
     m = x[fin].max()
     return np.float32((x[t] - m) - np.log(np.sum(np.exp(x[fin] - m))))
+
+
+def logprob_over_prefixes(w: synth.SelectWorkload, b: int, t: int, keep_min: int,
+                          keep_max: int) -> list:
+    """The log-probability of token t of row b over each kept set a top_p
+    boundary within the margin allows: the first k final scores in (score
+    desc, id asc) order, keep_min <= k <= keep_max, from the oracle's scores
+    before the top_p cut, in binary64."""
+    cfg = oracle.Config(**dict(w.settings, top_p=1.0))
+    r = oracle.select(w.logits, w.history, w.lens, w.prompt_lens, w.max_lengths, cfg,
+                      uniforms=w.uniforms, rows=[b], want_processed=True)
+    x = r["processed"][0].astype(np.float64)
+    fin = np.flatnonzero(np.isfinite(x))
+    if fin.size == 0:
+        return []
+    order = fin[np.lexsort((fin, -x[fin]))]
+    m = x[order[0]]
+    cs = np.cumsum(np.exp(x[order] - m))
+    pos = {int(v): k for k, v in enumerate(order)}
+    if t not in pos:
+        return []
+    return [np.float32((x[t] - m) - np.log(cs[k - 1]))
+            for k in range(max(keep_min, pos[t] + 1), min(keep_max, order.size) + 1)]
 
 
 def logprobs_agree(g: float, o: float) -> bool:

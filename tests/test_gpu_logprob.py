@@ -75,3 +75,23 @@ def test_logprobs_benchmark_batch():
     (and the final scores, against which a row whose top_p set may differ
     from the oracle's at its boundary is checked)."""
     _assert_select(synth.c3_select(), processed=True, logprobs=True)
+
+
+@pytest.mark.parametrize("dtype,V,s", PATHS)
+def test_logprobs_from_the_selection_kernels(dtype, V, s):
+    """Without the final scores: the kernels take the log-probability from
+    what the selection already holds (value-bin counts, the candidates, a
+    pass over the kept scores) rather than from a written row."""
+    _assert_select(_work(800 + V, dtype, V, s), processed=False, logprobs=True)
+
+
+def test_logprobs_benchmark_batch_from_the_kernel():
+    """The B=256, V=128256 bf16 batch without the final scores, as the
+    benchmark times it."""
+    _assert_select(synth.c3_select(), processed=False, logprobs=True)
+
+
+def test_logprobs_top_k_batch_from_the_kernel():
+    """The B=64, V=32000 bf16 top_k batch (candidate buffer) without the
+    final scores."""
+    _assert_select(synth.c2_select(), processed=False, logprobs=True)

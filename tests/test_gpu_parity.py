@@ -375,7 +375,8 @@ def test_verify_named(maker):
     gpu = harness.run_gpu_verify(w, d)
     ora = oracle.verify(w.logits, w.candidates, threads=8)
     assert harness.compare_verify(gpu, ora) == []
-    # a second call on the same workspace (the counters must be clear again)
+    # a second call on a workspace full of stale bytes: no state carries over
+    d["ws"].fill_(0xAB)
     gpu2 = harness.run_gpu_verify(w, d)
     assert harness.compare_verify(gpu2, ora) == []
 
