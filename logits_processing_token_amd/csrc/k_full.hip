@@ -455,7 +455,7 @@ __device__ __forceinline__ void full_row(const SelectArgs &a, int row, unsigned 
   }
   RowInfo ri;
   if (row_prologue(a, row, ri)) return;
-  stage_row<DT>(a, row, ri, s, sh);
+  stage_row<DT>(a, row, ri, s, sh, !want_res);
   const bool dense_pen = sh.dense_pen != 0;
   const int n_list = sh.n_list;
   uint64_t kcut = 0ull;
@@ -583,13 +583,23 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
   const int tid = threadIdx.x, row = blockIdx.x, V = a.V;
   RowInfo ri;
   if (row_prologue(a, row, ri)) return;
-  stage_row<DT>(a, row, ri, s, sh);
   const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  const int NG = V / EPC;
+  // every lane's first chunk and the stream's first batch fly while the
+  // history is staged
+  uint4 c0 = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < NG) c0 = load16(rowp + (int64_t)tid * 16);
+  uint4 c[U], nx[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = NT + tid + u * NT;
+    if (g < NG) c[u] = load16(rowp + (int64_t)g * 16);
+  }
+  stage_row<DT>(a, row, ri, s, sh);
   const bool dense_pen = sh.dense_pen != 0;
   const int n_list = sh.n_list;
   const float T = a.temperature;
   const int k_eff = min(a.top_k, V);
-  const int NG = V / EPC;
   const int tcap = a.tcap;
   float *cx = reinterpret_cast<float *>(s.area);
   int32_t *ci = reinterpret_cast<int32_t *>(s.area + 4 * tcap);
@@ -610,8 +620,7 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
   };
   // Threshold from the first chunk of every lane: the k-th largest alive
   // score among them, a lower bound of the row's.
-  uint4 c0 = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < NG) c0 = kill_chunk<DT>(load16(rowp + (int64_t)tid * 16), tid, s);
+  if (tid < NG) c0 = kill_chunk<DT>(c0, tid, s);
   const uint32_t t0 = radix_kth_largest(
       [&](auto &&f) {
         if (tid < NG)
@@ -634,12 +643,13 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
   for (int i = tid; i < n_list; i += NT)
     if (s.list_val[i] >= flt) append(s.list_id[i], s.list_val[i]);
   __syncthreads();
+  // Two batches of U chunks per lane: the next batch's loads fly while this
+  // one is filtered (the barrier after it waits for LDS work only).
   for (int t0g = NT; t0g < NG && !sh.overflow; t0g += NT * U) {
-    uint4 c[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int g = t0g + tid + u * NT;
-      if (g < NG) c[u] = load16(rowp + (int64_t)g * 16);
+      const int g = t0g + NT * U + tid + u * NT;
+      if (g < NG) nx[u] = load16(rowp + (int64_t)g * 16);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -653,7 +663,9 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
         }
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] = nx[u];
+    lds_barrier();
     if (!sh.overflow && sh.count > tcap / 2) {
       // Prune: the new threshold is the k-th largest in the buffer.
       const int cnt = sh.count;
@@ -734,32 +746,59 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
     const double m = (double)key_score(keys[0]);
     for (int i = tid; i < nk; i += NT) w[i] = exp((double)key_score(keys[i]) - m);
     __syncthreads();
-    if (tid == 0) {
+    // The top_p cut and the draw by wave 0 over the ordered candidates, 64
+    // at a time: binary64 prefix sums by row moves, a ballot naming the
+    // first candidate that meets each condition.
+    if (tid < kWave) {
+      const int lane = tid;
+      auto wv = [&](int j, int n) { return j < n ? w[j] : 0.0; };
+      auto excl_of = [&](double incl, double carry) {  // the lane before's inclusive sum
+        const double prev = __shfl_up(incl, 1, kWave);
+        return lane == 0 ? carry : prev;
+      };
       double W = 0.0;
-      for (int j = 0; j < nk; ++j) W += w[j];
+      for (int b0 = 0; b0 < nk; b0 += kWave) W += wave_sum_f64(wv(b0 + lane, nk));
+      // K: candidates are kept while the mass before them is below top_p of W
       int K = nk;
+      double Wp = W;
       if (a.top_p < 1.0f) {
-        double run = 0.0;
-        K = 0;
-        for (int j = 0; j < nk; ++j) {
-          if (run / W < (double)a.top_p) K = j + 1;
-          run += w[j];
+        const double p = (double)a.top_p;
+        double carry = 0.0;
+        for (int b0 = 0; b0 < nk; b0 += kWave) {
+          const int j = b0 + lane;
+          const double incl = carry + wave_incl_scan_f64_dpp(wv(j, nk));
+          const double excl = excl_of(incl, carry);
+          const uint64_t stop = __ballot(j < nk && !(excl / W < p));
+          if (stop) {
+            const int q = __ffsll((unsigned long long)stop) - 1;
+            K = b0 + q;
+            Wp = __shfl(excl, q, kWave);
+            break;
+          }
+          carry = __shfl(incl, kWave - 1, kWave);
         }
       }
-      double Wp = 0.0;
-      for (int j = 0; j < K; ++j) Wp += w[j];
+      // the draw: the first kept candidate whose mass through it exceeds u Wp
       const double target = (double)a.uniforms[row] * Wp;
-      double C = 0.0;
       int pick = K - 1;
-      for (int j = 0; j < K; ++j) {
-        C += w[j];
-        if (C > target) { pick = j; break; }
+      double carry = 0.0;
+      for (int b0 = 0; b0 < K; b0 += kWave) {
+        const int j = b0 + lane;
+        const double incl = carry + wave_incl_scan_f64_dpp(wv(j, K));
+        const uint64_t hit = __ballot(j < K && incl > target);
+        if (hit) {
+          pick = b0 + __ffsll((unsigned long long)hit) - 1;
+          break;
+        }
+        carry = __shfl(incl, kWave - 1, kWave);
       }
-      sh.token = (int)key_index(keys[pick]);
-      sh.kcut = (K < nk) ? keys[K - 1] : 0ull;
-      // the log-softmax of the kept scores at the token ("Log-probabilities")
-      if (a.out_logprobs)
-        a.out_logprobs[row] = (float)(((double)key_score(keys[pick]) - m) - log(Wp));
+      if (lane == 0) {
+        sh.token = (int)key_index(keys[pick]);
+        sh.kcut = (K < nk) ? keys[K - 1] : 0ull;
+        // the log-softmax of the kept scores at the token ("Log-probabilities")
+        if (a.out_logprobs)
+          a.out_logprobs[row] = (float)(((double)key_score(keys[pick]) - m) - log(Wp));
+      }
     }
     __syncthreads();
     kcut = sh.kcut;

@@ -13,7 +13,8 @@ namespace tsel {
 
 constexpr int NT = kSelectThreads;
 constexpr int NW = NT / kWave;
-constexpr int U = 8;                 // 16-byte chunks in flight per lane when streaming
+constexpr int U = 4;                 // 16-byte chunks per lane per batch when streaming
+                                     // (two batches: one consumed, one in flight)
 constexpr uint32_t kNoDigit = 0xFFFFFFFFu;
 constexpr int kPending = -2;         // token marker: row left for k_full
 constexpr float kLog2e = 1.4426950408889634f;
@@ -282,9 +283,13 @@ __device__ __forceinline__ bool row_prologue(const SelectArgs &a, int row, RowIn
 // Staging of one row (see the file comment).  Leaves in LDS: the kill mask
 // (seen ids included unless dense_pen), the seen mask, the list of
 // (id, penalized logit) and the kill-mask table.
+// prefer_dense: the caller streams the row anyway, so the penalty may be
+// applied in the stream (from the seen mask) rather than to gathered scores
+// whenever the seen ids would touch a large share of the row's cache lines
+// (a gather pulls a whole line for one score).
 template <int DT>
 __device__ __forceinline__ void stage_row(const SelectArgs &a, int row, const RowInfo &ri, const Lds &s,
-                          RowShared &sh) {
+                          RowShared &sh, bool prefer_dense = true) {
   using E = Elem<DT>;
   constexpr int EPC = E::EPC;
   const int tid = threadIdx.x;
@@ -318,21 +323,35 @@ __device__ __forceinline__ void stage_row(const SelectArgs &a, int row, const Ro
   }
   __syncthreads();
   const int32_t *h = a.hist + (int64_t)row * a.hist_stride;
-  for (int i = tid; i < L; i += NT) {
-    const int v = h[i];
-    if (v >= 0 && v < V) atomicOr(&s.smask[v >> 5], 1u << (v & 31));
-  }
+  // Seen ids and n-gram windows in batches of kHB ids per thread, every
+  // load of a batch in flight at once.  Window i bans its last id when its
+  // first n-1 ids equal the last n-1 ids of the history ("Lengths",
+  // no_repeat_ngram_size); its first id, already loaded, rules most windows
+  // out.
+  constexpr int kHB = 8;
   const int n = a.ngram;
-  if (n > 0 && L >= n) {
-    // Window i bans its last id when its first n-1 ids equal the last n-1
-    // ids of the history ("Lengths", no_repeat_ngram_size).
-    const int32_t *tail = h + (L - n + 1);
-    for (int i = tid; i + n <= L; i += NT) {
-      bool match = true;
-      for (int j = 0; j < n - 1; ++j)
-        if (h[i + j] != tail[j]) { match = false; break; }
-      const int t = h[i + n - 1];
-      if (match && t >= 0 && t < V) atomicOr(&s.kmask[t >> 5], 1u << (t & 31));
+  const bool ngram = n > 0 && L >= n;
+  const int32_t *tail = h + (L - n + 1);
+  const int tail0 = ngram && n > 1 ? tail[0] : 0;
+  for (int base = 0; base < L; base += NT * kHB) {
+    int hv[kHB];
+#pragma unroll
+    for (int k = 0; k < kHB; ++k) {
+      const int i = base + k * NT + tid;
+      hv[k] = i < L ? h[i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kHB; ++k) {
+      const int i = base + k * NT + tid;
+      const int v = hv[k];
+      if (v >= 0 && v < V) atomicOr(&s.smask[v >> 5], 1u << (v & 31));
+      if (ngram && i + n <= L && (n == 1 || v == tail0)) {
+        bool match = true;
+        for (int j = 1; j < n - 1; ++j)
+          if (h[i + j] != tail[j]) { match = false; break; }
+        const int t = h[i + n - 1];
+        if (match && t >= 0 && t < V) atomicOr(&s.kmask[t >> 5], 1u << (t & 31));
+      }
     }
   }
   const bool minlen_active = a.min_new > 0 ? (ri.new_tokens < a.min_new)
@@ -358,7 +377,7 @@ __device__ __forceinline__ void stage_row(const SelectArgs &a, int row, const Ro
   }
   int n_seen = 0;
   const int my_off = block_excl_scan_i32<NT>(my_cnt, sh.red_i32, &n_seen);
-  const bool dense_pen = n_seen > a.lcap - 8;
+  const bool dense_pen = n_seen > a.lcap - 8 || (prefer_dense && (int64_t)n_seen * 64 > NG);
   if (!dense_pen) {
     int o = my_off;
     for (int q = 0; q < wpt; ++q) {
@@ -387,11 +406,21 @@ __device__ __forceinline__ void stage_row(const SelectArgs &a, int row, const Ro
   if (!dense_pen)  // the stream kills seen ids; the list carries them
     for (int w = tid; w < mw; w += NT) s.kmask[w] |= s.smask[w];
   const int n_list = sh.n_list;
-  for (int i = tid; i < n_list; i += NT) {
-    const int v = s.list_id[i];
-    float x = E::load1(rowp, v);
-    if (bit_of(s.smask, v)) x = penalize(x, a.rep);
-    s.list_val[i] = x;
+  for (int base = 0; base < n_list; base += NT * kHB) {  // (gathers in flight together)
+    float xv[kHB];
+#pragma unroll
+    for (int k = 0; k < kHB; ++k) {
+      const int i = base + k * NT + tid;
+      xv[k] = i < n_list ? E::load1(rowp, s.list_id[i]) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kHB; ++k) {
+      const int i = base + k * NT + tid;
+      if (i < n_list) {
+        const int v = s.list_id[i];
+        s.list_val[i] = bit_of(s.smask, v) ? penalize(xv[k], a.rep) : xv[k];
+      }
+    }
   }
   __syncthreads();
 }
@@ -405,12 +434,19 @@ __device__ __forceinline__ void stream_row(const SelectArgs &a, const char *rowp
   using E = Elem<DT>;
   constexpr int EPC = E::EPC;
   const int NG = a.V / EPC;
+  // two batches of U chunks: the next batch's loads fly while this one is
+  // consumed
+  uint4 c[U], nx[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = threadIdx.x + u * NT;
+    if (g < NG) c[u] = load16(rowp + (int64_t)g * 16);
+  }
   for (int g0 = threadIdx.x; g0 < NG; g0 += NT * U) {
-    uint4 c[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int g = g0 + u * NT;
-      if (g < NG) c[u] = load16(rowp + (int64_t)g * 16);
+      const int g = g0 + NT * U + u * NT;
+      if (g < NG) nx[u] = load16(rowp + (int64_t)g * 16);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -426,6 +462,8 @@ __device__ __forceinline__ void stream_row(const SelectArgs &a, const char *rowp
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] = nx[u];
   }
 }
 

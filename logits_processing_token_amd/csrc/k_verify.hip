@@ -83,23 +83,35 @@ __global__ __launch_bounds__(VT) void k_verify_part(const char *logits, int64_t 
   }
 }
 
-// One wave per batch row b: merge each position's chunk keys, then the
-// left-to-right comparison (it stops at the first mismatch).
+// One wave per batch row b: merge each position's chunk keys (lane j takes
+// position j, its S loads in flight together), then compare every draft with
+// its position's token at once; the first mismatch ends the matches.
 __global__ __launch_bounds__(kWave) void k_verify_merge(int k, int S, const int32_t *cand,
                                                         const uint64_t *partials,
                                                         int32_t *n_match, int32_t *tokens,
                                                         int32_t *next, int32_t *k_out) {
   __shared__ int sel[kMaxVerifyK + 1];
+  __shared__ int first_miss;
   const int b = blockIdx.x, lane = threadIdx.x;
+  if (lane == 0) first_miss = k;
   for (int j = lane; j <= k; j += kWave) {
-    uint64_t m = 0ull;
     const uint64_t *p = partials + ((int64_t)b * (k + 1) + j) * S;
-    for (int q = 0; q < S; ++q) m = p[q] > m ? p[q] : m;
+    uint64_t m = 0ull;
+    int q = 0;
+    for (; q + 4 <= S; q += 4) {  // (four independent loads at a time)
+      const uint64_t a0 = p[q], a1 = p[q + 1], a2 = p[q + 2], a3 = p[q + 3];
+      const uint64_t x = a0 > a1 ? a0 : a1, y = a2 > a3 ? a2 : a3;
+      const uint64_t z = x > y ? x : y;
+      m = z > m ? z : m;
+    }
+    for (; q < S; ++q) m = p[q] > m ? p[q] : m;
     sel[j] = m == 0ull ? 0 : (int)key_index(m);  // every score -inf: the lowest id
   }
   __syncthreads();
-  int nm = 0;
-  while (nm < k && cand[(int64_t)b * k + nm] == sel[nm]) ++nm;  // (every lane alike)
+  for (int j = lane; j < k; j += kWave)
+    if (cand[(int64_t)b * k + j] != sel[j]) atomicMin(&first_miss, j);
+  __syncthreads();
+  const int nm = first_miss;  // drafts before the first mismatch are accepted
   if (lane == 0) {
     n_match[b] = nm;
     next[b] = sel[nm];
