@@ -13,11 +13,12 @@
 // then e ascending), so the best K are the K largest keys.  No key is 0, which
 // marks "no candidate".
 //
-//  * k_beam_rows, one workgroup per beam row: the row's largest logit m and
-//    log(sum exp(x - m)) in binary64 (a running pair per lane, joined at the
-//    row's maximum); the seen and removed ids as two bitmasks in LDS; then the
-//    row's best K keys, scores recomputed from the logits on every pass (the
-//    row stays in L2 and nothing of size V is written).
+//  * k_beam_rows, one workgroup per beam row: the row's largest logit m (one
+//    pass) and log(sum exp(x - m)) in binary64 (a second pass, exp_nonpos
+//    for the terms); the seen and
+//    removed ids as two bitmasks in LDS; then the row's best K keys, scores
+//    recomputed from the logits on every pass (16-byte loads; the row stays
+//    in L2 and nothing of size V is written).
 //  * k_beam_merge, one workgroup per prompt: the best K of its num_beams * K
 //    row keys, written as score, beam and id.
 //
@@ -54,13 +55,39 @@ __device__ __forceinline__ bool has_bit(const uint32_t *m, int v) {
   return (m[v >> 5] >> (v & 31)) & 1u;
 }
 
-// The largest min(K, present keys) of key(0..n) (0 = absent), each passed to
-// emit(rank, key), rank 0 the largest; returns how many.  Every thread of
-// the workgroup calls.  hist: kBeamSelBins words; cand: kSelCap keys.
-template <class KeyFn, class EmitFn>
-__device__ int select_top(int64_t n, int K, KeyFn key, EmitFn emit, uint32_t *hist,
-                          uint64_t *cand, SelShared &ss) {
+// The largest min(K, present keys) of the keys visit(f) passes to f, one
+// call per key and thread (0 = absent), each passed to emit(rank, key), rank
+// 0 the largest; returns how many.  Every thread of the workgroup calls.
+// hist: kBeamSelBins words; cand: kSelCap keys.
+// direct: first gather every key on chip in one pass, ranked there when
+// they number at most kSelCap (else the radix passes follow).
+template <class Visit, class EmitFn>
+__device__ __forceinline__ int select_top(int K, Visit visit, EmitFn emit, uint32_t *hist,
+                                          uint64_t *cand, SelShared &ss, bool direct = false) {
   const int tid = threadIdx.x;
+  if (direct) {
+    if (tid == 0) ss.nc = 0;
+    __syncthreads();
+    visit([&](uint64_t k) {
+      if (k != 0ull) {
+        const int slot = atomicAdd(&ss.nc, 1);
+        if (slot < kSelCap) cand[slot] = k;
+      }
+    });
+    __syncthreads();
+    const int nc = ss.nc;
+    __syncthreads();  // (ss is written again below)
+    if (nc <= kSelCap) {
+      const int keff = nc < K ? nc : K;
+      for (int j = tid; j < nc; j += kBT) {
+        const uint64_t kj = cand[j];
+        int r = 0;
+        for (int q = 0; q < nc; ++q) r += cand[q] > kj;
+        if (r < keff) emit(r, kj);
+      }
+      return keff;
+    }
+  }
   uint64_t prefix = 0ull, pmask = 0ull;
   int need = 0, above = 0, keff = 0;
   for (int pass = 0; pass < 5; ++pass) {
@@ -69,10 +96,9 @@ __device__ int select_top(int64_t n, int K, KeyFn key, EmitFn emit, uint32_t *hi
     const int nbins = 1 << width;
     for (int d = tid; d < nbins; d += kBT) hist[d] = 0u;
     __syncthreads();
-    for (int64_t e = tid; e < n; e += kBT) {
-      const uint64_t k = key(e);
+    visit([&](uint64_t k) {
       if (k != 0ull && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (nbins - 1)], 1u);
-    }
+    });
     __syncthreads();
     // thread t holds bins top, top-1, ..., the t-th group from the top
     const int per = nbins / kBT;
@@ -111,13 +137,12 @@ __device__ int select_top(int64_t n, int K, KeyFn key, EmitFn emit, uint32_t *hi
   }
   // the keys at or above the prefix: `above` with a larger prefix, then the
   // ones sharing it, the keff-th largest among them
-  for (int64_t e = tid; e < n; e += kBT) {
-    const uint64_t k = key(e);
+  visit([&](uint64_t k) {
     if (k != 0ull && (k & pmask) >= prefix) {
       const int slot = atomicAdd(&ss.nc, 1);
       if (slot < kSelCap) cand[slot] = k;
     }
-  }
+  });
   __syncthreads();
   const int nc = ss.nc < kSelCap ? ss.nc : kSelCap;
   for (int j = tid; j < nc; j += kBT) {
@@ -127,6 +152,53 @@ __device__ int select_top(int64_t n, int K, KeyFn key, EmitFn emit, uint32_t *hi
     if (r < keff) emit(r, kj);
   }
   return keff;
+}
+
+// f(v, x) for every element v of a row (16-byte rows: whole chunks of 8
+// bf16 or 4 fp32 per load, then the tail), x widened to binary32.  Two
+// batches of four chunks per lane: the next batch's loads fly while this one
+// is consumed.
+constexpr int kVB = 4;
+template <class F>
+__device__ __forceinline__ void visit_row(const char *rowp, bool bf16, int V, F &&f) {
+  const int tid = threadIdx.x;
+  const int epc = bf16 ? 8 : 4;
+  const int NG = V / epc;
+  auto consume = [&](const uint4 &c, int g) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    if (bf16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        f(g * 8 + j, (j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
+                             : __uint_as_float(w[j >> 1] << 16));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f(g * 4 + j, __uint_as_float(w[j]));
+    }
+  };
+  uint4 c[kVB], nx[kVB];
+#pragma unroll
+  for (int u = 0; u < kVB; ++u) {
+    const int g = tid + u * kBT;
+    if (g < NG) c[u] = *reinterpret_cast<const uint4 *>(rowp + (int64_t)g * 16);
+  }
+  for (int g0 = tid; g0 < NG; g0 += kBT * kVB) {
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int g = g0 + kBT * kVB + u * kBT;
+      if (g < NG) nx[u] = *reinterpret_cast<const uint4 *>(rowp + (int64_t)g * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int g = g0 + u * kBT;
+      if (g < NG) consume(c[u], g);
+    }
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) c[u] = nx[u];
+  }
+  for (int v = NG * epc + tid; v < V; v += kBT)
+    f(v, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
+              : reinterpret_cast<const float *>(rowp)[v]);
 }
 
 }  // namespace
@@ -147,29 +219,48 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   }
   const char *rowp = s.logits + (int64_t)r * s.row_bytes;
   const bool bf16 = s.dtype == 1;
-  auto load = [&](int v) -> float {
-    return bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
-                : reinterpret_cast<const float *>(rowp)[v];
-  };
   const int mw = (V + 31) / 32;
   uint32_t *seen = bsm, *kill = bsm + mw;
   uint32_t *hist = bsm + ((2 * mw + 3) & ~3);
   uint64_t *cand = reinterpret_cast<uint64_t *>(hist + kBeamSelBins);
   for (int w = tid; w < 2 * mw; w += kBT) bsm[w] = 0u;
-  // the log-softmax's shift and sum, in binary64
-  double m = -INFINITY, sum = 0.0;
-  for (int v = tid; v < V; v += kBT) {
-    const double x = (double)load(v);
-    if (!(x > -INFINITY)) continue;
-    if (x > m) {
-      sum = sum * exp(m - x) + 1.0;
-      m = x;
-    } else {
-      sum += exp(x - m);
-    }
+  // The log-softmax's shift M (the row's largest finite logit) and sum S =
+  // sum exp(x - M), in binary64, in one pass: the terms are taken against
+  // M0, the largest logit of every lane's first chunk, and the sum is
+  // rescaled by exp(M0 - M) once M is known (one more rounding).  Should
+  // some logit lie more than 700 above M0 (a term could overflow), a second
+  // pass takes the terms against M itself.
+  const int epc0 = bf16 ? 8 : 4;
+  float m0 = -INFINITY;
+  if (tid < V / epc0) {
+    const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    for (int j = 0; j < epc0; ++j)
+      m0 = fmaxf(m0, bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
+                                     : __uint_as_float(w[j >> 1] << 16))
+                          : __uint_as_float(w[j]));
   }
-  const float Mx = block_max_f32<kBT>((float)m, rmax);
-  const double S = block_sum_f64<kBT>(m > -INFINITY ? sum * exp(m - (double)Mx) : 0.0, rsum);
+  for (int v = (V / epc0) * epc0 + tid; v < V; v += kBT)  // (the row tail)
+    m0 = fmaxf(m0, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
+                        : reinterpret_cast<const float *>(rowp)[v]);
+  const float M0 = block_max_f32<kBT>(m0, rmax);
+  float mloc = -INFINITY;
+  double sum = 0.0;
+  const double dM0 = M0 > -INFINITY ? (double)M0 : 0.0;
+  visit_row(rowp, bf16, V, [&](int, float x) {  // (-inf adds 0)
+    mloc = fmaxf(mloc, x);
+    const double d = (double)x - dM0;
+    sum += d <= 0.0 ? exp_nonpos(d) : exp(fmin(d, 710.0));
+  });
+  const float Mx = block_max_f32<kBT>(mloc, rmax);
+  double S;
+  if (Mx > -INFINITY && (double)Mx - dM0 > 700.0) {  // (rare: far above the first chunks)
+    sum = 0.0;
+    visit_row(rowp, bf16, V, [&](int, float x) { sum += exp_nonpos((double)x - (double)Mx); });
+    S = block_sum_f64<kBT>(sum, rsum);
+  } else {
+    S = block_sum_f64<kBT>(sum, rsum) * (Mx > -INFINITY ? exp(dM0 - (double)Mx) : 1.0);
+  }
   // (the reductions' barriers order the clearing of the masks)
   const int new_tokens = L - P;
   const bool begin_active =
@@ -218,27 +309,116 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   const float lsf = any ? (float)log(S) : 0.0f;
   const float s_beam = a.beam_scores[r];
   const uint32_t flat0 = (uint32_t)beam * (uint32_t)V;
-  auto key = [&](int64_t e) -> uint64_t {
-    const int v = (int)e;
+  // A candidate's ordered score bits: plain_bits for an id neither removed
+  // nor seen, true_bits for any id (the forced row, the removal, the
+  // penalty); then its key.
+  auto finish = [&](float y) -> uint32_t {
+    float c = y + s_beam;
+    if (!(c >= -FLT_MAX)) c = -FLT_MAX;  // never below the smallest finite value
+    if (c == 0.0f) c = 0.0f;             // (-0 and +0 are one score)
+    return ordered32(c);
+  };
+  auto base = [&](float x) { return (any && x > -INFINITY) ? (x - Mx) - lsf : x; };
+  auto plain_bits = [&](float x) -> uint32_t { return finish(base(x)); };
+  auto true_bits = [&](int v, float x) -> uint32_t {
     float y;
     if (forced >= 0) {
       y = (forced_alive && v == forced) ? 0.0f : -FLT_MAX;
     } else {
-      const float x = load(v);
-      y = (any && x > -INFINITY) ? (x - Mx) - lsf : x;
+      y = base(x);
       if (has_bit(kill, v)) {
         y = -FLT_MAX;
       } else if (s.rep != 1.0f && has_bit(seen, v)) {
         y = penalize(y, s.rep);
       }
     }
-    float c = y + s_beam;
-    if (!(c >= -FLT_MAX)) c = -FLT_MAX;  // never below the smallest finite value
-    if (c == 0.0f) c = 0.0f;             // (-0 and +0 are one score)
-    return ((uint64_t)ordered32(c) << 32) | (uint64_t)(0xFFFFFFFFu - (flat0 + (uint32_t)v));
+    return finish(y);
   };
-  const int keff = select_top(
-      (int64_t)V, K, key, [&](int rank, uint64_t k) { keys_out[rank] = k; }, hist, cand, ss);
+  auto key_of = [&](int v, uint32_t ob) -> uint64_t {
+    return ((uint64_t)ob << 32) | (uint64_t)(0xFFFFFFFFu - (flat0 + (uint32_t)v));
+  };
+  auto emit_row = [&](int rank, uint64_t k) { keys_out[rank] = k; };
+  int keff;
+  if (forced >= 0) {
+    // every id but the forced one scores alike: the best K are among the
+    // forced id and the K lowest others
+    keff = select_top(
+        K,
+        [&](auto &&f) {
+          for (int v = tid; v <= K && v < V; v += kBT)
+            if (v != forced) f(key_of(v, true_bits(v, 0.0f)));
+          if (tid == 0 && forced < V) f(key_of(forced, true_bits(forced, 0.0f)));
+        },
+        emit_row, hist, cand, ss);
+  } else {
+    // A lower bound of the row's K-th key: the K-th largest key of a sample,
+    // every lane's first 16-byte chunk.  Only keys at or above it can be
+    // among the row's best K, so the row's select counts those alone (0: the
+    // sample is smaller than K and bounds nothing).
+    __shared__ uint64_t t0_s;
+    if (tid == 0) t0_s = 0ull;
+    const int epc = bf16 ? 8 : 4;
+    const int NGs = V / epc;
+    const int ns = select_top(
+        K,
+        [&](auto &&f) {
+          if (tid < NGs) {
+            const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
+            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+            for (int j = 0; j < epc; ++j) {
+              const float x = bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
+                                              : __uint_as_float(w[j >> 1] << 16))
+                                   : __uint_as_float(w[j]);
+              const int v = tid * epc + j;
+              f(key_of(v, true_bits(v, x)));
+            }
+          }
+        },
+        [&](int rank, uint64_t k) {
+          if (rank == K - 1) t0_s = k;
+        },
+        hist, cand, ss);
+    __syncthreads();
+    const uint64_t t0 = ns == K ? t0_s : 0ull;
+    const uint32_t t0hi = (uint32_t)(t0 >> 32);
+    // The row pass scores every id as plain; removal lowers a score and a
+    // penalty p >= 1 lowers a log-probability (all <= 0), so an id whose
+    // plain key misses the bound misses it truly, and the few that pass are
+    // rescored.  A penalty p < 1 raises the seen ids' scores: those the row
+    // pass dropped are scored again from the seen mask.
+    const bool raise = s.rep < 1.0f;
+    keff = select_top(
+        K,
+        [&](auto &&f) {
+          visit_row(rowp, bf16, V, [&](int v, float x) {
+            const uint32_t ob = plain_bits(x);
+            if (ob >= t0hi) {
+              uint64_t k = key_of(v, ob);
+              if (k >= t0) {
+                if (has_bit(kill, v) || (s.rep != 1.0f && has_bit(seen, v)))
+                  k = key_of(v, true_bits(v, x));
+                if (k >= t0) f(k);
+              }
+            }
+          });
+          if (raise)
+            for (int w = tid; w < mw; w += kBT) {
+              uint32_t bits = seen[w] & ~kill[w];
+              while (bits) {
+                const int v = w * 32 + __ffs(bits) - 1;
+                bits &= bits - 1u;
+                const float x =
+                    bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
+                         : reinterpret_cast<const float *>(rowp)[v];
+                if (key_of(v, plain_bits(x)) < t0) {
+                  const uint64_t k = key_of(v, true_bits(v, x));
+                  if (k >= t0) f(k);
+                }
+              }
+            }
+        },
+        emit_row, hist, cand, ss, true);
+  }
   for (int i = keff + tid; i < K; i += kBT) keys_out[i] = 0ull;
 }
 
@@ -251,15 +431,16 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_merge(BeamArgs a) {
   uint64_t *cand = reinterpret_cast<uint64_t *>(hist + kBeamSelBins);
   float *sc = a.out_scores + (int64_t)p * K;
   int32_t *bm = a.out_beams + (int64_t)p * K, *tk = a.out_tokens + (int64_t)p * K;
+  const int64_t n = (int64_t)a.nb * K;
   const int keff = select_top(
-      (int64_t)a.nb * K, K, [&](int64_t e) { return keys[e]; },
+      K, [&](auto &&f) { for (int64_t e = tid; e < n; e += kBT) f(keys[e]); },
       [&](int rank, uint64_t k) {
         const uint32_t e = 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu);
         sc[rank] = unordered32((uint32_t)(k >> 32));
         bm[rank] = (int32_t)(e / (uint32_t)V);
         tk[rank] = (int32_t)(e % (uint32_t)V);
       },
-      hist, cand, ss);
+      hist, cand, ss, true);
   for (int i = keff + tid; i < K; i += kBT) {  // fewer candidates than slots
     sc[i] = -INFINITY;
     bm[i] = -1;

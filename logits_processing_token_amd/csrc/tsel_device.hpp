@@ -41,6 +41,36 @@ __device__ __forceinline__ float key_score(uint64_t k) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// e^d in binary64 for d <= 0 (-inf included: 0), by Cody and Waite's
+// reduction and a Taylor polynomial: d = k ln2 + r with |r| <= ln2/2 (ln2
+// split in two so that k * ln2_hi is exact), e^r by its Taylor series through
+// r^13 (the next term is below 2^-57 of the sum), scaled by 2^k.  Within a
+// unit in the last place of the exact value; no branch and a third of the
+// operations of the general exp, for sums over every element of a row.
+// (d is clamped at -746, where 2^k underflows to 0.)
+__device__ __forceinline__ double exp_nonpos(double d) {
+  d = fmax(d, -746.0);
+  const double kInvLn2 = 1.4426950408889634074;
+  const double kLn2Hi = 0x1.62e42fee00000p-1, kLn2Lo = 0x1.a39ef35793c76p-33;
+  const double k = rint(d * kInvLn2);
+  const double r = fma(-k, kLn2Lo, fma(-k, kLn2Hi, d));
+  double p = 1.0 / 6227020800.0;             // 1/13!
+  p = fma(p, r, 1.0 / 479001600.0);          // 1/12!
+  p = fma(p, r, 1.0 / 39916800.0);           // 1/11!
+  p = fma(p, r, 1.0 / 3628800.0);            // 1/10!
+  p = fma(p, r, 1.0 / 362880.0);             // 1/9!
+  p = fma(p, r, 1.0 / 40320.0);              // 1/8!
+  p = fma(p, r, 1.0 / 5040.0);               // 1/7!
+  p = fma(p, r, 1.0 / 720.0);                // 1/6!
+  p = fma(p, r, 1.0 / 120.0);                // 1/5!
+  p = fma(p, r, 1.0 / 24.0);                 // 1/4!
+  p = fma(p, r, 1.0 / 6.0);                  // 1/3!
+  p = fma(p, r, 0.5);                        // 1/2!
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)k);
+}
+
 // Repetition penalty of a seen id, as in Python transformers: a negative
 // score is multiplied by p, any other is divided by p (IEEE, round to
 // nearest even; HIP keeps binary32 division correctly rounded by default).
