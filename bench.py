@@ -108,6 +108,26 @@ def select_bytes(w, forced_free: bool = True) -> int:
     return int((~forced).sum()) * per_row + B * scalars + masks
 
 
+# Per workload: the launches of one step (the dominant first), the committed
+# counter summary, and the sources whose hash that summary must match.
+PROFILED = {
+    "C1": (("k_greedy",), "k_greedy_c1_traffic.txt", SELECT_COMMON + (CSRC + "k_greedy.hip",)),
+    "C1v": (("k_verify_part", "k_verify_merge"), "k_verify_c1_traffic.txt",
+            COMMON + (CSRC + "k_verify.hip",)),
+    "C2": (("k_topk",), "k_topk_c2_traffic.txt", SELECT_COMMON + (CSRC + "k_full.hip",)),
+    "C3": (("k_vres",), "k_vres_b256_v128256_traffic.txt",
+           SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp")),
+    "C4": (("k_verify_part", "k_verify_merge"), "k_verify_c4_traffic.txt",
+           COMMON + (CSRC + "k_verify.hip",)),
+    "C5": (("k_topk",), "k_topk_c5_traffic.txt", SELECT_COMMON + (CSRC + "k_full.hip",)),
+    "F1": (("k_vres",), "k_vres_logprob_c3_traffic.txt",
+           SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp")),
+    "F2": (("k_beam_rows", "k_beam_merge"), "k_beam_c3_traffic.txt", COMMON + (CSRC + "k_beam.hip",)),
+    "F3": (("k_full", "k_vsel_expand", "k_vsel_match"), "k_vsel_c4_traffic.txt",
+           SELECT_COMMON + (CSRC + "k_full.hip", CSRC + "k_vsel.hip")),
+}
+
+
 # --------------------------------------------------------------------------
 # One case per workload: device inputs, the step, its bytes, the CPU oracle.
 
@@ -135,12 +155,11 @@ def _copies(nbytes: int) -> int:
 
 
 class SelectCase(Case):
-    def __init__(self, name, w, workload, kernels, traffic_file, sources, rotate=None,
-                 logprobs=False):
+    def __init__(self, name, w, workload, rotate=None, logprobs=False):
         import torch
         from logits_processing_token_amd import tsel, upload
         self.name, self.w, self.workload = name, w, workload
-        self.kernels, self.traffic_file, self.sources = kernels, traffic_file, sources
+        self.kernels, self.traffic_file, self.sources = PROFILED[name]
         self.rows = w.batch
         self.alg_bytes = select_bytes(w) + (4 * w.batch if logprobs else 0)
         d = upload.upload_select(w)
@@ -192,13 +211,11 @@ class SelectCase(Case):
 
 
 class VerifyCase(Case):
-    def __init__(self, name, w, workload, traffic_file, rotate=None):
+    def __init__(self, name, w, workload, rotate=None):
         import torch
         from logits_processing_token_amd import tsel, upload
         self.name, self.w, self.workload = name, w, workload
-        self.kernels = ("k_verify",)
-        self.traffic_file = traffic_file
-        self.sources = COMMON + (CSRC + "k_verify.hip",)
+        self.kernels, self.traffic_file, self.sources = PROFILED[name]
         B, K1, V = w.logits.shape
         self.rows = B
         esize = 2 if w.dtype == "bf16" else 4
@@ -240,14 +257,12 @@ class VerifyCase(Case):
 
 
 class VerifySelectCase(Case):
-    def __init__(self, name, w, workload, traffic_file, rotate=None):
+    def __init__(self, name, w, workload, rotate=None):
         import numpy as np
         import torch
         from logits_processing_token_amd import tsel
         self.name, self.w, self.workload = name, w, workload
-        self.kernels = ("k_full", "k_vsel_expand", "k_vsel_match")
-        self.traffic_file = traffic_file
-        self.sources = SELECT_COMMON + (CSRC + "k_full.hip", CSRC + "k_vsel.hip")
+        self.kernels, self.traffic_file, self.sources = PROFILED[name]
         B, K1, V = w.logits.shape
         k = K1 - 1
         H = w.history.shape[1]
@@ -300,14 +315,12 @@ class VerifySelectCase(Case):
 
 
 class BeamCase(Case):
-    def __init__(self, name, w, workload, traffic_file, rotate=None):
+    def __init__(self, name, w, workload, rotate=None):
         import numpy as np
         import torch
         from logits_processing_token_amd import tsel, upload, synth
         self.name, self.w, self.workload = name, w, workload
-        self.kernels = ("k_beam_rows", "k_beam_merge")
-        self.traffic_file = traffic_file
-        self.sources = COMMON + (CSRC + "k_beam.hip",)
+        self.kernels, self.traffic_file, self.sources = PROFILED[name]
         sw = synth.SelectWorkload(w.name, w.logits, w.history, w.lens, w.prompt_lens,
                                   w.max_lengths, w.settings, None)
         rows, V = w.logits.shape
@@ -365,56 +378,46 @@ def make_case(name: str) -> Case:
     if name == "C1":
         return SelectCase("C1", synth.c1_select(),
                           "C1 greedy: B=1 V=50272 fp32 logits N(0,3), history 64, "
-                          "repetition_penalty 1.2 (warm latency)",
-                          ("k_greedy",), "k_greedy_c1_traffic.txt",
-                          SELECT_COMMON + (CSRC + "k_greedy.hip",), rotate=1)
+                          "repetition_penalty 1.2 (warm latency)", rotate=1)
     if name == "C1v":
         return VerifyCase("C1v", synth.c1_verify(),
                           "C1 verify: [1, 6, 50272] fp32 N(0,3), k=5 greedy drafts (warm latency)",
-                          "k_verify_c1_traffic.txt", rotate=1)
+                          rotate=1)
     if name == "C2":
         return SelectCase("C2", synth.c2_select(),
                           "C2: B=64 V=32000 bf16 N(0,2), history 1024 with planted 3-gram "
                           "repeats; rep 1.1, no_repeat_ngram 3, min_new_tokens 300 (eos 2), "
-                          "temperature 0.7, top_k 50, top_p 0.9, sampling",
-                          ("k_topk",), "k_topk_c2_traffic.txt",
-                          SELECT_COMMON + (CSRC + "k_full.hip",))
+                          "temperature 0.7, top_k 50, top_p 0.9, sampling")
     if name == "C3":
         return SelectCase("C3", synth.c3_select(),
                           "C3 full chain: B=256 V=128256 bf16 logits, log-Zipf(1.1) over a "
                           "random permutation + N(0,1); history 4096; repetition_penalty 1.05; "
                           "100 suppress_tokens; 50 bad words; temperature 1.0; top_p 0.95; "
-                          "inverse-CDF sampling",
-                          ("k_vres",), "k_vres_b256_v128256_traffic.txt",
-                          SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp"),
-                          rotate=8)
+                          "inverse-CDF sampling", rotate=8)
     if name == "C4":
         return VerifyCase("C4", synth.c4_verify(),
                           "C4 verify: [32, 9, 151936] bf16 N(0,3), k=8 greedy drafts",
-                          "k_verify_c4_traffic.txt", rotate=6)
+                          rotate=6)
     if name == "C5":
         return SelectCase("C5", synth.c5_select(),
                           "C5: B=1024 V=262144 fp32, log-Zipf(1.2) + N(0,0.5); history 8192 "
                           "with planted 4-gram repeats; rep 1.1, no_repeat_ngram 4, forced_eos "
                           "on 102 rows, temperature 0.8, top_k 64, top_p 0.95, sampling",
-                          ("k_topk",), "k_topk_c5_traffic.txt",
-                          SELECT_COMMON + (CSRC + "k_full.hip",), rotate=1)
+                          rotate=1)
     if name == "F1":
         return SelectCase("F1", synth.c3_select(),
                           "C3 with the token log-probability (output_logprobs)",
-                          ("k_vres", "k_logprob"), "k_vres_logprob_c3_traffic.txt",
-                          SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp",
-                                           CSRC + "k_lsm.hip"), rotate=8, logprobs=True)
+                          rotate=8, logprobs=True)
     if name == "F2":
         return BeamCase("F2", synth.c3_beam(),
                         "one beam-search step over the C3 batch read as 64 prompts x 4 beams "
                         "(V=128256 bf16, history 4096, rep 1.05, 100 suppress, 50 bad words, "
-                        "1 eos id: K=8 per prompt)", "k_beam_c3_traffic.txt", rotate=8)
+                        "1 eos id: K=8 per prompt)", rotate=8)
     if name == "F3":
         return VerifySelectCase("F3", synth.c4_verify_select(),
                                 "verification with sampling at every position: [32, 9, 151936] "
                                 "bf16 N(0,3), k=8, history 256, rep 1.1, temperature 0.7, "
-                                "top_p 0.9", "k_vsel_c4_traffic.txt", rotate=6)
+                                "top_p 0.9", rotate=6)
     raise ValueError(f"unknown config {name}")
 
 
