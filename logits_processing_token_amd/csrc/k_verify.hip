@@ -6,9 +6,9 @@
 // Two launches.  k_verify_part: every (position row, vocabulary chunk) pair
 // is one workgroup of 256 threads that streams its chunk once (16 bytes per
 // lane per load) and writes the (score, id) argmax key of the chunk to the
-// workspace.  k_verify_merge: one wave per batch row merges the chunk keys of
-// its k+1 positions, counts the left-to-right matches, and writes the kept
-// tokens, the next token and the next draft count.  The launch boundary
+// workspace.  k_verify_merge: one workgroup per batch row merges the chunk
+// keys of its k+1 positions, counts the left-to-right matches, and writes
+// the kept tokens, the next token and the next draft count.  The launch boundary
 // orders the partial keys before the merge, so no workgroup needs a
 // device-wide fence (on this GPU one writes back and invalidates the L2), and
 // nothing in the workspace carries over from one call to the next.  Chunks
@@ -83,41 +83,39 @@ __global__ __launch_bounds__(VT) void k_verify_part(const char *logits, int64_t 
   }
 }
 
-// One wave per batch row b: merge each position's chunk keys (lane j takes
-// position j, its S loads in flight together), then compare every draft with
-// its position's token at once; the first mismatch ends the matches.
-__global__ __launch_bounds__(kWave) void k_verify_merge(int k, int S, const int32_t *cand,
-                                                        const uint64_t *partials,
-                                                        int32_t *n_match, int32_t *tokens,
-                                                        int32_t *next, int32_t *k_out) {
-  __shared__ int sel[kMaxVerifyK + 1];
+// One workgroup per batch row b: every (position, chunk) key is loaded by
+// its own thread (one round trip) and merged into the position's maximum
+// with an LDS max; then every draft is compared with its position's token at
+// once, and the first mismatch ends the matches.
+constexpr int kMT = 256;  // threads of the merge
+__global__ __launch_bounds__(kMT) void k_verify_merge(int k, int S, const int32_t *cand,
+                                                     const uint64_t *partials, int32_t *n_match,
+                                                     int32_t *tokens, int32_t *next,
+                                                     int32_t *k_out) {
+  __shared__ unsigned long long best[kMaxVerifyK + 1];
   __shared__ int first_miss;
-  const int b = blockIdx.x, lane = threadIdx.x;
-  if (lane == 0) first_miss = k;
-  for (int j = lane; j <= k; j += kWave) {
-    const uint64_t *p = partials + ((int64_t)b * (k + 1) + j) * S;
-    uint64_t m = 0ull;
-    int q = 0;
-    for (; q + 4 <= S; q += 4) {  // (four independent loads at a time)
-      const uint64_t a0 = p[q], a1 = p[q + 1], a2 = p[q + 2], a3 = p[q + 3];
-      const uint64_t x = a0 > a1 ? a0 : a1, y = a2 > a3 ? a2 : a3;
-      const uint64_t z = x > y ? x : y;
-      m = z > m ? z : m;
-    }
-    for (; q < S; ++q) m = p[q] > m ? p[q] : m;
-    sel[j] = m == 0ull ? 0 : (int)key_index(m);  // every score -inf: the lowest id
-  }
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = (k + 1) * S;
+  const uint64_t *p = partials + (int64_t)b * n;
+  for (int j = tid; j <= k; j += kMT) best[j] = 0ull;
+  if (tid == 0) first_miss = k;
   __syncthreads();
-  for (int j = lane; j < k; j += kWave)
-    if (cand[(int64_t)b * k + j] != sel[j]) atomicMin(&first_miss, j);
+  for (int i = tid; i < n; i += kMT) atomicMax(&best[i / S], (unsigned long long)p[i]);
+  __syncthreads();
+  auto sel = [&](int j) {  // every score -inf: the lowest id
+    const uint64_t m = best[j];
+    return m == 0ull ? 0 : (int)key_index(m);
+  };
+  for (int j = tid; j < k; j += kMT)
+    if (cand[(int64_t)b * k + j] != sel(j)) atomicMin(&first_miss, j);
   __syncthreads();
   const int nm = first_miss;  // drafts before the first mismatch are accepted
-  if (lane == 0) {
+  if (tid == 0) {
     n_match[b] = nm;
-    next[b] = sel[nm];
+    next[b] = sel(nm);
     k_out[b] = nm == k ? k + 2 : (k - 1 > 1 ? k - 1 : 1);
   }
-  for (int j = lane; j <= k; j += kWave) tokens[(int64_t)b * (k + 1) + j] = j <= nm ? sel[j] : -1;
+  for (int j = tid; j <= k; j += kMT) tokens[(int64_t)b * (k + 1) + j] = j <= nm ? sel(j) : -1;
 }
 
 // ---- the variant that allocates nothing -------------------------------------
@@ -178,7 +176,7 @@ hipError_t launch_verify(const void *logits, int32_t dtype, int32_t B, int32_t k
                        V, chunks, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_verify_merge, dim3(B), dim3(kWave), 0, s, k, chunks, cand,
+  hipLaunchKernelGGL(k_verify_merge, dim3(B), dim3(kMT), 0, s, k, chunks, cand,
                      (const uint64_t *)partials, n_match, tokens, next, k_out);
   return hipGetLastError();
 }
