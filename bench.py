@@ -68,6 +68,43 @@ def measured_traffic(name: str, sources):
         return None
 
 
+def read_ceiling_gbs(dev) -> float:
+    """The HBM read rate a plain streaming kernel (libtsel_probe.so: 16-byte
+    loads, four in flight, 512 workgroups of 256 lanes, the fastest grid of a
+    sweep from 128 to 16384) reaches over 1 GiB, two buffers alternating so
+    that neither stays in the 256 MB last-level cache."""
+    import ctypes as C
+    import torch
+    lib = C.CDLL(os.path.join(ROOT, "logits_processing_token_amd", "libtsel_probe.so"))
+    lib.tsel_probe_read.restype = C.c_int
+    lib.tsel_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
+    n = 1 << 30
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(1) for _ in range(2)]
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        rc = lib.tsel_probe_read(bufs[i % 2].data_ptr(), n, 512, out.data_ptr(),
+                                 stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"read probe failed: {rc}")
+    for i in range(4):
+        run(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    K = 20
+    for i in range(K):
+        run(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / K
+    del bufs
+    torch.cuda.empty_cache()
+    return n / (ms * 1e-3) / 1e9
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -428,7 +465,7 @@ SINGLE_THREAD_ROWS = {"C1": 1, "C1v": 1, "C2": 8, "C3": 4}
 ORACLE_ROWS = {"C5": 64, "F2": 16, "F3": 8}
 
 
-def run_case(case: Case, args) -> dict:
+def run_case(case: Case, args, ceiling=None) -> dict:
     import numpy as np
     import torch
     print(f"bench: {case.name}: warmup", file=sys.stderr, flush=True)
@@ -481,6 +518,9 @@ def run_case(case: Case, args) -> dict:
                      "algorithmic_bytes": case.alg_bytes,
                      "kernel": " + ".join(case.kernels)},
     }
+    if ceiling:
+        result["roofline"]["measured_read_ceiling"] = ceiling
+        result["roofline"]["frac_of_measured_ceiling"] = achieved / ceiling
     if not args.no_cpu_baseline:
         threads = host_threads()
         rows = ORACLE_ROWS.get(case.name)
@@ -520,6 +560,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C3", help="one of %s, or all" % ", ".join(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured HBM read ceiling (a plain streaming kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -548,10 +590,14 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceiling = None
+    if not args.no_ceiling:
+        print("bench: read ceiling", file=sys.stderr, flush=True)
+        ceiling = read_ceiling_gbs(dev)
     for n in names:
         print(f"bench: {n}: generating the workload", file=sys.stderr, flush=True)
         case = make_case(n)
-        print(json.dumps(run_case(case, args)), flush=True)
+        print(json.dumps(run_case(case, args, ceiling)), flush=True)
         del case
         torch.cuda.empty_cache()
     return 0
