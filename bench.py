@@ -73,21 +73,15 @@ def read_ceiling_gbs(dev) -> float:
     loads, four in flight, 512 workgroups of 256 lanes, the fastest grid of a
     sweep from 128 to 16384) reaches over 1 GiB, two buffers alternating so
     that neither stays in the 256 MB last-level cache."""
-    import ctypes as C
     import torch
-    lib = C.CDLL(os.path.join(ROOT, "logits_processing_token_amd", "libtsel_probe.so"))
-    lib.tsel_probe_read.restype = C.c_int
-    lib.tsel_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
+    from logits_processing_token_amd import probe
     n = 1 << 30
     bufs = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(1) for _ in range(2)]
     out = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def run(i):
-        rc = lib.tsel_probe_read(bufs[i % 2].data_ptr(), n, 512, out.data_ptr(),
-                                 stream.cuda_stream)
-        if rc != 0:
-            raise RuntimeError(f"read probe failed: {rc}")
+        probe.read(bufs[i % 2], 512, out, stream)
     for i in range(4):
         run(i)
     ev0 = torch.cuda.Event(enable_timing=True)

@@ -357,19 +357,6 @@ tsel_status tsel_finish_step(int32_t batch, const int32_t *tokens, const int32_t
                              const int32_t *max_lengths, const int32_t *eos_ids, int32_t n_eos,
                              uint8_t *finished, int32_t *out_tokens, void *stream);
 
-/*
- * tsel_selftest_exp2_monotone -- counts the binary32 inputs x in
- * [lo, hi] (taken in numeric order) for which the device's exp2 instruction
- * gives exp2(next(x)) < exp2(x).  Sampling without top_k maps histogram bins
- * of exp2 masses back to score intervals, which needs 0 here.
- *
- *  violations  device uint64 [1]; the count is added to it (the caller
- *              zeroes it first).
- * Errors: TSEL_ERR_INVALID_ARG for NULL violations, NaN bounds or lo > hi.
- */
-tsel_status tsel_selftest_exp2_monotone(float lo, float hi, unsigned long long *violations,
-                                        void *stream);
-
 /* Static text for a status code. */
 const char *tsel_status_string(tsel_status s);
 

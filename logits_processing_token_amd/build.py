@@ -3,8 +3,9 @@
     python -m logits_processing_token_amd.build
 
 compiles every source under csrc/ with hipcc (one process per file) and links
-the shared library next to this file; then libtsel_probe.so, the read-rate
-probe the benchmark reports beside its roofline (probe/).  hipcc
+the shared library next to this file; then libtsel_probe.so (probe/), the
+diagnostics: the read-rate probe the benchmark reports beside its roofline
+and the device exp2 check.  hipcc
 cross-compiles, so this runs on a machine without a GPU.
 """
 from __future__ import annotations
@@ -20,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtsel.so")
-PROBE_SRC = os.path.join(HERE, "probe", "k_read.hip")
+PROBE_SRC = [os.path.join(HERE, "probe", f) for f in ("k_read.hip", "k_exp2.hip")]
 PROBE_LIB = os.path.join(HERE, "libtsel_probe.so")
 ARCH = "gfx950"
 
@@ -65,7 +66,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-shared", "-o", tmp, PROBE_SRC]
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-shared", "-o", tmp, *PROBE_SRC]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")

@@ -532,20 +532,6 @@ tsel_status tsel_finish_step(int32_t batch, const int32_t *tokens, const int32_t
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 
-tsel_status tsel_selftest_exp2_monotone(float lo, float hi, unsigned long long *violations,
-                                        void *stream) {
-  if (!violations || !(lo <= hi)) return TSEL_ERR_INVALID_ARG;
-  auto ordered = [](float x) {
-    uint32_t u;
-    memcpy(&u, &x, sizeof u);
-    if (u == 0x80000000u) u = 0u;  // -0 and +0 are one point
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  };
-  hipError_t e = tsel::launch_exp2_monotone(ordered(lo), ordered(hi), violations,
-                                            static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
-}
-
 static size_t verify_partial_bytes(int32_t batch, int32_t k, int32_t vocab);
 
 size_t tsel_verify_workspace_size(int32_t batch, int32_t k, int32_t vocab) {

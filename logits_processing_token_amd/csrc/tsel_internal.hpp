@@ -152,9 +152,6 @@ hipError_t launch_verify_noalloc(const void *logits, int32_t dtype, int32_t B, i
                                  const int32_t *cand, int32_t *n_match, int32_t *tokens,
                                  int32_t *next, int32_t *k_out, hipStream_t s);
 
-hipError_t launch_exp2_monotone(uint32_t k0, uint32_t k1, unsigned long long *violations,
-                                hipStream_t s);
-
 constexpr int kMaxFinishEos = 256;  // stop ids one end-of-step call takes
 hipError_t launch_finish(int32_t B, const int32_t *tokens, const int32_t *lens,
                          const int32_t *max_lengths, const int32_t *eos, int32_t n_eos,

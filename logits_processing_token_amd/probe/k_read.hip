@@ -12,6 +12,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "tsel_probe.h"
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -34,9 +36,6 @@ __global__ __launch_bounds__(kThreads) void k_read(const uint4 *p, size_t n, uin
 
 }  // namespace
 
-// Reads `bytes` (a multiple of 16) from the 16-byte aligned device buffer
-// `src` once, with `blocks` workgroups of 256 lanes, on `stream`; `out` is a
-// device word the kernel may write.  Returns 0, or the HIP error code.
 extern "C" int tsel_probe_read(const void *src, size_t bytes, int blocks, uint32_t *out,
                                void *stream) {
   if (!src || !out || bytes % 16 != 0 || blocks < 1) return (int)hipErrorInvalidValue;

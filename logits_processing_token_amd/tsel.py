@@ -28,7 +28,7 @@ TSEL_MAX_EOS = 8
 EXPORTS = (
     "tsel_process_select", "tsel_process_select_workspace_size", "tsel_validate_params",
     "tsel_mask_build", "tsel_verify", "tsel_verify_workspace_size", "tsel_status_string",
-    "tsel_selftest_exp2_monotone", "tsel_finish_step", "tsel_verify_noalloc",
+    "tsel_finish_step", "tsel_verify_noalloc",
     "tsel_verify_select", "tsel_verify_select_workspace_size", "tsel_beam_step",
     "tsel_beam_width", "tsel_beam_step_workspace_size",
 )
@@ -102,8 +102,6 @@ def load() -> C.CDLL:
     lib.tsel_status_string.argtypes = [i32]
     lib.tsel_finish_step.restype = i32
     lib.tsel_finish_step.argtypes = [i32, vp, vp, vp, vp, i32, vp, vp, vp]
-    lib.tsel_selftest_exp2_monotone.restype = i32
-    lib.tsel_selftest_exp2_monotone.argtypes = [C.c_float, C.c_float, vp, vp]
     _lib = lib
     return lib
 
@@ -227,15 +225,6 @@ def finish_step(tokens, lens, max_lengths, eos_ids, finished, out_tokens=None, s
                                  _ptr(out_tokens), _stream(stream))
     _check(st, "tsel_finish_step")
     return out_tokens
-
-
-def selftest_exp2_monotone(lo: float, hi: float, stream=None) -> int:
-    """Number of inputs in [lo, hi] where the device exp2 decreases."""
-    import torch
-    out = torch.zeros(1, dtype=torch.int64, device="cuda")
-    _check(load().tsel_selftest_exp2_monotone(lo, hi, _ptr(out), _stream(stream)),
-           "tsel_selftest_exp2_monotone")
-    return int(out.item())
 
 
 def verify_workspace_size(batch: int, k: int, vocab: int) -> int:

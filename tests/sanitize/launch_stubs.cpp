@@ -41,9 +41,6 @@ hipError_t launch_verify_noalloc(const void *, int32_t, int32_t, int32_t, int32_
                                  int32_t *, hipStream_t) {
   return hipSuccess;
 }
-hipError_t launch_exp2_monotone(uint32_t, uint32_t, unsigned long long *, hipStream_t) {
-  return hipSuccess;
-}
 hipError_t launch_finish(int32_t, const int32_t *, const int32_t *, const int32_t *,
                          const int32_t *, int32_t, uint8_t *, int32_t *, hipStream_t) {
   return hipSuccess;

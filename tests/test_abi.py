@@ -1,6 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every entry point
 include/tsel.h declares, and its host-side checks return the documented
-status codes before touching the GPU."""
+status codes before touching the GPU; the diagnostics library exports what
+include/tsel_probe.h declares."""
 import ctypes as C
 import os
 import re
@@ -12,8 +13,8 @@ from logits_processing_token_amd import tsel
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    text = open(os.path.join(ROOT, "include", "tsel.h")).read()
+def _declared(header="tsel.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(tsel_\w+)\s*\(", text)))
 
@@ -26,6 +27,15 @@ def test_library_exports_every_declared_symbol():
     lib = tsel.load()
     for name in _declared():
         assert hasattr(lib, name), name
+
+
+def test_probe_library_matches_its_header():
+    from logits_processing_token_amd import probe
+    assert _declared("tsel_probe.h") == sorted(probe.EXPORTS)
+    lib = probe.load()
+    for name in probe.EXPORTS:
+        assert hasattr(lib, name), name
+    assert not hasattr(tsel.load(), "tsel_probe_read")
 
 
 def _params(**kw):

@@ -51,10 +51,11 @@ def _assert_select(w, rows=None, processed=True, max_low_mismatch_frac=0.0,
 def test_device_exp2_is_monotone():
     """The full sampling path maps histogram bins of exp2 masses back to
     score intervals; that needs the device exp2 to be monotone.  Checked
-    exhaustively over every binary32 input in [-160, 130]."""
-    from logits_processing_token_amd import tsel
-    assert tsel.selftest_exp2_monotone(-160.0, -0.0) == 0
-    assert tsel.selftest_exp2_monotone(0.0, 130.0) == 0
+    exhaustively over every binary32 input in [-160, 130] by the diagnostics
+    library."""
+    from logits_processing_token_amd import probe
+    assert probe.exp2_monotone(-160.0, -0.0) == 0
+    assert probe.exp2_monotone(0.0, 130.0) == 0
 
 
 def test_mask_build():
