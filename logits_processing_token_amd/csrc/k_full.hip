@@ -35,18 +35,230 @@
 #include <stdint.h>
 
 #include "k_mass.hpp"
+#include "k_vkey.hpp"
 
 namespace tsel {
+
+// ---------------------------------------------------------------------------
+// The histogram pass over a streamed bf16 row, by value.  Equal bf16 scores
+// have equal masses, so the row is counted into one bin per bf16 value (a
+// 32-bit LDS add per element, two copies by lane parity; no temperature
+// division and no exponential per element) and each value bin then adds
+// count * (its mass's word) to the mass histogram: the same exact words as
+// one add per element.  The value bins span the keys [klo, klo + kVBins - 1)
+// with klo the lowest key whose mass reaches mass bin 1 (lower keys count for
+// nothing, as in the mass histogram).  Elements that a value bin cannot
+// stand for take the mass histogram one by one: near-zero scores (one key
+// for a range of values), keys past the value bins, scores penalized in the
+// stream, and the list.  With `keep`, elements of mass bins >= keep_bin are
+// appended to the collect buffer; a value-counted one as its raw score and
+// id, marked by a negative mass, to be finished after the pass.  Returns
+// this lane's maximum final score.
+template <bool TOPK>
+__device__ __forceinline__ float value_hist_pass(const SelectArgs &a, int row, const Lds &s,
+                                                 RowShared &sh, float t_y, float c, bool keep,
+                                                 int keep_bin, uint64_t *hist, uint64_t *ckey,
+                                                 float *cval, uint32_t *vb) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int nb = a.nb, shift = 23 - a.bin_mant, base = (127 - kBinBelow) << a.bin_mant;
+  const uint32_t lowmask = (1u << shift) - 1u;
+  const float T = TOPK ? a.temperature : 1.0f;
+  const int NG = a.V / 8;
+  const char *rowp = a.logits + (int64_t)row * a.row_bytes;
+  const bool dense_pen = sh.dense_pen != 0;
+  auto final_y = [&](float x) { return (T != 1.0f) ? x / T : x; };
+  auto bin_of = [&](float y) {
+    return mass_bin(__float_as_uint(mass_of<TOPK>(y, t_y, c)), shift, base, nb);
+  };
+  // Smallest key whose value reaches mass bin `target` (the near-zero keys
+  // stand for -2^-kZoneExp and +2^-kZoneExp; neither is counted by value).
+  auto first_key = [&](int target) {
+    auto val = [&](uint32_t k) {
+      const float z = __uint_as_float((uint32_t)(127 - kZoneExp) << 23);
+      return k == kKeyZoneNeg ? -z : k == kKeyZonePos ? z : vkey_value(k);
+    };
+    uint32_t lo = kKeyLowFinite - 1u, hi = vkey(0x7F80u);  // -inf: no mass; +inf: every bin
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      if (bin_of(final_y(val(mid))) >= target) hi = mid;
+      else lo = mid;
+    }
+    return hi;
+  };
+  __shared__ uint32_t lim[2];
+  if (tid == 0) lim[0] = first_key(1);
+  if (tid == kWave) lim[1] = keep ? first_key(keep_bin) : 0xFFFFFFFFu;
+  for (int i = tid; i < 2 * kVStride; i += NT) vb[i] = 0u;
+  __syncthreads();
+  const uint32_t klo = lim[0], kkeep = lim[1];
+  const uint32_t khi = klo + (uint32_t)(kVBins - 1);  // keys from here: one by one
+  uint32_t *vbl = vb + (lane & 1) * kVStride;
+  float lmx = -INFINITY;
+  uint32_t kmx = 0u;
+  // An element that a value bin does not stand for (few per row: near-zero
+  // scores, keys past the bins, scores penalized in the stream): one by one
+  // into the mass histogram, appended when kept.
+  auto one_by_one = [&](int v, uint32_t raw, bool pen) {
+    float x = __uint_as_float(raw << 16);
+    if (pen) x = penalize(x, a.rep);
+    const float y = final_y(x);
+    lmx = fmaxf(lmx, y);
+    const uint32_t bits = __float_as_uint(mass_of<TOPK>(y, t_y, c));
+    const int b = mass_bin(bits, shift, base, nb);
+    atomicAdd(&hist[b], (1ull << 40) | (bits & lowmask));
+    if (keep && b >= keep_bin) {
+      const int slot = atomicAdd(&sh.n_coll, 1);
+      if (slot < a.ccap) {
+        ckey[slot] = sel_key(y, (uint32_t)v);
+        cval[slot] = __uint_as_float(bits);
+      }
+    }
+  };
+  // One chunk (every lane of the wave calls; `real`: the chunk is in the
+  // row): every element adds 1 to its value bin (elements a value bin does
+  // not stand for, and chunks past the row, add to spare words past the
+  // bins); the kept ones are appended as raw score and id at slots that one
+  // add per wave reserves (a wave scan of the lanes' counts places them).
+  const uint8_t *kbyte = reinterpret_cast<const uint8_t *>(s.kmask);
+  const uint8_t *sbyte = reinterpret_cast<const uint8_t *>(s.smask);
+  auto chunk = [&](int g, uint4 cw, uint32_t kb, uint32_t sb, bool real) {
+    const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+    uint32_t slow = 0u, kept = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t raw = ((kb >> j) & 1u) ? 0xFF80u : (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const uint32_t k = vkey(raw);
+      const bool by_value = !((sb >> j) & 1u) && k != kKeyZoneNeg && k != kKeyZonePos && k < khi;
+      kmx = max(kmx, by_value && real ? k : 0u);
+      atomicAdd(&vbl[!real ? (uint32_t)kVBins + 1u
+                           : by_value ? (k >= klo ? k - klo + 1u : 0u) : (uint32_t)kVBins],
+                1u);
+      slow |= real && !by_value ? 1u << j : 0u;
+      kept |= real && by_value && k >= kkeep ? 1u << j : 0u;
+    }
+    if (slow) {
+#pragma unroll 1
+      for (uint32_t m = slow; m; m &= m - 1u) {
+        const int j = __ffs(m) - 1;
+        const uint32_t raw = ((kb >> j) & 1u) ? 0xFF80u : (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        one_by_one(g * 8 + j, raw, (sb >> j) & 1u);
+      }
+    }
+    if (keep) {
+      const int n = __popc(kept);
+      const int incl = wave_incl_scan_i32(n);
+      const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+      if (tot > 0) {
+        int first = 0;
+        if (lane == kWave - 1) first = atomicAdd(&sh.n_coll, tot);
+        int o = __builtin_amdgcn_readlane(first, kWave - 1) + incl - n;
+#pragma unroll 1
+        for (uint32_t m = kept; m; m &= m - 1u, ++o) {
+          const int j = __ffs(m) - 1;
+          if (o < a.ccap) {
+            ckey[o] = ((uint64_t)((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 32) | (uint32_t)(g * 8 + j);
+            cval[o] = -1.0f;
+          }
+        }
+      }
+    }
+  };
+  // The stream: batches of U chunks through a buffer resource (a read past
+  // the row returns 0 and touches no memory, so every load is issued by every
+  // lane and the batches alternate between two register sets: each batch's
+  // loads fly while the other is counted).  Each chunk's kill (and
+  // stream-penalty) byte is read one chunk ahead.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, NG * 16, 0x00020000);
+  auto ld = [&](int g) {
+    const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rs, g * 16, 0, 0);
+    return make_uint4(q.x, q.y, q.z, q.w);
+  };
+  uint32_t kb_n = tid < NG ? kbyte[tid] : 0u;
+  uint32_t sb_n = dense_pen && tid < NG ? sbyte[tid] : 0u;
+  auto batch = [&](int i, const uint4 *cw) {  // batch i: chunks tid + (i U + u) NT
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = tid + (i * U + u) * NT;
+      if (__ballot(g < NG) == 0ull) continue;  // (past the row for the whole wave)
+      const uint32_t kb = kb_n, sb = sb_n;
+      const int gn = min(g + NT, NG - 1);
+      kb_n = kbyte[gn];
+      sb_n = dense_pen ? sbyte[gn] : 0u;
+      chunk(g, cw[u], kb, sb, g < NG);
+    }
+  };
+  const int nbat = (NG + NT * U - 1) / (NT * U);
+  uint4 ca[U], cb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) ca[u] = ld(tid + u * NT);
+  for (int i = 0; i < nbat; i += 2) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) cb[u] = ld(tid + ((i + 1) * U + u) * NT);
+    batch(i, ca);
+#pragma unroll
+    for (int u = 0; u < U; ++u) ca[u] = ld(tid + ((i + 2) * U + u) * NT);
+    if (i + 1 < nbat) batch(i + 1, cb);
+  }
+  // the list: penalized seen ids and the row's tail, one by one
+  const int n_list = sh.n_list;
+  for (int i = tid; i < n_list; i += NT) {
+    const float y = final_y(s.list_val[i]);
+    lmx = fmaxf(lmx, y);
+    const uint32_t bits = __float_as_uint(mass_of<TOPK>(y, t_y, c));
+    const int b = mass_bin(bits, shift, base, nb);
+    atomicAdd(&hist[b], (1ull << 40) | (bits & lowmask));
+    if (keep && b >= keep_bin) {
+      const int slot = atomicAdd(&sh.n_coll, 1);
+      if (slot < a.ccap) {
+        ckey[slot] = sel_key(y, (uint32_t)s.list_id[i]);
+        cval[slot] = __uint_as_float(bits);
+      }
+    }
+  }
+  __syncthreads();
+  // value bins -> mass histogram (bin 0: below klo, nothing)
+  for (int b = 1 + tid; b < kVBins; b += NT) {
+    const uint32_t n = vb[b] + vb[kVStride + b];
+    if (n == 0u) continue;
+    const uint32_t bits = __float_as_uint(mass_of<TOPK>(final_y(vkey_value(klo + (uint32_t)b - 1u)), t_y, c));
+    atomicAdd(&hist[mass_bin(bits, shift, base, nb)],
+              (uint64_t)n * ((1ull << 40) | (bits & lowmask)));
+  }
+  // the kept value-counted elements: their keys and masses
+  if (keep) {
+    const int nc = min(sh.n_coll, a.ccap);
+    for (int i = tid; i < nc; i += NT) {
+      if (cval[i] < 0.0f) {
+        const uint64_t kk = ckey[i];
+        const float y = final_y(__uint_as_float((uint32_t)(kk >> 32) << 16));
+        ckey[i] = sel_key(y, (uint32_t)kk);
+        cval[i] = mass_of<TOPK>(y, t_y, c);
+      }
+    }
+  }
+  const float vmx = kmx >= kKeyLowFinite ? final_y(vkey_value(kmx)) : -INFINITY;
+  return fmaxf(lmx, vmx);
+}
 
 // ---------------------------------------------------------------------------
 // Histogram, bins, collect and walk for one row.  visit(f) calls f(id, y)
 // once for every element of the row (dense stream and list), y the final
 // score before top_k / top_p (killed ids as -inf).  Returns the token, or -1
 // when the bisection must decide; *kcut / *t_out describe the kept set.
-template <bool TOPK, class Visit>
+//
+// VF: the histogram pass counts a streamed bf16 row by value
+// (value_hist_pass); a second pass, when the maximum outruns the reference,
+// is the plain one.  keep1 (with VF): that pass also keeps every element of
+// the mass bins from kKeepBelow binades under the reference up; when those
+// bins hold the boundary's and the sample's and the buffer did not overflow,
+// step 3 takes them from there instead of visiting the row again.
+template <bool TOPK, bool VF = false, class Visit>
 __device__ __forceinline__ int full_core(const SelectArgs &a, int row, const Lds &s,
                                          RowShared &sh, float t_y, float m0, Visit &&visit,
-                                         uint64_t *kcut_out, float *t_out, float *cref_out) {
+                                         uint64_t *kcut_out, float *t_out, float *cref_out,
+                                         bool keep1 = false) {
   const int tid = threadIdx.x;
   const int nb = a.nb;
   const int shift = 23 - a.bin_mant;
@@ -59,20 +271,30 @@ __device__ __forceinline__ int full_core(const SelectArgs &a, int row, const Lds
   // ---- 1. mass histogram (a second pass when the maximum outruns r) ----
   float ref = m0 == -INFINITY ? 0.0f : m0 + kRefSlack;
   float mx = -INFINITY;
+  const int keep_bin = (kBinBelow - kKeepBelow) << a.bin_mant;  // first kept bin
+  bool kept = false;  // the collect buffer holds every element of bins >= keep_bin
   for (int attempt = 0; attempt < 2; ++attempt) {
     const float c = ref * kLog2e;
+    const bool keep = VF && keep1 && attempt == 0;
     for (int i = tid; i < nb; i += NT) hist[i] = 0ull;
+    if (tid == 0) sh.n_coll = 0;
     __syncthreads();
     float lmx = -INFINITY;
-    visit([&](int, float y) {
+    if (VF && attempt == 0) {
+      uint32_t *vb = reinterpret_cast<uint32_t *>(s.area + 8 * (size_t)nb + 12 * (size_t)a.ccap +
+                                                  12 * (size_t)kGatherCap);
+      lmx = value_hist_pass<TOPK>(a, row, s, sh, t_y, c, keep, keep_bin, hist, ckey, cval, vb);
+    } else visit([&](int, float y) {
       lmx = fmaxf(lmx, y);
       const uint32_t bits = __float_as_uint(mass_of<TOPK>(y, t_y, c));
       atomicAdd(&hist[mass_bin(bits, shift, base, nb)], (1ull << 40) | (bits & lowmask));
     });
     mx = block_max_f32<NT>(lmx, sh.red_f32);
+    kept = keep && sh.n_coll <= a.ccap;
     // Masses below 2^(kBinAbove - 1) stay under the top bin.
     if (mx == -INFINITY || (mx - ref) * kLog2e < (float)(kBinAbove - 1)) break;
     ref = mx;
+    kept = false;
   }
   const float cref = ref * kLog2e;
   *cref_out = cref;
@@ -164,44 +386,49 @@ __device__ __forceinline__ int full_core(const SelectArgs &a, int row, const Lds
   if (!(shi >= 1 && slo >= 1 && slo <= shi && ncount <= (uint32_t)a.ccap)) return -1;
 
   // ---- 3. collect bin bp and bins [slo, shi] ----------------------------
-  // Bins are score intervals: Y(b) = smallest ordered score key of bin >= b,
-  // four bisections run on four lanes.
-  __shared__ uint32_t ylim[4];
-  if (tid < 4) {
-    const int bsel = tid == 0 ? slo : tid == 1 ? shi + 1 : tid == 2 ? bp : bp + 1;
-    uint32_t r = 0u;
-    if (tid < 2 || bp >= 0) {
-      if (bsel >= nb) {
-        r = 0xFFFFFFFFu;
-      } else {
-        uint32_t lo = ordered_f32(-INFINITY), hi = ordered_f32(INFINITY);
-        while (hi - lo > 1) {
-          const uint32_t mid = lo + (hi - lo) / 2;
-          if (mass_bin(__float_as_uint(mass_of<TOPK>(unordered_f32(mid), t_y, cref)), shift, base,
-                       nb) >= bsel)
-            hi = mid;
-          else
-            lo = mid;
+  // Kept by the histogram pass when every bin needed lies at or above the
+  // kept bins: the buffer then holds each of their elements (and others,
+  // which step 4 filters out by bin).  Otherwise: bins are score intervals,
+  // Y(b) = smallest ordered score key of bin >= b (four bisections run on
+  // four lanes), and the row is visited again.
+  if (!(kept && slo >= keep_bin && (bp < 0 || bp >= keep_bin))) {
+    __shared__ uint32_t ylim[4];
+    if (tid < 4) {
+      const int bsel = tid == 0 ? slo : tid == 1 ? shi + 1 : tid == 2 ? bp : bp + 1;
+      uint32_t r = 0u;
+      if (tid < 2 || bp >= 0) {
+        if (bsel >= nb) {
+          r = 0xFFFFFFFFu;
+        } else {
+          uint32_t lo = ordered_f32(-INFINITY), hi = ordered_f32(INFINITY);
+          while (hi - lo > 1) {
+            const uint32_t mid = lo + (hi - lo) / 2;
+            if (mass_bin(__float_as_uint(mass_of<TOPK>(unordered_f32(mid), t_y, cref)), shift, base,
+                         nb) >= bsel)
+              hi = mid;
+            else
+              lo = mid;
+          }
+          r = hi;
         }
-        r = hi;
       }
+      ylim[tid] = r;
     }
-    ylim[tid] = r;
+    if (tid == 0) sh.n_coll = 0;
+    __syncthreads();
+    const uint32_t s_lo = ylim[0], s_hi = ylim[1], p_lo = ylim[2], p_hi = ylim[3];
+    visit([&](int v, float y) {
+      const uint32_t ky = ordered_f32(y);
+      if ((ky >= s_lo && ky < s_hi) || (ky >= p_lo && ky < p_hi)) {
+        const int slot = atomicAdd(&sh.n_coll, 1);
+        if (slot < a.ccap) {
+          ckey[slot] = sel_key(y, (uint32_t)v);
+          cval[slot] = mass_of<TOPK>(y, t_y, cref);
+        }
+      }
+    });
+    __syncthreads();
   }
-  if (tid == 0) sh.n_coll = 0;
-  __syncthreads();
-  const uint32_t s_lo = ylim[0], s_hi = ylim[1], p_lo = ylim[2], p_hi = ylim[3];
-  visit([&](int v, float y) {
-    const uint32_t ky = ordered_f32(y);
-    if ((ky >= s_lo && ky < s_hi) || (ky >= p_lo && ky < p_hi)) {
-      const int slot = atomicAdd(&sh.n_coll, 1);
-      if (slot < a.ccap) {
-        ckey[slot] = sel_key(y, (uint32_t)v);
-        cval[slot] = mass_of<TOPK>(y, t_y, cref);
-      }
-    }
-  });
-  __syncthreads();
   const int nc = min(sh.n_coll, a.ccap);
 
   // ---- 4. exact order inside one bin --------------------------------------
@@ -517,12 +744,34 @@ __device__ __forceinline__ void full_row(const SelectArgs &a, int row, unsigned 
         f(s.list_id[i], (T != 1.0f) ? x / T : x);
       }
     };
+    // reference: every lane's first chunk and the list, as the stream
+    // transforms them (the histogram pass moves it up if the row's maximum
+    // outruns it); a pass over the row when none of them is kept
     float m0 = -INFINITY;
-    visit([&](int, float y) {
+    if (tid < NG) {
+      const uint4 ck = kill_chunk<DT>(load16(rowp + (int64_t)tid * 16), tid, s);
+      const uint32_t sb = dense_pen ? chunk_bits<DT>(s.smask, tid) : 0u;
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        float x = E::get(ck, j);
+        if ((sb >> j) & 1u) x = penalize(x, a.rep);
+        const float y = (T != 1.0f) ? x / T : x;
+        if (y >= t_y) m0 = fmaxf(m0, y);
+      }
+    }
+    for (int i = tid; i < n_list; i += NT) {
+      const float x = s.list_val[i];
+      const float y = (T != 1.0f) ? x / T : x;
       if (y >= t_y) m0 = fmaxf(m0, y);
-    });
+    }
     m0 = block_max_f32<NT>(m0, sh.red_f32);
-    token = full_core<!SIMPLE>(a, row, s, sh, t_y, m0, visit, &kcut, &t_out, &cref);
+    if (m0 == -INFINITY) {
+      visit([&](int, float y) {
+        if (y >= t_y) m0 = fmaxf(m0, y);
+      });
+      m0 = block_max_f32<NT>(m0, sh.red_f32);
+    }
+    token = full_core<!SIMPLE, DT == 1>(a, row, s, sh, t_y, m0, visit, &kcut, &t_out, &cref, true);
   }
   if (token < 0) token = bisect_select<DT>(a, row, s, sh, t_y, cref, &kcut);
   if (tid == 0) a.out_tokens[row] = token;

@@ -89,10 +89,12 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   } else if (kind == SelectKernel::kFull) {
     mant = 6;
     ccap = 4096;
+    // bf16 rows: two copies of the value bins of the streamed histogram pass
+    const size_t vbins = p->dtype == TSEL_BF16 ? 2 * 4 * (size_t)tsel::kVStride : 0;
     auto need = [&]() {
       nb = (tsel::kBinBelow + tsel::kBinAbove) << mant;
       // collected (key, mass) pairs, then room to order one sub-bin
-      return 8 * (size_t)nb + 12 * (size_t)ccap + 12 * (size_t)tsel::kGatherCap;
+      return 8 * (size_t)nb + 12 * (size_t)ccap + 12 * (size_t)tsel::kGatherCap + vbins;
     };
     area = need();
     while ((mant > 3 || ccap > 256) && fixed + area + 8 * lcap > budget) {
