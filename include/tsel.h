@@ -104,9 +104,11 @@ typedef struct tsel_params {
  * every id is removed selects id 0.
  *
  *  logits      device, B rows of V elements of params->dtype, row b at
- *              logits + b * logits_row_stride.  The start of every row must be
- *              16-byte aligned (so logits_row_stride * element size must be a
- *              multiple of 16).  Not modified.
+ *              logits + b * logits_row_stride, 16-byte aligned.  Any stride
+ *              >= V: when logits_row_stride * element size is not a multiple
+ *              of 16 the rows are first copied into the workspace at the
+ *              smallest stride that is (one more read and write of the
+ *              logits).  Not modified.
  *  history     device int32 [B, hist_stride]: the prompt then the new tokens
  *              of each row, oldest first; row b uses its first lens[b] ids.
  *              Ids outside [0, V) are ignored by every processor.
@@ -129,9 +131,10 @@ typedef struct tsel_params {
  *              NULL).
  *  workspace, workspace_bytes  device scratch of at least
  *              tsel_process_select_workspace_size(params) bytes, 256-byte
- *              aligned (NULL/0 when that is 0): fp32 rows of the
- *              renormalized scores when renormalize_logits is set, and of
- *              the final scores when output_logprobs is.
+ *              aligned (NULL/0 when that is 0): the copied rows when the
+ *              stride needs them, fp32 rows of the renormalized scores when
+ *              renormalize_logits is set, and of the final scores when
+ *              output_logprobs is.
  *
  * Errors: TSEL_ERR_INVALID_ARG for B < 0, V < 1, a stride below V, a
  * hist_stride below 0, penalty <= 0, n < 0, min lengths < 0, n_eos outside
@@ -139,8 +142,8 @@ typedef struct tsel_params {
  * outside (0, 1] when sampling, a NULL required pointer, or out_logprobs
  * given without output_logprobs (or the reverse); TSEL_ERR_WORKSPACE when
  * the workspace is missing or too small;
- * TSEL_ERR_UNSUPPORTED for a misaligned row layout or a vocabulary too large
- * for the on-chip masks (V > 524,288).
+ * TSEL_ERR_UNSUPPORTED for logits not 16-byte aligned or a vocabulary too
+ * large for the on-chip masks (V > 524,288).
  */
 tsel_status tsel_process_select(const void *logits, const int32_t *history,
                                 const int32_t *lens, const tsel_params *params,
@@ -247,7 +250,8 @@ tsel_status tsel_verify_noalloc(const void *logits, int32_t dtype, int32_t batch
  * selected token.
  *
  *  logits      device [B, k+1, params->logits_row_stride] of params->dtype
- *              (16-byte aligned rows); params->batch is B.
+ *              (16-byte aligned; any stride >= V, as tsel_process_select);
+ *              params->batch is B.
  *  history, lens  as tsel_process_select (history [B, params->hist_stride],
  *              lens [3 * B]).
  *  params      the selection settings (processors, warpers,
@@ -258,7 +262,7 @@ tsel_status tsel_verify_noalloc(const void *logits, int32_t dtype, int32_t batch
  *  workspace   device, 256-byte aligned, at least
  *              tsel_verify_select_workspace_size(params, k) bytes: the
  *              position rows' histories, lengths and tokens (and what the
- *              selection itself needs).
+ *              selection itself needs, the copied rows among it).
  * Errors: those of tsel_process_select for the settings; TSEL_ERR_INVALID_ARG
  * for k < 0, output_logprobs set, or NULL required pointers;
  * TSEL_ERR_WORKSPACE for a missing or small workspace; TSEL_ERR_UNSUPPORTED
@@ -291,7 +295,7 @@ size_t tsel_verify_select_workspace_size(const tsel_params *params, int32_t k);
  * Slots past a prompt's candidates hold score -inf, beam -1, id -1.
  *
  *  logits       device, params->batch = P * num_beams rows as in
- *               tsel_process_select (16-byte aligned rows).
+ *               tsel_process_select (16-byte aligned; any stride >= V).
  *  history, lens  as tsel_process_select, one row per beam.
  *  params       the processors' settings; the warpers are not used
  *               (do_sample must be 0), nor are renormalize_logits and
@@ -303,8 +307,9 @@ size_t tsel_verify_select_workspace_size(const tsel_params *params, int32_t k);
  *  out_scores   device float [P, K]; out_beams, out_tokens device int32
  *               [P, K]: the kept candidates, best first.
  *  workspace    device, 256-byte aligned, at least
- *               tsel_beam_step_workspace_size(params, num_beams) bytes: each
- *               beam row's best K candidates.
+ *               tsel_beam_step_workspace_size(params, num_beams) bytes: the
+ *               copied rows when the stride needs them, then each beam row's
+ *               best K candidates.
  * Errors: those of tsel_process_select for the params; TSEL_ERR_INVALID_ARG
  * for do_sample, renormalize_logits or output_logprobs set, num_beams < 1,
  * a batch that is not a multiple of num_beams, or NULL required pointers;

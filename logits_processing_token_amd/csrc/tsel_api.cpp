@@ -37,8 +37,6 @@ tsel_status check_params(const tsel_params *p, bool uniforms_given) {
     if (!uniforms_given) return TSEL_ERR_INVALID_ARG;
   }
   if (p->vocab > kMaxVocab) return TSEL_ERR_UNSUPPORTED;
-  const int64_t esize = p->dtype == TSEL_BF16 ? 2 : 4;
-  if ((p->logits_row_stride * esize) % 16 != 0) return TSEL_ERR_UNSUPPORTED;
   return TSEL_OK;
 }
 
@@ -262,6 +260,35 @@ static size_t renorm_bytes(const tsel_params *p) {
   return p->renormalize_logits ? align256((size_t)p->batch * renorm_stride(p) * 4) : 0;
 }
 
+// Rows whose byte stride is not a multiple of 16 are first copied into the
+// workspace at the smallest stride that is (the kernels read rows in 16-byte
+// units from 16-byte aligned starts).
+static int64_t esize_of(const tsel_params *p) { return p->dtype == TSEL_BF16 ? 2 : 4; }
+static bool needs_repack(const tsel_params *p) {
+  return (p->logits_row_stride * esize_of(p)) % 16 != 0;
+}
+static int64_t repack_stride(const tsel_params *p) {
+  const int64_t epu = 16 / esize_of(p);
+  return ((int64_t)p->vocab + epu - 1) / epu * epu;
+}
+static size_t repack_bytes(const tsel_params *p) {
+  return needs_repack(p) ? align256((size_t)p->batch * (size_t)repack_stride(p) * esize_of(p)) : 0;
+}
+// The repacked rows at the start of `ws` (when needed): *pr is params with
+// their stride, *src their address; returns the workspace after them.
+static char *repack_rows(const tsel_params *params, const void *logits, char *ws, tsel_params *pr,
+                         const void **src, hipStream_t s, hipError_t *e) {
+  *pr = *params;
+  *src = logits;
+  *e = hipSuccess;
+  if (!needs_repack(params)) return ws;
+  pr->logits_row_stride = repack_stride(params);
+  *e = tsel::launch_repack(logits, params->dtype, params->logits_row_stride, ws,
+                           pr->logits_row_stride, params->batch, params->vocab, s);
+  *src = ws;
+  return ws + repack_bytes(params);
+}
+
 // The params the selection itself sees: after renormalize_logits, fp32 rows
 // with every processor switched off (the lengths still mark padding rows).
 static tsel_params selection_params(const tsel_params *params) {
@@ -281,7 +308,7 @@ static tsel_params selection_params(const tsel_params *params) {
 
 size_t tsel_process_select_workspace_size(const tsel_params *params) {
   if (!params || params->batch <= 0 || params->vocab < 1) return 0;
-  size_t n = renorm_bytes(params);
+  size_t n = repack_bytes(params) + renorm_bytes(params);
   if (params->output_logprobs) {
     const tsel_params q = selection_params(params);
     if (!fused_logprobs(select_path(&q)))
@@ -368,10 +395,14 @@ tsel_status tsel_process_select(const void *logits, const int32_t *history, cons
   if (need > 0 && (!workspace || workspace_bytes < need)) return TSEL_ERR_WORKSPACE;
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TSEL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char *ws = static_cast<char *>(workspace);
+  tsel_params pr;
+  const void *src;
+  hipError_t e;
+  char *ws = repack_rows(params, logits, static_cast<char *>(workspace), &pr, &src, s, &e);
+  if (e != hipSuccess) return TSEL_ERR_LAUNCH;
+  params = &pr;
+  logits = src;
   const tsel_params p = selection_params(params);
-  const void *src = logits;
-  hipError_t e = hipSuccess;
   if (params->renormalize_logits) {
     // the processors and the log-softmax into fp32 rows; the selection then
     // reads those with every processor switched off (the lengths still mark
@@ -474,7 +505,7 @@ int32_t tsel_beam_width(int32_t num_beams, int32_t n_eos) {
 size_t tsel_beam_step_workspace_size(const tsel_params *params, int32_t num_beams) {
   if (!params || params->batch <= 0 || num_beams < 1) return 0;
   const int32_t K = tsel_beam_width(num_beams, std::max(params->n_eos, 0));
-  return align256((size_t)params->batch * (size_t)K * 8);
+  return repack_bytes(params) + align256((size_t)params->batch * (size_t)K * 8);
 }
 
 tsel_status tsel_beam_step(const void *logits, const int32_t *history, const int32_t *lens,
@@ -499,17 +530,23 @@ tsel_status tsel_beam_step(const void *logits, const int32_t *history, const int
   const size_t need = tsel_beam_step_workspace_size(params, num_beams);
   if (!workspace || workspace_bytes < need) return TSEL_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TSEL_ERR_UNSUPPORTED;
+  tsel_params pr;
+  const void *src;
+  hipError_t e;
+  char *ws = repack_rows(params, logits, static_cast<char *>(workspace), &pr, &src,
+                         static_cast<hipStream_t>(stream), &e);
+  if (e != hipSuccess) return TSEL_ERR_LAUNCH;
   tsel::BeamArgs a{};
-  a.s = proc_args(params, logits, history, lens);
+  a.s = proc_args(&pr, src, history, lens);
   a.nb = num_beams;
   a.width = tsel_beam_width(num_beams, params->n_eos);
   a.first_step = first_step ? 1 : 0;
   a.beam_scores = beam_scores;
-  a.row_keys = static_cast<uint64_t *>(workspace);
+  a.row_keys = reinterpret_cast<uint64_t *>(ws);
   a.out_scores = out_scores;
   a.out_beams = out_beams;
   a.out_tokens = out_tokens;
-  hipError_t e = tsel::launch_beam(a, static_cast<hipStream_t>(stream));
+  e = tsel::launch_beam(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TSEL_OK : TSEL_ERR_LAUNCH;
 }
 

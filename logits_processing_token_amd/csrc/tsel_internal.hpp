@@ -155,6 +155,11 @@ hipError_t launch_verify_noalloc(const void *logits, int32_t dtype, int32_t B, i
                                  int32_t *next, int32_t *k_out, hipStream_t s);
 
 constexpr int kMaxFinishEos = 256;  // stop ids one end-of-step call takes
+// Rows of V elements (dtype 1: bf16, else fp32) at src_stride elements apart
+// copied to dst_stride elements apart (dst_stride * element size a multiple
+// of 16; the destination 16-byte aligned), zeros after each row's V.
+hipError_t launch_repack(const void *src, int32_t dtype, int64_t src_stride, void *dst,
+                         int64_t dst_stride, int32_t rows, int32_t V, hipStream_t s);
 hipError_t launch_finish(int32_t B, const int32_t *tokens, const int32_t *lens,
                          const int32_t *max_lengths, const int32_t *eos, int32_t n_eos,
                          uint8_t *finished, int32_t *out, hipStream_t s);

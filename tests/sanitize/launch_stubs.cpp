@@ -41,6 +41,10 @@ hipError_t launch_verify_noalloc(const void *, int32_t, int32_t, int32_t, int32_
                                  int32_t *, hipStream_t) {
   return hipSuccess;
 }
+hipError_t launch_repack(const void *, int32_t, int64_t, void *, int64_t, int32_t, int32_t,
+                         hipStream_t) {
+  return hipSuccess;
+}
 hipError_t launch_finish(int32_t, const int32_t *, const int32_t *, const int32_t *,
                          const int32_t *, int32_t, uint8_t *, int32_t *, hipStream_t) {
   return hipSuccess;

@@ -64,14 +64,31 @@ def _params(**kw):
     (dict(do_sample=True, top_p=1.5), tsel.TSEL_ERR_INVALID_ARG),
     (dict(do_sample=True, top_p=1.0, top_k=5, temperature=0.5), tsel.TSEL_OK),
     (dict(temperature=0.0), tsel.TSEL_OK),           # greedy ignores the warpers
-    (dict(vocab=1001, row_stride=1001), tsel.TSEL_ERR_UNSUPPORTED),  # 4004-byte rows
+    (dict(vocab=1001, row_stride=1001), tsel.TSEL_OK),  # 4004-byte rows: copied first
     (dict(vocab=1001, row_stride=1004), tsel.TSEL_OK),
     (dict(vocab=600000, row_stride=600000), tsel.TSEL_ERR_UNSUPPORTED),
-    (dict(dtype=tsel.TSEL_BF16, vocab=1004, row_stride=1004), tsel.TSEL_ERR_UNSUPPORTED),
+    (dict(dtype=tsel.TSEL_BF16, vocab=1004, row_stride=1004), tsel.TSEL_OK),
     (dict(dtype=tsel.TSEL_BF16, vocab=1004, row_stride=1008), tsel.TSEL_OK),
 ])
 def test_validate(kw, status):
     assert tsel.validate(_params(**kw)) == status
+
+
+def test_unaligned_rows_take_workspace():
+    """Rows whose byte stride is not a multiple of 16 are copied into the
+    workspace at the next such stride, ahead of everything else."""
+    lib = tsel.load()
+    for dt, V, es in ((tsel.TSEL_F32, 1001, 4), (tsel.TSEL_BF16, 50273, 2)):
+        al = _params(dtype=dt, vocab=V, row_stride=V + (-V) % (16 // es), batch=3)
+        un = _params(dtype=dt, vocab=V, row_stride=V, batch=3)
+        stride = V + (-V) % (16 // es)
+        copy = (3 * stride * es + 255) // 256 * 256
+        assert lib.tsel_process_select_workspace_size(C.byref(al)) == 0
+        assert lib.tsel_process_select_workspace_size(C.byref(un)) == copy
+        assert (lib.tsel_beam_step_workspace_size(C.byref(un), 3)
+                == copy + lib.tsel_beam_step_workspace_size(C.byref(al), 3))
+        assert (lib.tsel_verify_select_workspace_size(C.byref(un), 2)
+                > lib.tsel_verify_select_workspace_size(C.byref(al), 2))
 
 
 def test_eos_count_checked():
