@@ -13,12 +13,16 @@
 // then e ascending), so the best K are the K largest keys.  No key is 0, which
 // marks "no candidate".
 //
-//  * k_beam_rows, one workgroup per beam row: the row's largest logit m (one
-//    pass) and log(sum exp(x - m)) in binary64 (a second pass, exp_nonpos
-//    for the terms); the seen and
-//    removed ids as two bitmasks in LDS; then the row's best K keys, scores
-//    recomputed from the logits on every pass (16-byte loads; the row stays
-//    in L2 and nothing of size V is written).
+//  * k_beam_rows, one workgroup per beam row: the seen and removed ids as two
+//    bitmasks in LDS; a logit bound from a sample (the K-th largest logit of
+//    every lane's first chunk among ids neither removed nor seen); one pass
+//    for the row's largest logit m and log(sum exp(x - m)) in binary64
+//    (exp_nonpos for the terms) that also keeps on chip the ids at or above
+//    the bound; then the row's best K keys among those, rescored.  When the
+//    bound fails (too many kept, a sample smaller than K, or rounding that
+//    could tie a left-out id with the sample's K-th), the best K come from a
+//    second pass over the row, bounded by the sample's K-th key.  Nothing of
+//    size V is written.
 //  * k_beam_merge, one workgroup per prompt: the best K of its num_beams * K
 //    row keys, written as score, beam and id.
 //
@@ -223,45 +227,18 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   uint32_t *seen = bsm, *kill = bsm + mw;
   uint32_t *hist = bsm + ((2 * mw + 3) & ~3);
   uint64_t *cand = reinterpret_cast<uint64_t *>(hist + kBeamSelBins);
+  int32_t *kid = reinterpret_cast<int32_t *>(cand + kSelCap);  // ids the sum pass keeps
+  float *kx = reinterpret_cast<float *>(kid + kSelCap);        // and their logits
+  __shared__ int keep_n;
+  __shared__ float xf_s;
   for (int w = tid; w < 2 * mw; w += kBT) bsm[w] = 0u;
-  // The log-softmax's shift M (the row's largest finite logit) and sum S =
-  // sum exp(x - M), in binary64, in one pass: the terms are taken against
-  // M0, the largest logit of every lane's first chunk, and the sum is
-  // rescaled by exp(M0 - M) once M is known (one more rounding).  Should
-  // some logit lie more than 700 above M0 (a term could overflow), a second
-  // pass takes the terms against M itself.
-  const int epc0 = bf16 ? 8 : 4;
-  float m0 = -INFINITY;
-  if (tid < V / epc0) {
-    const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    for (int j = 0; j < epc0; ++j)
-      m0 = fmaxf(m0, bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
-                                     : __uint_as_float(w[j >> 1] << 16))
-                          : __uint_as_float(w[j]));
+  if (tid == 0) {
+    keep_n = 0;
+    xf_s = -INFINITY;
   }
-  for (int v = (V / epc0) * epc0 + tid; v < V; v += kBT)  // (the row tail)
-    m0 = fmaxf(m0, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
-                        : reinterpret_cast<const float *>(rowp)[v]);
-  const float M0 = block_max_f32<kBT>(m0, rmax);
-  float mloc = -INFINITY;
-  double sum = 0.0;
-  const double dM0 = M0 > -INFINITY ? (double)M0 : 0.0;
-  visit_row(rowp, bf16, V, [&](int, float x) {  // (-inf adds 0)
-    mloc = fmaxf(mloc, x);
-    const double d = (double)x - dM0;
-    sum += d <= 0.0 ? exp_nonpos(d) : exp(fmin(d, 710.0));
-  });
-  const float Mx = block_max_f32<kBT>(mloc, rmax);
-  double S;
-  if (Mx > -INFINITY && (double)Mx - dM0 > 700.0) {  // (rare: far above the first chunks)
-    sum = 0.0;
-    visit_row(rowp, bf16, V, [&](int, float x) { sum += exp_nonpos((double)x - (double)Mx); });
-    S = block_sum_f64<kBT>(sum, rsum);
-  } else {
-    S = block_sum_f64<kBT>(sum, rsum) * (Mx > -INFINITY ? exp(dM0 - (double)Mx) : 1.0);
-  }
-  // (the reductions' barriers order the clearing of the masks)
+  __syncthreads();
+  // ---- the processors' masks (LDS): seen ids; n-gram and minimum-length bans
+  // and the static masks as removals ----
   const int new_tokens = L - P;
   const bool begin_active =
       s.begin_mask != nullptr && new_tokens == ((s.forced_bos >= 0 && P == 1) ? 1 : 0);
@@ -305,6 +282,87 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
     kill[w] = k;
   }
   __syncthreads();
+  // ---- a logit bound from a sample: the K-th largest logit among every
+  // lane's first chunk's ids that are neither removed nor seen.  Those K ids
+  // score their plain log-probability, so an id whose logit lies below the
+  // bound far enough that even its plain score is lower (checked once the
+  // log-softmax is known) cannot be among the row's best K: the sum pass
+  // keeps the ids at or above the bound less a small slack, on chip. ----
+  const int epc = bf16 ? 8 : 4;
+  const int NGs = V / epc;
+  auto elem = [&](const uint4 &c, int j) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    return bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u) : __uint_as_float(w[j >> 1] << 16))
+                : __uint_as_float(w[j]);
+  };
+  bool bounded = false;
+  float xthr = INFINITY;
+  if (forced < 0) {
+    const int ns = select_top(
+        K,
+        [&](auto &&f) {
+          if (tid < NGs) {
+            const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
+            for (int j = 0; j < epc; ++j) {
+              const int v = tid * epc + j;
+              const float x = elem(c, j);
+              if (x > -INFINITY && !has_bit(kill, v) && !has_bit(seen, v))
+                f(((uint64_t)ordered32(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v));
+            }
+          }
+        },
+        [&](int rank, uint64_t k) {
+          if (rank == K - 1) xf_s = unordered32((uint32_t)(k >> 32));
+        },
+        hist, cand, ss);
+    __syncthreads();
+    bounded = ns == K && xf_s > -INFINITY;
+    if (bounded) xthr = xf_s - fmaxf(fabsf(xf_s) * 0x1p-12f, 0x1p-20f);
+  }
+  // The log-softmax's shift M (the row's largest finite logit) and sum S =
+  // sum exp(x - M), in binary64, in one pass: the terms are taken against
+  // M0, the largest logit of every lane's first chunk, and the sum is
+  // rescaled by exp(M0 - M) once M is known (one more rounding).  Should
+  // some logit lie more than 700 above M0 (a term could overflow), a second
+  // pass takes the terms against M itself.
+  const int epc0 = bf16 ? 8 : 4;
+  float m0 = -INFINITY;
+  if (tid < V / epc0) {
+    const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    for (int j = 0; j < epc0; ++j)
+      m0 = fmaxf(m0, bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
+                                     : __uint_as_float(w[j >> 1] << 16))
+                          : __uint_as_float(w[j]));
+  }
+  for (int v = (V / epc0) * epc0 + tid; v < V; v += kBT)  // (the row tail)
+    m0 = fmaxf(m0, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
+                        : reinterpret_cast<const float *>(rowp)[v]);
+  const float M0 = block_max_f32<kBT>(m0, rmax);
+  float mloc = -INFINITY;
+  double sum = 0.0;
+  const double dM0 = M0 > -INFINITY ? (double)M0 : 0.0;
+  visit_row(rowp, bf16, V, [&](int v, float x) {  // (-inf adds 0)
+    mloc = fmaxf(mloc, x);
+    const double d = (double)x - dM0;
+    sum += d <= 0.0 ? exp_nonpos(d) : exp(fmin(d, 710.0));
+    if (x >= xthr) {
+      const int slot = atomicAdd(&keep_n, 1);
+      if (slot < kSelCap) {
+        kid[slot] = v;
+        kx[slot] = x;
+      }
+    }
+  });
+  const float Mx = block_max_f32<kBT>(mloc, rmax);
+  double S;
+  if (Mx > -INFINITY && (double)Mx - dM0 > 700.0) {  // (rare: far above the first chunks)
+    sum = 0.0;
+    visit_row(rowp, bf16, V, [&](int, float x) { sum += exp_nonpos((double)x - (double)Mx); });
+    S = block_sum_f64<kBT>(sum, rsum);
+  } else {
+    S = block_sum_f64<kBT>(sum, rsum) * (Mx > -INFINITY ? exp(dM0 - (double)Mx) : 1.0);
+  }
   const bool any = Mx > -INFINITY;
   const float lsf = any ? (float)log(S) : 0.0f;
   const float s_beam = a.beam_scores[r];
@@ -350,6 +408,30 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
           if (tid == 0 && forced < V) f(key_of(forced, true_bits(forced, 0.0f)));
         },
         emit_row, hist, cand, ss);
+  } else if (bounded && keep_n <= kSelCap && plain_bits(nextafterf(xthr, -INFINITY)) < plain_bits(xf_s)) {
+    // Every id left out of the sum pass's list scores below the sample's K
+    // ids (whose scores are plain): the best K are among the list, rescored,
+    // and (a penalty below 1 raising them) the seen ids below the bound.
+    const int nk = keep_n;
+    const bool raise = s.rep < 1.0f;
+    keff = select_top(
+        K,
+        [&](auto &&f) {
+          for (int i = tid; i < nk; i += kBT) f(key_of(kid[i], true_bits(kid[i], kx[i])));
+          if (raise)
+            for (int w = tid; w < mw; w += kBT) {
+              uint32_t bits = seen[w] & ~kill[w];
+              while (bits) {
+                const int v = w * 32 + __ffs(bits) - 1;
+                bits &= bits - 1u;
+                const float x =
+                    bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
+                         : reinterpret_cast<const float *>(rowp)[v];
+                if (!(x >= xthr)) f(key_of(v, true_bits(v, x)));
+              }
+            }
+        },
+        emit_row, hist, cand, ss, true);
   } else {
     // A lower bound of the row's K-th key: the K-th largest key of a sample,
     // every lane's first 16-byte chunk.  Only keys at or above it can be
@@ -357,20 +439,14 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
     // sample is smaller than K and bounds nothing).
     __shared__ uint64_t t0_s;
     if (tid == 0) t0_s = 0ull;
-    const int epc = bf16 ? 8 : 4;
-    const int NGs = V / epc;
     const int ns = select_top(
         K,
         [&](auto &&f) {
           if (tid < NGs) {
             const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
-            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
             for (int j = 0; j < epc; ++j) {
-              const float x = bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
-                                              : __uint_as_float(w[j >> 1] << 16))
-                                   : __uint_as_float(w[j]);
               const int v = tid * epc + j;
-              f(key_of(v, true_bits(v, x)));
+              f(key_of(v, true_bits(v, elem(c, j))));
             }
           }
         },
@@ -450,7 +526,8 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_merge(BeamArgs a) {
 
 size_t beam_rows_lds(int32_t V) {
   const size_t mw = ((size_t)V + 31) / 32;
-  return (((2 * mw + 3) & ~size_t(3)) + kBeamSelBins) * 4 + (size_t)kSelCap * 8;
+  // masks, radix bins, the select's keys, the sum pass's kept ids and logits
+  return (((2 * mw + 3) & ~size_t(3)) + kBeamSelBins) * 4 + (size_t)kSelCap * 16;
 }
 
 hipError_t launch_beam(const BeamArgs &a, hipStream_t st) {
