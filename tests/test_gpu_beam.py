@@ -147,6 +147,29 @@ def test_beam_processors(dtype):
     _check(w)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beam_penalty_below_one(dtype):
+    """A penalty below 1 raises the seen ids' log-probabilities (all <= 0):
+    seen ids far down the row, left out of the pass's bounded list, can
+    enter the best K and are scored from the seen mask."""
+    w = _workload(53, 6, 4, 20000, dtype, dict(repetition_penalty=0.3, eos_token_ids=[4]),
+                  hist_len=64, hot_hist=False)
+    gpu = _check(w)
+    # (the case is reached: kept candidates that are seen ids of their beam,
+    # none of them among their row's 64 largest logits)
+    x = w["x"].astype(np.float32) if w["x"].dtype != np.uint16 else \
+        (w["x"].astype(np.uint32) << 16).view(np.float32)
+    raised = 0
+    for p in range(gpu["tokens"].shape[0]):
+        for b, t in zip(gpu["beams"][p], gpu["tokens"][p]):
+            if t < 0:
+                continue
+            r = p * w["nb"] + b
+            if t in w["hist"][r] and (x[r] > x[r, t]).sum() >= 64:
+                raised += 1
+    assert raised > 0
+
+
 def test_beam_first_step_and_short_vocab():
     w = _workload(41, 5, 4, 9000, "bf16", dict(repetition_penalty=1.2, eos_token_ids=[1]))
     _check(w, first_step=True)
