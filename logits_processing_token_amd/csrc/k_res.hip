@@ -389,7 +389,6 @@ __global__ __launch_bounds__(NT, 1) void k_res(SelectArgs a) {
   }
   __syncthreads();
   const int shi = uni(sh.bin_hi);
-  const double S_top = shi >= 0 ? uni(sh.sbase) : 0.0;
   int slo = uni(sh.found);
   if (slo < 0 || (bp >= 0 && slo < bp)) slo = bp >= 0 ? bp : shi;
 
