@@ -867,20 +867,23 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
     if (dense_pen && ((chunk_bits<DT>(s.smask, g) >> j) & 1u)) x = penalize(x, a.rep);
     return x;
   };
-  // Threshold from the first chunk of every lane: the k-th largest alive
-  // score among them, a lower bound of the row's.
+  // Threshold from the first chunk of every lane: a lower bound of the k-th
+  // largest alive score among them, hence of the row's.
+  // (a coarse bound: a lower one only lets more candidates in; the
+  // histogram borrows the candidate buffer, still empty: 24 tcap bytes)
   if (tid < NG) c0 = kill_chunk<DT>(c0, tid, s);
-  const uint32_t t0 = radix_kth_largest(
+  const int nbins = 24 * tcap >= 16 * NT ? 4 * NT : NT;
+  const float t0 = kth_lower_bound(
       [&](auto &&f) {
         if (tid < NG)
 #pragma unroll
           for (int j = 0; j < EPC; ++j) {
             const float x = prep(c0, tid, j);
-            if (x > -INFINITY) f(ordered_f32(x));
+            if (x > -INFINITY) f(x);
           }
       },
-      k_eff, s.rhist, sh);
-  if (tid == 0) sh.tau_x = pre_temperature_floor(t0 == 0u ? -INFINITY : unordered_f32(t0), T);
+      k_eff, reinterpret_cast<uint32_t *>(s.area), nbins, sh);
+  if (tid == 0) sh.tau_x = pre_temperature_floor(t0, T);
   __syncthreads();
   float flt = sh.tau_x;
   if (tid < NG)

@@ -212,6 +212,84 @@ __device__ __forceinline__ uint32_t radix_kth_largest(Visit &&visit, int k, uint
   return prefix;
 }
 
+// A lower bound of the k-th largest of the values that visit(f) passes to
+// f (every thread calls; values above -inf): the values are counted into
+// nbins (NT, 2 NT or 4 NT) equal-width bins spanning their minimum to
+// maximum (spread out, so the LDS adds rarely meet on one word), and the
+// bound is the lower edge of the bin one below the one holding the k-th
+// largest (a bin of slack for the rounding of the bin arithmetic).  -inf
+// when there are fewer than k values.  hist: nbins words.
+template <class Visit>
+__device__ __forceinline__ float kth_lower_bound(Visit &&visit, int k, uint32_t *hist, int nbins,
+                                                 RowShared &sh) {
+  const int tid = threadIdx.x;
+  float lmax = -INFINITY, lmin = INFINITY;
+  int lcnt = 0;
+  visit([&](float x) {
+    lmax = fmaxf(lmax, x);
+    lmin = fminf(lmin, x);
+    ++lcnt;
+  });
+  for (int i = tid; i < nbins; i += NT) hist[i] = 0u;
+  // the maximum, minimum and count in one exchange (one barrier; the scan
+  // below passes a barrier before it writes these slots again)
+  {
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    const float wmx = wave_max_f32_uni(lmax), wmn = -wave_max_f32_uni(-lmin);
+    const int wc = __builtin_amdgcn_readlane(wave_incl_scan_i32(lcnt), kWave - 1);
+    if (lane == 0) {
+      sh.red_f32[wid] = wmx;
+      sh.red_u64[wid] = __float_as_uint(wmn);
+      sh.red_i32[wid] = wc;
+    }
+  }
+  __syncthreads();
+  float mx = -INFINITY, mn = INFINITY;
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < NT / kWave; ++q) {
+    mx = fmaxf(mx, sh.red_f32[q]);
+    mn = fminf(mn, __uint_as_float((uint32_t)sh.red_u64[q]));
+    n += sh.red_i32[q];
+  }
+  if (n < k || k < 1) return -INFINITY;
+  if (!(mx > mn)) return mn;
+  const float scale = (float)(nbins - 1) / (mx - mn);  // (0 if the span overflows)
+  visit([&](float x) {
+    const int b = min(max((int)((x - mn) * scale), 0), nbins - 1);
+    atomicAdd(&hist[b], 1u);
+  });
+  __syncthreads();
+  // thread t holds bins nbins - 1 - bpt t downwards (from the top); the
+  // counts above its bins by an exclusive scan over threads
+  const int bpt = nbins / NT;
+  const int top = nbins - 1 - bpt * tid;
+  uint32_t c[4];
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = q < bpt ? hist[top - q] : 0u;
+    mine += (int)c[q];
+  }
+  int total;
+  int above = block_excl_scan_i32<NT>(mine, sh.red_i32, &total);
+  if (tid == 0) sh.found = 0;
+  __syncthreads();
+  if (above < k && k <= above + mine) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      above += (int)c[q];
+      if (above >= k) {
+        sh.found = top - q;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int b = sh.found;
+  return b <= 1 || scale == 0.0f ? mn : mn + (float)(b - 1) / scale;
+}
+
 // ---------------------------------------------------------------------------
 // Row prologue: padding rows (no token) and forced rows (forced_bos at one
 // token, forced_eos at max_length - 1; the later processor wins; a forced id
