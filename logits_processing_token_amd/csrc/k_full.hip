@@ -862,23 +862,27 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
     if (slot < tcap) { cx[slot] = x; ci[slot] = v; }
     else sh.overflow = 1;
   };
-  auto prep = [&](const uint4 &c, int g, int j) {
+  // element j of a chunk whose stream-penalty bits are sb (read once per
+  // chunk: a read per element would wait behind the appends' LDS adds)
+  auto prep = [&](const uint4 &c, uint32_t sb, int j) {
     float x = E::get(c, j);
-    if (dense_pen && ((chunk_bits<DT>(s.smask, g) >> j) & 1u)) x = penalize(x, a.rep);
+    if ((sb >> j) & 1u) x = penalize(x, a.rep);
     return x;
   };
+  auto pen_bits = [&](int g) { return dense_pen ? chunk_bits<DT>(s.smask, g) : 0u; };
   // Threshold from the first chunk of every lane: a lower bound of the k-th
   // largest alive score among them, hence of the row's.
   // (a coarse bound: a lower one only lets more candidates in; the
   // histogram borrows the candidate buffer, still empty: 24 tcap bytes)
   if (tid < NG) c0 = kill_chunk<DT>(c0, tid, s);
+  const uint32_t sb0 = tid < NG ? pen_bits(tid) : 0u;
   const int nbins = 24 * tcap >= 16 * NT ? 4 * NT : NT;
   const float t0 = kth_lower_bound(
       [&](auto &&f) {
         if (tid < NG)
 #pragma unroll
           for (int j = 0; j < EPC; ++j) {
-            const float x = prep(c0, tid, j);
+            const float x = prep(c0, sb0, j);
             if (x > -INFINITY) f(x);
           }
       },
@@ -889,7 +893,7 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
   if (tid < NG)
 #pragma unroll
     for (int j = 0; j < EPC; ++j) {
-      const float x = prep(c0, tid, j);
+      const float x = prep(c0, sb0, j);
       if (x > -INFINITY && x >= flt) append(tid * EPC + j, x);
     }
   for (int i = tid; i < n_list; i += NT)
@@ -908,9 +912,10 @@ __global__ __launch_bounds__(NT, 1) void k_topk(SelectArgs a, SelectArgs af) {
       const int g = t0g + tid + u * NT;
       if (g < NG) {
         const uint4 ck = kill_chunk<DT>(c[u], g, s);
+        const uint32_t sb = pen_bits(g);
 #pragma unroll
         for (int j = 0; j < EPC; ++j) {
-          const float x = prep(ck, g, j);
+          const float x = prep(ck, sb, j);
           if (x > -INFINITY && x >= flt) append(g * EPC + j, x);
         }
       }
