@@ -36,6 +36,7 @@
 #include <stdint.h>
 
 #include "tsel_device.hpp"
+#include "k_vkey.hpp"
 #include "tsel_internal.hpp"
 
 namespace tsel {
@@ -342,10 +343,34 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   float mloc = -INFINITY;
   double sum = 0.0;
   const double dM0 = M0 > -INFINITY ? (double)M0 : 0.0;
+  auto term = [&](double d) { return d <= 0.0 ? exp_nonpos(d) : exp(fmin(d, 710.0)); };
+  // bf16 rows: each logit adds 1 to a bin per bf16 value, and the sum takes
+  // one exponential per bin (count times it) instead of one per logit.  The
+  // bins run from the value 746 below M0 (every term below underflows to 0)
+  // up; near-zero logits (one key for a range of values) and logits past
+  // the bins take their own term.  The select's radix bins are free during
+  // the pass and hold two copies (by lane parity).
+  static_assert(2 * kVStride <= kBeamSelBins, "two copies of the value bins");
+  const bool vsum = bf16 && M0 > -INFINITY;
+  uint32_t klo = 0u, khi = 0u;
+  uint32_t *vbl = hist + (tid & 1) * kVStride;
+  if (vsum) {
+    klo = max(vkey_floor(M0 - 746.0f), kKeyLowFinite);
+    khi = klo + (uint32_t)(kVBins - 1);
+    for (int i = tid; i < 2 * kVStride; i += kBT) hist[i] = 0u;
+    __syncthreads();
+  }
   visit_row(rowp, bf16, V, [&](int v, float x) {  // (-inf adds 0)
     mloc = fmaxf(mloc, x);
-    const double d = (double)x - dM0;
-    sum += d <= 0.0 ? exp_nonpos(d) : exp(fmin(d, 710.0));
+    if (vsum) {
+      const uint32_t k = vkey(__float_as_uint(x) >> 16);
+      if (k != kKeyZoneNeg && k != kKeyZonePos && k < khi)
+        atomicAdd(&vbl[k >= klo ? k - klo + 1u : 0u], 1u);  // (bin 0: below the bins, no term)
+      else
+        sum += term((double)x - dM0);
+    } else {
+      sum += term((double)x - dM0);
+    }
     if (x >= xthr) {
       const int slot = atomicAdd(&keep_n, 1);
       if (slot < kSelCap) {
@@ -354,7 +379,14 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
       }
     }
   });
-  const float Mx = block_max_f32<kBT>(mloc, rmax);
+  const float Mx = block_max_f32<kBT>(mloc, rmax);  // (its barriers end the counting)
+  if (vsum)
+    for (int b = 1 + tid; b < kVBins; b += kBT) {
+      const uint32_t n = hist[b] + hist[kVStride + b];
+      const uint32_t kb = klo + (uint32_t)b - 1u;
+      if (n != 0u && kb != kKeyZoneNeg && kb != kKeyZonePos)
+        sum += (double)n * term((double)vkey_value(kb) - dM0);
+    }
   double S;
   if (Mx > -INFINITY && (double)Mx - dM0 > 700.0) {  // (rare: far above the first chunks)
     sum = 0.0;
