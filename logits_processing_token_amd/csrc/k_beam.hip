@@ -14,8 +14,8 @@
 // marks "no candidate".
 //
 //  * k_beam_rows, one workgroup per beam row: the seen and removed ids as two
-//    bitmasks in LDS; a logit bound from a sample (the K-th largest logit of
-//    every lane's first chunk among ids neither removed nor seen); one pass
+//    bitmasks in LDS; a logit bound from a sample, every lane's first chunk
+//    (K of its ids neither removed nor seen lie at or above it); one pass
 //    for the row's largest logit m and log(sum exp(x - m)) in binary64
 //    (exp_nonpos for the terms) that also keeps on chip the ids at or above
 //    the bound; then the row's best K keys among those, rescored.  When the
@@ -159,51 +159,109 @@ __device__ __forceinline__ int select_top(int K, Visit visit, EmitFn emit, uint3
   return keff;
 }
 
-// f(v, x) for every element v of a row (16-byte rows: whole chunks of 8
-// bf16 or 4 fp32 per load, then the tail), x widened to binary32.  Two
-// batches of four chunks per lane: the next batch's loads fly while this one
-// is consumed.
+// The row's whole 16-byte chunks, each passed to consume(c, g) (g the
+// chunk's index) by the lane that loads it: lane t takes chunks t, t + kBT,
+// ...  in batches of kVB per lane, the batches' registers alternating
+// between two sets so that a batch's loads fly while the one before it is
+// consumed.  Buffer loads read 0 past the chunks, so no branch guards them
+// and the wait before a batch is for that batch alone.
 constexpr int kVB = 4;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <class C>
+__device__ __forceinline__ void stream_chunks(const char *rowp, int NG, C &&consume) {
+  constexpr int S = kBT * kVB;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, NG * 16, 0x00020000);
+  const int nb = (NG + S - 1) / S;
+  u32x4_t p[kVB], q[kVB];
+  auto load = [&](u32x4_t (&d)[kVB], int b) {
+#pragma unroll
+    for (int u = 0; u < kVB; ++u)
+      d[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (b * S + u * kBT + tid) * 16, 0, 0);
+  };
+  auto use = [&](const u32x4_t (&d)[kVB], int b) {
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int g = b * S + u * kBT + tid;
+      if (g < NG) consume(d[u], g);
+    }
+  };
+  load(p, 0);
+  for (int b = 0; b < nb; b += 2) {
+    load(q, b + 1);
+    use(p, b);
+    load(p, b + 2);
+    use(q, b + 1);
+  }
+}
+
+// f(v, x) for every element v of a row (16-byte rows: whole chunks of 8
+// bf16 or 4 fp32, then the tail), x widened to binary32.
 template <class F>
 __device__ __forceinline__ void visit_row(const char *rowp, bool bf16, int V, F &&f) {
   const int tid = threadIdx.x;
   const int epc = bf16 ? 8 : 4;
   const int NG = V / epc;
-  auto consume = [&](const uint4 &c, int g) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  stream_chunks(rowp, NG, [&](const u32x4_t &c, int g) {
     if (bf16) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        f(g * 8 + j, (j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
-                             : __uint_as_float(w[j >> 1] << 16));
+        f(g * 8 + j, (j & 1) ? __uint_as_float(c[j >> 1] & 0xFFFF0000u)
+                             : __uint_as_float(c[j >> 1] << 16));
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f(g * 4 + j, __uint_as_float(w[j]));
+      for (int j = 0; j < 4; ++j) f(g * 4 + j, __uint_as_float(c[j]));
     }
-  };
-  uint4 c[kVB], nx[kVB];
-#pragma unroll
-  for (int u = 0; u < kVB; ++u) {
-    const int g = tid + u * kBT;
-    if (g < NG) c[u] = *reinterpret_cast<const uint4 *>(rowp + (int64_t)g * 16);
-  }
-  for (int g0 = tid; g0 < NG; g0 += kBT * kVB) {
-#pragma unroll
-    for (int u = 0; u < kVB; ++u) {
-      const int g = g0 + kBT * kVB + u * kBT;
-      if (g < NG) nx[u] = *reinterpret_cast<const uint4 *>(rowp + (int64_t)g * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < kVB; ++u) {
-      const int g = g0 + u * kBT;
-      if (g < NG) consume(c[u], g);
-    }
-#pragma unroll
-    for (int u = 0; u < kVB; ++u) c[u] = nx[u];
-  }
+  });
   for (int v = NG * epc + tid; v < V; v += kBT)
     f(v, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
               : reinterpret_cast<const float *>(rowp)[v]);
+}
+
+// The counting pass of a bf16 row: every element adds 1 to the bin of its
+// value key k (vkey), clamped to [lo, hi]: bins[k - lo] (bin 0 takes the
+// keys below lo, bin hi - lo the keys at or above hi).  A 16-byte chunk
+// with an element on a near-zero key or at or above `spec` has
+// special(v, x, k, t) called for each of those elements by the lane that
+// holds it (t = 0 on the near-zero keys), and so has every element of the
+// row tail.
+template <class Special>
+__device__ __forceinline__ void count_row_bf16(const char *rowp, int V, uint32_t *bins, uint32_t lo,
+                                               uint32_t hi, uint32_t spec, Special &&special) {
+  const int tid = threadIdx.x;
+  const int NG = V / 8;
+  auto key = [&](uint32_t hw, uint32_t &t) {  // hw: the bf16 pattern in the low 16 bits
+    const uint32_t m = hw & 0x7FFFu;
+    t = m > kZoneMag ? m - kZoneMag : 0u;
+    const uint32_t sgn = 0u - ((hw >> 15) & 1u);  // all ones for a negative value
+    return (t ^ sgn) + 0x8000u;                    // 0x8000 + t, or 0x7FFF - t
+  };
+  stream_chunks(rowp, NG, [&](const u32x4_t &w, int g) {
+    bool odd = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t t;
+      const uint32_t k = key((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1], t);
+      atomicAdd(&bins[min(max(k, lo), hi) - lo], 1u);
+      odd |= (k >= spec) | (t == 0u);
+    }
+    if (odd)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t hw = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+        uint32_t t;
+        const uint32_t k = key(hw, t);
+        if (k >= spec || t == 0u) special(g * 8 + j, __uint_as_float(hw << 16), k, t);
+      }
+  });
+  for (int v = NG * 8 + tid; v < V; v += kBT) {  // (the row tail: every element special)
+    const uint32_t hw = reinterpret_cast<const uint16_t *>(rowp)[v];
+    uint32_t t;
+    const uint32_t k = key(hw, t);
+    atomicAdd(&bins[min(max(k, lo), hi) - lo], 1u);
+    special(v, __uint_as_float(hw << 16), k, t);
+  }
 }
 
 }  // namespace
@@ -232,14 +290,9 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   float *kx = reinterpret_cast<float *>(kid + kSelCap);        // and their logits
   __shared__ int keep_n;
   __shared__ float xf_s;
-  for (int w = tid; w < 2 * mw; w += kBT) bsm[w] = 0u;
-  if (tid == 0) {
-    keep_n = 0;
-    xf_s = -INFINITY;
-  }
-  __syncthreads();
-  // ---- the processors' masks (LDS): seen ids; n-gram and minimum-length bans
-  // and the static masks as removals ----
+  __shared__ float wmax_s[2][kBT / kWave];
+  constexpr int NW = kBT / kWave;
+  const int lane = tid & (kWave - 1);
   const int new_tokens = L - P;
   const bool begin_active =
       s.begin_mask != nullptr && new_tokens == ((s.forced_bos >= 0 && P == 1) ? 1 : 0);
@@ -248,10 +301,49 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   if (s.forced_eos >= 0 && L == M - 1) forced = s.forced_eos;
   const int32_t *h = s.hist + (int64_t)r * s.hist_stride;
   const int Lh = L < s.hist_stride ? L : s.hist_stride;  // (ids past the stride are not the row's)
+  const int epc = bf16 ? 8 : 4;
+  const int NGs = V / epc;
+  // every lane's first 16-byte chunk of the row (the sample below), in
+  // flight while the masks are built
+  uint4 c0 = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < NGs) c0 = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
+  // ---- the processors' masks (LDS): seen ids; the static masks, n-gram and
+  // minimum-length bans as removals (the removals start as the static
+  // masks; four words of each per lane are loaded at once) ----
+  for (int w0 = tid; w0 < mw; w0 += 4 * kBT) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int w = w0 + u * kBT;
+      k[u] = 0u;
+      if (w < mw) {
+        if (s.bad_mask) k[u] |= s.bad_mask[w];
+        if (s.sup_mask) k[u] |= s.sup_mask[w];
+        if (begin_active) k[u] |= s.begin_mask[w];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int w = w0 + u * kBT;
+      if (w < mw) {
+        seen[w] = 0u;
+        kill[w] = k[u];
+      }
+    }
+  }
+  if (tid == 0) {
+    keep_n = 0;
+    xf_s = -INFINITY;
+  }
+  __syncthreads();
   if (forced < 0) {
-    for (int i = tid; i < Lh; i += kBT) {
-      const int v = h[i];
-      if (v >= 0 && v < V) atomicOr(&seen[v >> 5], 1u << (v & 31));
+    for (int i0 = tid; i0 < Lh; i0 += 4 * kBT) {
+      int hv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hv[u] = i0 + u * kBT < Lh ? h[i0 + u * kBT] : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (hv[u] >= 0 && hv[u] < V) atomicOr(&seen[hv[u] >> 5], 1u << (hv[u] & 31));
     }
     const int n = s.ngram;
     if (n > 0 && Lh >= n) {  // window i bans its last id when its head is the history's tail
@@ -275,75 +367,91 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   bool forced_alive = forced >= 0 && forced < V;
   if (forced_alive && s.sup_mask && has_bit(s.sup_mask, forced)) forced_alive = false;
   if (forced_alive && begin_active && has_bit(s.begin_mask, forced)) forced_alive = false;
-  for (int w = tid; w < mw; w += kBT) {
-    uint32_t k = kill[w];
-    if (s.bad_mask) k |= s.bad_mask[w];
-    if (s.sup_mask) k |= s.sup_mask[w];
-    if (begin_active) k |= s.begin_mask[w];
-    kill[w] = k;
-  }
-  __syncthreads();
-  // ---- a logit bound from a sample: the K-th largest logit among every
-  // lane's first chunk's ids that are neither removed nor seen.  Those K ids
-  // score their plain log-probability, so an id whose logit lies below the
-  // bound far enough that even its plain score is lower (checked once the
-  // log-softmax is known) cannot be among the row's best K: the sum pass
-  // keeps the ids at or above the bound less a small slack, on chip. ----
-  const int epc = bf16 ? 8 : 4;
-  const int NGs = V / epc;
   auto elem = [&](const uint4 &c, int j) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     return bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u) : __uint_as_float(w[j >> 1] << 16))
                 : __uint_as_float(w[j]);
   };
-  bool bounded = false;
-  float xthr = INFINITY;
-  if (forced < 0) {
-    const int ns = select_top(
-        K,
-        [&](auto &&f) {
-          if (tid < NGs) {
-            const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
-            for (int j = 0; j < epc; ++j) {
-              const int v = tid * epc + j;
-              const float x = elem(c, j);
-              if (x > -INFINITY && !has_bit(kill, v) && !has_bit(seen, v))
-                f(((uint64_t)ordered32(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v));
-            }
-          }
-        },
-        [&](int rank, uint64_t k) {
-          if (rank == K - 1) xf_s = unordered32((uint32_t)(k >> 32));
-        },
-        hist, cand, ss);
-    __syncthreads();
-    bounded = ns == K && xf_s > -INFINITY;
-    if (bounded) xthr = xf_s - fmaxf(fabsf(xf_s) * 0x1p-12f, 0x1p-20f);
-  }
-  // The log-softmax's shift M (the row's largest finite logit) and sum S =
-  // sum exp(x - M), in binary64, in one pass: the terms are taken against
-  // M0, the largest logit of every lane's first chunk, and the sum is
-  // rescaled by exp(M0 - M) once M is known (one more rounding).  Should
-  // some logit lie more than 700 above M0 (a term could overflow), a second
-  // pass takes the terms against M itself.
-  const int epc0 = bf16 ? 8 : 4;
-  float m0 = -INFINITY;
-  if (tid < V / epc0) {
-    const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    for (int j = 0; j < epc0; ++j)
-      m0 = fmaxf(m0, bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u)
-                                     : __uint_as_float(w[j >> 1] << 16))
-                          : __uint_as_float(w[j]));
-  }
-  for (int v = (V / epc0) * epc0 + tid; v < V; v += kBT)  // (the row tail)
+  // ---- from the sample, in one exchange: M0, the largest logit of the
+  // first chunks and the row tail (the log-softmax's provisional shift),
+  // and each wave's largest logit among its sample ids that are neither
+  // removed nor seen ----
+  float m0 = -INFINITY, me = -INFINITY;
+  if (tid < NGs)
+    for (int j = 0; j < epc; ++j) {
+      const int v = tid * epc + j;
+      const float x = elem(c0, j);
+      m0 = fmaxf(m0, x);
+      if (x > -INFINITY && !has_bit(kill, v) && !has_bit(seen, v)) me = fmaxf(me, x);
+    }
+  for (int v = NGs * epc + tid; v < V; v += kBT)  // (the row tail)
     m0 = fmaxf(m0, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
                         : reinterpret_cast<const float *>(rowp)[v]);
-  const float M0 = block_max_f32<kBT>(m0, rmax);
+  {
+    const float wm = wave_max_f32_uni(m0), we = wave_max_f32_uni(me);
+    if (lane == 0) {
+      wmax_s[0][tid / kWave] = wm;
+      wmax_s[1][tid / kWave] = we;
+    }
+  }
+  __syncthreads();
+  float M0 = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < NW; ++q) M0 = fmaxf(M0, wmax_s[0][q]);
+  // ---- a logit bound from the sample, xf: K ids of the sample that are
+  // neither removed nor seen have logits at or above it.  Those K score
+  // their plain log-probability, so an id whose logit lies below xf far
+  // enough that even its plain score is lower (checked once the log-softmax
+  // is known) cannot be among the row's best K: the sum pass keeps the ids
+  // at or above xf less a small slack, on chip.  For K up to the number of
+  // waves, xf is the K-th largest of the waves' maxima (each held by an id
+  // of its own wave); else the K-th largest of the sample itself. ----
+  bool bounded = false;
+  float xthr = INFINITY, xf = -INFINITY;
+  if (forced < 0) {
+    if (K <= NW) {
+      const float wv = lane < NW ? wmax_s[1][lane] : -INFINITY;
+      int rank = 0;  // (equal maxima ranked by wave)
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const float o = wmax_s[1][q];
+        rank += (o > wv || (o == wv && q < lane)) ? 1 : 0;
+      }
+      const uint64_t hit = __ballot(lane < NW && rank == K - 1);  // (one lane)
+      xf = wmax_s[1][__ffsll((unsigned long long)hit) - 1];
+    } else {
+      const int ns = select_top(
+          K,
+          [&](auto &&f) {
+            if (tid < NGs)
+              for (int j = 0; j < epc; ++j) {
+                const int v = tid * epc + j;
+                const float x = elem(c0, j);
+                if (x > -INFINITY && !has_bit(kill, v) && !has_bit(seen, v))
+                  f(((uint64_t)ordered32(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v));
+              }
+          },
+          [&](int rank, uint64_t k) {
+            if (rank == K - 1) xf_s = unordered32((uint32_t)(k >> 32));
+          },
+          hist, cand, ss);
+      __syncthreads();
+      xf = ns == K ? xf_s : -INFINITY;
+    }
+    bounded = xf > -INFINITY;
+    if (bounded) xthr = xf - fmaxf(fabsf(xf) * 0x1p-12f, 0x1p-20f);
+  }
   float mloc = -INFINITY;
   double sum = 0.0;
   const double dM0 = M0 > -INFINITY ? (double)M0 : 0.0;
-  auto term = [&](double d) { return d <= 0.0 ? exp_nonpos(d) : exp(fmin(d, 710.0)); };
+  // e^d: exp_nonpos for d <= 0; above (a logit over M0), e^(d - 700) e^700,
+  // enough up to d = 700 (past that the sum is taken again against the
+  // row's maximum): one polynomial either way.
+  auto term = [&](double d) {
+    const bool neg = d <= 0.0;
+    const double e = exp_nonpos(neg ? d : fmin(d, 700.0) - 700.0);
+    return neg ? e : e * 0x1.d945df4f8ec8ep+1009;  // (e^700)
+  };
   // bf16 rows: each logit adds 1 to a bin per bf16 value, and the sum takes
   // one exponential per bin (count times it) instead of one per logit.  The
   // bins run from the value 746 below M0 (every term below underflows to 0)
@@ -360,17 +468,7 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
     for (int i = tid; i < 2 * kVStride; i += kBT) hist[i] = 0u;
     __syncthreads();
   }
-  visit_row(rowp, bf16, V, [&](int v, float x) {  // (-inf adds 0)
-    mloc = fmaxf(mloc, x);
-    if (vsum) {
-      const uint32_t k = vkey(__float_as_uint(x) >> 16);
-      if (k != kKeyZoneNeg && k != kKeyZonePos && k < khi)
-        atomicAdd(&vbl[k >= klo ? k - klo + 1u : 0u], 1u);  // (bin 0: below the bins, no term)
-      else
-        sum += term((double)x - dM0);
-    } else {
-      sum += term((double)x - dM0);
-    }
+  auto keep = [&](int v, float x) {
     if (x >= xthr) {
       const int slot = atomicAdd(&keep_n, 1);
       if (slot < kSelCap) {
@@ -378,15 +476,35 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
         kx[slot] = x;
       }
     }
-  });
-  const float Mx = block_max_f32<kBT>(mloc, rmax);  // (its barriers end the counting)
-  if (vsum)
+  };
+  if (vsum) {
+    // the keys at or above kspec include every logit at or above xthr
+    const uint32_t kspec = min(vkey_floor(xthr), khi);
+    count_row_bf16(rowp, V, vbl, klo - 1u, khi, kspec, [&](int v, float x, uint32_t k, uint32_t t) {
+      if (t == 0u || k >= khi) {  // (not in a bin the sum reads)
+        mloc = fmaxf(mloc, x);
+        sum += term((double)x - dM0);
+      }
+      keep(v, x);
+    });
+    __syncthreads();
     for (int b = 1 + tid; b < kVBins; b += kBT) {
       const uint32_t n = hist[b] + hist[kVStride + b];
       const uint32_t kb = klo + (uint32_t)b - 1u;
-      if (n != 0u && kb != kKeyZoneNeg && kb != kKeyZonePos)
-        sum += (double)n * term((double)vkey_value(kb) - dM0);
+      if (n != 0u && kb != kKeyZoneNeg && kb != kKeyZonePos) {
+        const float xb = vkey_value(kb);
+        mloc = fmaxf(mloc, xb);
+        sum += (double)n * term((double)xb - dM0);
+      }
     }
+  } else {
+    visit_row(rowp, bf16, V, [&](int v, float x) {  // (-inf adds 0)
+      mloc = fmaxf(mloc, x);
+      sum += term((double)x - dM0);
+      keep(v, x);
+    });
+  }
+  const float Mx = block_max_f32<kBT>(mloc, rmax);
   double S;
   if (Mx > -INFINITY && (double)Mx - dM0 > 700.0) {  // (rare: far above the first chunks)
     sum = 0.0;
@@ -440,7 +558,7 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
           if (tid == 0 && forced < V) f(key_of(forced, true_bits(forced, 0.0f)));
         },
         emit_row, hist, cand, ss);
-  } else if (bounded && keep_n <= kSelCap && plain_bits(nextafterf(xthr, -INFINITY)) < plain_bits(xf_s)) {
+  } else if (bounded && keep_n <= kSelCap && plain_bits(nextafterf(xthr, -INFINITY)) < plain_bits(xf)) {
     // Every id left out of the sum pass's list scores below the sample's K
     // ids (whose scores are plain): the best K are among the list, rescored,
     // and (a penalty below 1 raising them) the seen ids below the bound.
