@@ -24,7 +24,8 @@
 //    second pass over the row, bounded by the sample's K-th key.  Nothing of
 //    size V is written.
 //  * k_beam_merge, one workgroup per prompt: the best K of its num_beams * K
-//    row keys, written as score, beam and id.
+//    row keys, written as score, beam and id (k_beam_merge_wave, one wave,
+//    when those keys number at most 64).
 //
 // Both select with the same routine: a radix select over the keys, 12 bits
 // then 13 at a time from the top, stopping as soon as the keys at or above
@@ -58,6 +59,29 @@ __device__ __forceinline__ float unordered32(uint32_t k) {
 }
 __device__ __forceinline__ bool has_bit(const uint32_t *m, int v) {
   return (m[v >> 5] >> (v & 31)) & 1u;
+}
+
+// The wave's largest key, on every lane: row moves (quad swaps, half-row and
+// row mirrors, then the row broadcasts) on both halves, read from the last
+// lane.
+template <int C, int RM>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, C, RM, 0xF, false);
+  const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, C, RM, 0xF, false);
+  const uint64_t w = ((uint64_t)h2 << 32) | l2;
+  return w > v ? w : v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64_uni(uint64_t v) {
+  v = dpp_max_u64<0xB1, 0xF>(v);
+  v = dpp_max_u64<0x4E, 0xF>(v);
+  v = dpp_max_u64<0x141, 0xF>(v);
+  v = dpp_max_u64<0x140, 0xF>(v);
+  v = dpp_max_u64<0x142, 0xA>(v);
+  v = dpp_max_u64<0x143, 0xC>(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, kWave - 1);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), kWave - 1);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // The largest min(K, present keys) of the keys visit(f) passes to f, one
@@ -164,22 +188,25 @@ __device__ __forceinline__ int select_top(int K, Visit visit, EmitFn emit, uint3
 // ...  in batches of kVB per lane, the batches' registers alternating
 // between two sets so that a batch's loads fly while the one before it is
 // consumed.  Buffer loads read 0 past the chunks, so no branch guards them
-// and the wait before a batch is for that batch alone.
+// and the wait before a batch is for that batch alone.  p holds batch 0,
+// asked for by the caller (load_batch(rs, p, 0)).
 constexpr int kVB = 4;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const char *rowp, int NG) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, NG * 16, 0x00020000);
+}
+__device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t rs, u32x4_t (&d)[kVB], int b) {
+#pragma unroll
+  for (int u = 0; u < kVB; ++u)
+    d[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((b * kVB + u) * kBT + (int)threadIdx.x) * 16, 0, 0);
+}
 template <class C>
-__device__ __forceinline__ void stream_chunks(const char *rowp, int NG, C &&consume) {
+__device__ __forceinline__ void stream_chunks(__amdgpu_buffer_rsrc_t rs, int NG, u32x4_t (&p)[kVB],
+                                              C &&consume) {
   constexpr int S = kBT * kVB;
   const int tid = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rowp), (short)0, NG * 16, 0x00020000);
   const int nb = (NG + S - 1) / S;
-  u32x4_t p[kVB], q[kVB];
-  auto load = [&](u32x4_t (&d)[kVB], int b) {
-#pragma unroll
-    for (int u = 0; u < kVB; ++u)
-      d[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (b * S + u * kBT + tid) * 16, 0, 0);
-  };
+  u32x4_t q[kVB];
   auto use = [&](const u32x4_t (&d)[kVB], int b) {
 #pragma unroll
     for (int u = 0; u < kVB; ++u) {
@@ -187,23 +214,24 @@ __device__ __forceinline__ void stream_chunks(const char *rowp, int NG, C &&cons
       if (g < NG) consume(d[u], g);
     }
   };
-  load(p, 0);
   for (int b = 0; b < nb; b += 2) {
-    load(q, b + 1);
+    load_batch(rs, q, b + 1);
     use(p, b);
-    load(p, b + 2);
+    load_batch(rs, p, b + 2);
     use(q, b + 1);
   }
 }
 
 // f(v, x) for every element v of a row (16-byte rows: whole chunks of 8
-// bf16 or 4 fp32, then the tail), x widened to binary32.
+// bf16 or 4 fp32, then the tail), x widened to binary32; p: the row's batch
+// 0, asked for through rs = chunk_rsrc(rowp, V / (8 or 4)).
 template <class F>
-__device__ __forceinline__ void visit_row(const char *rowp, bool bf16, int V, F &&f) {
+__device__ __forceinline__ void visit_row(const char *rowp, bool bf16, int V, __amdgpu_buffer_rsrc_t rs,
+                                          u32x4_t (&p)[kVB], F &&f) {
   const int tid = threadIdx.x;
   const int epc = bf16 ? 8 : 4;
   const int NG = V / epc;
-  stream_chunks(rowp, NG, [&](const u32x4_t &c, int g) {
+  stream_chunks(rs, NG, p, [&](const u32x4_t &c, int g) {
     if (bf16) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -218,6 +246,13 @@ __device__ __forceinline__ void visit_row(const char *rowp, bool bf16, int V, F 
     f(v, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
               : reinterpret_cast<const float *>(rowp)[v]);
 }
+template <class F>
+__device__ __forceinline__ void visit_row(const char *rowp, bool bf16, int V, F &&f) {
+  const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(rowp, V / (bf16 ? 8 : 4));
+  u32x4_t p[kVB];
+  load_batch(rs, p, 0);
+  visit_row(rowp, bf16, V, rs, p, f);
+}
 
 // The counting pass of a bf16 row: every element adds 1 to the bin of its
 // value key k (vkey), clamped to [lo, hi]: bins[k - lo] (bin 0 takes the
@@ -225,9 +260,10 @@ __device__ __forceinline__ void visit_row(const char *rowp, bool bf16, int V, F 
 // with an element on a near-zero key or at or above `spec` has
 // special(v, x, k, t) called for each of those elements by the lane that
 // holds it (t = 0 on the near-zero keys), and so has every element of the
-// row tail.
+// row tail.  rs, p: as visit_row's.
 template <class Special>
-__device__ __forceinline__ void count_row_bf16(const char *rowp, int V, uint32_t *bins, uint32_t lo,
+__device__ __forceinline__ void count_row_bf16(const char *rowp, int V, __amdgpu_buffer_rsrc_t rs,
+                                               u32x4_t (&p)[kVB], uint32_t *bins, uint32_t lo,
                                                uint32_t hi, uint32_t spec, Special &&special) {
   const int tid = threadIdx.x;
   const int NG = V / 8;
@@ -237,7 +273,7 @@ __device__ __forceinline__ void count_row_bf16(const char *rowp, int V, uint32_t
     const uint32_t sgn = 0u - ((hw >> 15) & 1u);  // all ones for a negative value
     return (t ^ sgn) + 0x8000u;                    // 0x8000 + t, or 0x7FFF - t
   };
-  stream_chunks(rowp, NG, [&](const u32x4_t &w, int g) {
+  stream_chunks(rs, NG, p, [&](const u32x4_t &w, int g) {
     bool odd = false;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -275,14 +311,47 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, V = s.V, K = a.width;
   const int beam = r % a.nb;
   uint64_t *keys_out = a.row_keys + (int64_t)r * K;
+  const char *rowp = s.logits + (int64_t)r * s.row_bytes;
+  const bool bf16 = s.dtype == 1;
+  const int mw = (V + 31) / 32;
+  const int epc = bf16 ? 8 : 4;
+  const int NGs = V / epc;
+  const int32_t *h = s.hist + (int64_t)r * s.hist_stride;
+  // Asked for before the row's lengths arrive: the first history ids and
+  // the static masks' first words, four per lane, then the row's first
+  // batch of chunks (its first chunk per lane is the sample below; the sum
+  // pass starts on the batch), which stays in flight while the masks are
+  // built (the barriers up to the sample order LDS alone).
+  // (through buffer resources, which read 0 past their end, so that no
+  // branch splits the loads: an absent mask is a resource of length 0)
+  auto rsrc = [&](const void *q, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(q ? q : (const void *)s.lens), (short)0,
+                                             q ? bytes : 0, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t hrs = rsrc(s.hist_stride > 0 ? h : nullptr, 4 * s.hist_stride);
+  const __amdgpu_buffer_rsrc_t brs = rsrc(s.bad_mask, 4 * mw), srs = rsrc(s.sup_mask, 4 * mw);
+  int hv0[4];
+  uint32_t km0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + u * kBT;
+    hv0[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(hrs, 4 * i, 0, 0);
+    km0[u] = __builtin_amdgcn_raw_buffer_load_b32(brs, 4 * i, 0, 0) |
+             __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * i, 0, 0);
+  }
+  auto static_word = [&](int w) {
+    return __builtin_amdgcn_raw_buffer_load_b32(brs, 4 * w, 0, 0) |
+           __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * w, 0, 0);
+  };
+  const __amdgpu_buffer_rsrc_t rrs = chunk_rsrc(rowp, NGs);
+  u32x4_t b0[kVB];
+  load_batch(rrs, b0, 0);
   const int L = s.lens[r], P = s.lens[s.B + r], M = s.lens[2 * s.B + r];
+  const float s_beam = a.beam_scores[r];
   if ((a.first_step && beam > 0) || L <= 0) {  // no candidates
     for (int i = tid; i < K; i += kBT) keys_out[i] = 0ull;
     return;
   }
-  const char *rowp = s.logits + (int64_t)r * s.row_bytes;
-  const bool bf16 = s.dtype == 1;
-  const int mw = (V + 31) / 32;
   uint32_t *seen = bsm, *kill = bsm + mw;
   uint32_t *hist = bsm + ((2 * mw + 3) & ~3);
   uint64_t *cand = reinterpret_cast<uint64_t *>(hist + kBeamSelBins);
@@ -299,17 +368,10 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   int forced = -1;
   if (s.forced_bos >= 0 && L == 1) forced = s.forced_bos;
   if (s.forced_eos >= 0 && L == M - 1) forced = s.forced_eos;
-  const int32_t *h = s.hist + (int64_t)r * s.hist_stride;
   const int Lh = L < s.hist_stride ? L : s.hist_stride;  // (ids past the stride are not the row's)
-  const int epc = bf16 ? 8 : 4;
-  const int NGs = V / epc;
-  // every lane's first 16-byte chunk of the row (the sample below), in
-  // flight while the masks are built
-  uint4 c0 = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < NGs) c0 = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
   // ---- the processors' masks (LDS): seen ids; the static masks, n-gram and
   // minimum-length bans as removals (the removals start as the static
-  // masks; four words of each per lane are loaded at once) ----
+  // masks) ----
   for (int w0 = tid; w0 < mw; w0 += 4 * kBT) {
     uint32_t k[4];
 #pragma unroll
@@ -317,8 +379,7 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
       const int w = w0 + u * kBT;
       k[u] = 0u;
       if (w < mw) {
-        if (s.bad_mask) k[u] |= s.bad_mask[w];
-        if (s.sup_mask) k[u] |= s.sup_mask[w];
+        k[u] = w0 == tid ? km0[u] : static_word(w);
         if (begin_active) k[u] |= s.begin_mask[w];
       }
     }
@@ -335,9 +396,13 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
     keep_n = 0;
     xf_s = -INFINITY;
   }
-  __syncthreads();
+  lds_barrier();
   if (forced < 0) {
-    for (int i0 = tid; i0 < Lh; i0 += 4 * kBT) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (tid + u * kBT < Lh && hv0[u] >= 0 && hv0[u] < V)
+        atomicOr(&seen[hv0[u] >> 5], 1u << (hv0[u] & 31));
+    for (int i0 = tid + 4 * kBT; i0 < Lh; i0 += 4 * kBT) {
       int hv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) hv[u] = i0 + u * kBT < Lh ? h[i0 + u * kBT] : -1;
@@ -363,27 +428,30 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
       if (e >= 0 && e < V) atomicOr(&kill[e >> 5], 1u << (e & 31));
     }
   }
-  __syncthreads();
+  lds_barrier();
   bool forced_alive = forced >= 0 && forced < V;
   if (forced_alive && s.sup_mask && has_bit(s.sup_mask, forced)) forced_alive = false;
   if (forced_alive && begin_active && has_bit(s.begin_mask, forced)) forced_alive = false;
-  auto elem = [&](const uint4 &c, int j) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    return bf16 ? ((j & 1) ? __uint_as_float(w[j >> 1] & 0xFFFF0000u) : __uint_as_float(w[j >> 1] << 16))
-                : __uint_as_float(w[j]);
+  const u32x4_t c0 = b0[0];
+  auto elem = [&](const u32x4_t &c, int j) {
+    return bf16 ? ((j & 1) ? __uint_as_float(c[j >> 1] & 0xFFFF0000u) : __uint_as_float(c[j >> 1] << 16))
+                : __uint_as_float(c[j]);
   };
   // ---- from the sample, in one exchange: M0, the largest logit of the
   // first chunks and the row tail (the log-softmax's provisional shift),
   // and each wave's largest logit among its sample ids that are neither
   // removed nor seen ----
   float m0 = -INFINITY, me = -INFINITY;
-  if (tid < NGs)
+  if (tid < NGs) {
+    // (a lane's epc ids lie in one word of each mask)
+    const int w = (tid * epc) >> 5, b0 = (tid * epc) & 31;
+    const uint32_t out = (kill[w] | seen[w]) >> b0;
     for (int j = 0; j < epc; ++j) {
-      const int v = tid * epc + j;
       const float x = elem(c0, j);
       m0 = fmaxf(m0, x);
-      if (x > -INFINITY && !has_bit(kill, v) && !has_bit(seen, v)) me = fmaxf(me, x);
+      if (x > -INFINITY && !((out >> j) & 1u)) me = fmaxf(me, x);
     }
+  }
   for (int v = NGs * epc + tid; v < V; v += kBT)  // (the row tail)
     m0 = fmaxf(m0, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
                         : reinterpret_cast<const float *>(rowp)[v]);
@@ -394,7 +462,7 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
       wmax_s[1][tid / kWave] = we;
     }
   }
-  __syncthreads();
+  lds_barrier();
   float M0 = -INFINITY;
 #pragma unroll
   for (int q = 0; q < NW; ++q) M0 = fmaxf(M0, wmax_s[0][q]);
@@ -480,7 +548,7 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   if (vsum) {
     // the keys at or above kspec include every logit at or above xthr
     const uint32_t kspec = min(vkey_floor(xthr), khi);
-    count_row_bf16(rowp, V, vbl, klo - 1u, khi, kspec, [&](int v, float x, uint32_t k, uint32_t t) {
+    count_row_bf16(rowp, V, rrs, b0, vbl, klo - 1u, khi, kspec, [&](int v, float x, uint32_t k, uint32_t t) {
       if (t == 0u || k >= khi) {  // (not in a bin the sum reads)
         mloc = fmaxf(mloc, x);
         sum += term((double)x - dM0);
@@ -498,7 +566,7 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
       }
     }
   } else {
-    visit_row(rowp, bf16, V, [&](int v, float x) {  // (-inf adds 0)
+    visit_row(rowp, bf16, V, rrs, b0, [&](int v, float x) {  // (-inf adds 0)
       mloc = fmaxf(mloc, x);
       sum += term((double)x - dM0);
       keep(v, x);
@@ -515,7 +583,6 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   }
   const bool any = Mx > -INFINITY;
   const float lsf = any ? (float)log(S) : 0.0f;
-  const float s_beam = a.beam_scores[r];
   const uint32_t flat0 = (uint32_t)beam * (uint32_t)V;
   // A candidate's ordered score bits: plain_bits for an id neither removed
   // nor seen, true_bits for any id (the forced row, the removal, the
@@ -564,11 +631,71 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
     // and (a penalty below 1 raising them) the seen ids below the bound.
     const int nk = keep_n;
     const bool raise = s.rep < 1.0f;
-    keff = select_top(
-        K,
-        [&](auto &&f) {
-          for (int i = tid; i < nk; i += kBT) f(key_of(kid[i], true_bits(kid[i], kx[i])));
-          if (raise)
+    if (!raise && nk <= kBT / 4) {
+      // The list alone, a key a lane: a key's rank is the count of larger
+      // keys, counted by kBT / nk lanes, a share of the list each.
+      if (tid < nk) cand[tid] = key_of(kid[tid], true_bits(kid[tid], kx[tid]));
+      uint32_t *rk = hist;  // (the bins, read)
+      if (tid < nk) rk[tid] = 0u;
+      __syncthreads();
+      keff = nk < K ? nk : K;
+      if (nk > 0) {
+        const int parts = kBT / nk, j = tid % nk, part = tid / nk;
+        if (part < parts) {
+          const int q0 = part * nk / parts, q1 = (part + 1) * nk / parts;
+          const uint64_t kj = cand[j];
+          uint32_t c = 0u;
+          for (int q = q0; q < q1; ++q) c += cand[q] > kj ? 1u : 0u;
+          if (c) atomicAdd(&rk[j], c);
+        }
+        __syncthreads();
+        if (tid < nk && rk[tid] < (uint32_t)keff) emit_row((int)rk[tid], cand[tid]);
+      }
+    } else if (!raise && K <= NW && nk <= 2 * kBT) {
+      // The list alone, at most two keys a lane: each wave's K best by K
+      // rounds of the wave's maximum (taken out of the lane that holds it),
+      // then wave 0 takes the best K of the waves' the same way.
+      const int wid = tid / kWave;
+      uint64_t k0 = 0ull, k1 = 0ull, best = 0ull;  // best: on lane i, the wave's i-th
+      if (tid < nk) k0 = key_of(kid[tid], true_bits(kid[tid], kx[tid]));
+      if (tid + kBT < nk) k1 = key_of(kid[tid + kBT], true_bits(kid[tid + kBT], kx[tid + kBT]));
+      for (int i = 0; i < K; ++i) {
+        const uint64_t m = wave_max_u64_uni(k0 > k1 ? k0 : k1);
+        if (m == 0ull) break;
+        if (lane == i) best = m;
+        if (k0 == m) k0 = 0ull;
+        else if (k1 == m) k1 = 0ull;
+      }
+      if (lane < K) cand[wid * K + lane] = best;
+      __syncthreads();
+      keff = nk < K ? nk : K;
+      if (wid == 0) {
+        uint64_t c[NW * 16 / kWave];  // (NW * K <= 256 keys, four a lane)
+#pragma unroll
+        for (int u = 0; u < NW * 16 / kWave; ++u)
+          c[u] = lane + u * kWave < NW * K ? cand[lane + u * kWave] : 0ull;
+        uint64_t top = 0ull;
+        for (int i = 0; i < keff; ++i) {
+          uint64_t mine = 0ull;
+#pragma unroll
+          for (int u = 0; u < NW * 16 / kWave; ++u) mine = c[u] > mine ? c[u] : mine;
+          const uint64_t m = wave_max_u64_uni(mine);
+          if (lane == i) top = m;
+#pragma unroll
+          for (int u = 0; u < NW * 16 / kWave; ++u)
+            if (c[u] == m) c[u] = 0ull;
+        }
+        if (lane < keff) emit_row(lane, top);
+      }
+    } else if (!raise) {  // the list alone, ranked on chip
+      keff = select_top(
+          K, [&](auto &&f) { for (int i = tid; i < nk; i += kBT) f(key_of(kid[i], true_bits(kid[i], kx[i]))); },
+          emit_row, hist, cand, ss, true);
+    } else {  // and the seen ids below the bound, which the penalty raises
+      keff = select_top(
+          K,
+          [&](auto &&f) {
+            for (int i = tid; i < nk; i += kBT) f(key_of(kid[i], true_bits(kid[i], kx[i])));
             for (int w = tid; w < mw; w += kBT) {
               uint32_t bits = seen[w] & ~kill[w];
               while (bits) {
@@ -580,8 +707,9 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
                 if (!(x >= xthr)) f(key_of(v, true_bits(v, x)));
               }
             }
-        },
-        emit_row, hist, cand, ss, true);
+          },
+          emit_row, hist, cand, ss, true);
+    }
   } else {
     // A lower bound of the row's K-th key: the K-th largest key of a sample,
     // every lane's first 16-byte chunk.  Only keys at or above it can be
@@ -592,13 +720,11 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
     const int ns = select_top(
         K,
         [&](auto &&f) {
-          if (tid < NGs) {
-            const uint4 c = *reinterpret_cast<const uint4 *>(rowp + (int64_t)tid * 16);
+          if (tid < NGs)
             for (int j = 0; j < epc; ++j) {
               const int v = tid * epc + j;
-              f(key_of(v, true_bits(v, elem(c, j))));
+              f(key_of(v, true_bits(v, elem(c0, j))));
             }
-          }
         },
         [&](int rank, uint64_t k) {
           if (rank == K - 1) t0_s = k;
@@ -674,6 +800,35 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_merge(BeamArgs a) {
   }
 }
 
+// k_beam_merge for a prompt whose num_beams * K row keys fit one wave, a key
+// a lane: each key's rank is the count of larger keys, read lane by lane.
+__global__ __launch_bounds__(kWave) void k_beam_merge_wave(BeamArgs a) {
+  const int p = blockIdx.x, lane = threadIdx.x, V = a.s.V, K = a.width;
+  const int n = a.nb * K;
+  const uint64_t k = lane < n ? a.row_keys[(int64_t)p * n + lane] : 0ull;
+  int rank = 0;
+  for (int q = 0; q < kWave; ++q) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, q);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), q);
+    rank += (((uint64_t)hi << 32) | lo) > k ? 1 : 0;
+  }
+  const int present = __popcll(__ballot(k != 0ull));
+  const int keff = present < K ? present : K;
+  float *sc = a.out_scores + (int64_t)p * K;
+  int32_t *bm = a.out_beams + (int64_t)p * K, *tk = a.out_tokens + (int64_t)p * K;
+  if (k != 0ull && rank < keff) {
+    const uint32_t e = 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu);
+    sc[rank] = unordered32((uint32_t)(k >> 32));
+    bm[rank] = (int32_t)(e / (uint32_t)V);
+    tk[rank] = (int32_t)(e % (uint32_t)V);
+  }
+  if (lane >= keff && lane < K) {  // fewer candidates than slots
+    sc[lane] = -INFINITY;
+    bm[lane] = -1;
+    tk[lane] = -1;
+  }
+}
+
 size_t beam_rows_lds(int32_t V) {
   const size_t mw = ((size_t)V + 31) / 32;
   // masks, radix bins, the select's keys, the sum pass's kept ids and logits
@@ -696,7 +851,10 @@ hipError_t launch_beam(const BeamArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(k_beam_rows, dim3(a.s.B), dim3(kBT), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_beam_merge, dim3(a.s.B / a.nb), dim3(kBT), mlds, st, a);
+  if ((int64_t)a.nb * a.width <= kWave)
+    hipLaunchKernelGGL(k_beam_merge_wave, dim3(a.s.B / a.nb), dim3(kWave), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_beam_merge, dim3(a.s.B / a.nb), dim3(kBT), mlds, st, a);
   return hipGetLastError();
 }
 
