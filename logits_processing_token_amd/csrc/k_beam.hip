@@ -18,19 +18,22 @@
 //    (K of its ids neither removed nor seen lie at or above it); one pass
 //    for the row's largest logit m and log(sum exp(x - m)) in binary64
 //    (exp_nonpos for the terms) that also keeps on chip the ids at or above
-//    the bound; then the row's best K keys among those, rescored.  When the
-//    bound fails (too many kept, a sample smaller than K, or rounding that
-//    could tie a left-out id with the sample's K-th), the best K come from a
-//    second pass over the row, bounded by the sample's K-th key.  Nothing of
-//    size V is written.
+//    the bound; then the row's best K keys among those, rescored.  A bf16
+//    row's pass counts each logit into a bin per bf16 value and takes one
+//    exponential per bin.  When the bound fails (too many kept, a sample
+//    smaller than K, or rounding that could tie a left-out id with the
+//    sample's K-th), the best K come from a second pass over the row,
+//    bounded by the sample's K-th key.  Nothing of size V is written.
 //  * k_beam_merge, one workgroup per prompt: the best K of its num_beams * K
 //    row keys, written as score, beam and id (k_beam_merge_wave, one wave,
 //    when those keys number at most 64).
 //
-// Both select with the same routine: a radix select over the keys, 12 bits
-// then 13 at a time from the top, stopping as soon as the keys at or above
-// the current prefix number at most kSelCap; those are gathered into LDS and
-// each one's rank is the count of larger keys among them.
+// The selections: a short kept list (at most a quarter of the workgroup's
+// lanes) is ranked on chip, each key's rank the count of larger keys; for
+// K up to the number of waves, a longer one by rounds of wave maxima; any
+// other set by a radix select over the keys, 12 bits then 13 at a time from
+// the top, stopping as soon as the keys at or above the current prefix
+// number at most kSelCap, which are then ranked on chip.
 
 #include <hip/hip_runtime.h>
 #include <float.h>

@@ -221,6 +221,28 @@ def test_beam_scores_clamp_at_the_smallest_finite_value():
     assert (g2["beams"][1, 9:] == 5).all() and (g2["scores"][1, 9:] > -FMAX).all()
 
 
+@pytest.mark.parametrize("dtype,shift", [("bf16", 3.0), ("f32", 2.0)])
+def test_beam_long_kept_list(dtype, shift):
+    """Rows whose sample (every lane's first 16-byte chunk) lies below the
+    rest, so that the sample's bound keeps several hundred to a couple of
+    thousand ids: the kept list is longer than a quarter of the workgroup
+    and goes through the rounds of wave maxima; penalties above 1 and
+    removed ids among them."""
+    V = 32000
+    w = _workload(2600 + int(shift), 4, 4, V, dtype,
+                  dict(eos_token_ids=[2], repetition_penalty=1.2, bad_words_ids=[7, 9000]),
+                  hist_len=40, hot_hist=False)
+    x = w["x"]
+    n_sample = 1024 * (8 if dtype == "bf16" else 4)
+    if dtype == "bf16":
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+        xf[:, :n_sample] -= shift
+        w["x"] = synth.bf16_bits(xf)
+    else:
+        x[:, :n_sample] -= shift
+    _check(w)
+
+
 def test_beam_large_vocab():
     """The 151,936-id bf16 vocabulary, 8 prompts x 4 beams, with the penalty
     and an n-gram ban on histories of 256 ids."""
