@@ -153,7 +153,7 @@ PROFILED = {
     "C5": (("k_topk",), "k_topk_c5_traffic.txt", SELECT_COMMON + (CSRC + "k_full.hip",)),
     "F1": (("k_vres",), "k_vres_logprob_c3_traffic.txt",
            SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp")),
-    "F2": (("k_beam_rows", "k_beam_merge"), "k_beam_c3_traffic.txt", COMMON + (CSRC + "k_beam.hip",)),
+    "F2": (("k_beam_rows", "k_beam_merge_wave"), "k_beam_c3_traffic.txt", COMMON + (CSRC + "k_beam.hip",)),
     "F3": (("k_full", "k_vsel_expand", "k_vsel_match"), "k_vsel_c4_traffic.txt",
            SELECT_COMMON + (CSRC + "k_full.hip", CSRC + "k_vsel.hip")),
 }
