@@ -94,7 +94,7 @@ __device__ __forceinline__ float value_hist_pass(const SelectArgs &a, int row, c
   const uint32_t khi = klo + (uint32_t)(kVBins - 1);  // keys from here: one by one
   uint32_t *vbl = vb + (lane & 1) * kVStride;
   float lmx = -INFINITY;
-  uint32_t kmx = 0u;
+  uint32_t kmx = 0u;  // the largest key of the row's elements (of this lane)
   // An element that a value bin does not stand for (few per row: near-zero
   // scores, keys past the bins, scores penalized in the stream): one by one
   // into the mass histogram, appended when kept.
@@ -115,53 +115,57 @@ __device__ __forceinline__ float value_hist_pass(const SelectArgs &a, int row, c
     }
   };
   // One chunk (every lane of the wave calls; `real`: the chunk is in the
-  // row): every element adds 1 to its value bin (elements a value bin does
-  // not stand for, and chunks past the row, add to spare words past the
-  // bins); the kept ones are appended as raw score and id at slots that one
-  // add per wave reserves (a wave scan of the lanes' counts places them).
+  // row).  Killed elements become -inf, below every bin.  Every element adds
+  // 1 to the bin of its value key clamped to the bins: keys below klo to bin
+  // 0 (no mass), keys from khi on to a spare word past the bins, the two
+  // near-zero keys to their own words, which the conversion skips.  The
+  // elements a value bin does not stand for (near-zero, past the bins,
+  // penalized in the stream) go one by one, a penalized one first taking its
+  // count back.  Returns the elements to keep by value (bit j for element
+  // j).  (Chunks past the row read as +0: near-zero, and not real.)
   const uint8_t *kbyte = reinterpret_cast<const uint8_t *>(s.kmask);
   const uint8_t *sbyte = reinterpret_cast<const uint8_t *>(s.smask);
-  auto chunk = [&](int g, uint4 cw, uint32_t kb, uint32_t sb, bool real) {
+  const uint32_t klo1 = klo - 1u, ninf = 0xFF80FF80u;
+  auto bin_word = [&](uint32_t k) { return &vbl[min(max(k, klo1), khi) - klo1]; };
+  auto chunk = [&](int g, uint4 cw, uint32_t kb, uint32_t sb, bool real) -> uint32_t {
+    cw = vkill(cw, kb, ninf);
     const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-    uint32_t slow = 0u, kept = 0u;
+    uint32_t slow = 0u, kept = 0u, kc = 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t raw = ((kb >> j) & 1u) ? 0xFF80u : (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      const uint32_t k = vkey(raw);
-      const bool by_value = !((sb >> j) & 1u) && k != kKeyZoneNeg && k != kKeyZonePos && k < khi;
-      kmx = max(kmx, by_value && real ? k : 0u);
-      atomicAdd(&vbl[!real ? (uint32_t)kVBins + 1u
-                           : by_value ? (k >= klo ? k - klo + 1u : 0u) : (uint32_t)kVBins],
-                1u);
-      slow |= real && !by_value ? 1u << j : 0u;
-      kept |= real && by_value && k >= kkeep ? 1u << j : 0u;
+      uint32_t t;
+      const uint32_t k = vkey_t((j & 1) ? w[j >> 1] >> 16 : w[j >> 1], t);
+      atomicAdd(bin_word(k), 1u);
+      slow |= (t == 0u || k >= khi) ? 1u << j : 0u;
+      kept |= k >= kkeep ? 1u << j : 0u;
+      kc = max(kc, k);
     }
+    if (sb) {  // (the penalized elements' raw keys do not count)
+      kc = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t t;
+        const uint32_t k = vkey_t((j & 1) ? w[j >> 1] >> 16 : w[j >> 1], t);
+        kc = ((sb >> j) & 1u) ? kc : max(kc, k);
+      }
+    }
+    kmx = real ? max(kmx, kc) : kmx;
+    slow = real ? slow | sb : 0u;
+    kept = real ? kept & ~slow : 0u;
     if (slow) {
 #pragma unroll 1
       for (uint32_t m = slow; m; m &= m - 1u) {
         const int j = __ffs(m) - 1;
-        const uint32_t raw = ((kb >> j) & 1u) ? 0xFF80u : (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        one_by_one(g * 8 + j, raw, (sb >> j) & 1u);
-      }
-    }
-    if (keep) {
-      const int n = __popc(kept);
-      const int incl = wave_incl_scan_i32(n);
-      const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
-      if (tot > 0) {
-        int first = 0;
-        if (lane == kWave - 1) first = atomicAdd(&sh.n_coll, tot);
-        int o = __builtin_amdgcn_readlane(first, kWave - 1) + incl - n;
-#pragma unroll 1
-        for (uint32_t m = kept; m; m &= m - 1u, ++o) {
-          const int j = __ffs(m) - 1;
-          if (o < a.ccap) {
-            ckey[o] = ((uint64_t)((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 32) | (uint32_t)(g * 8 + j);
-            cval[o] = -1.0f;
-          }
+        const uint32_t raw = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        const bool pen = (sb >> j) & 1u;
+        if (pen) {
+          uint32_t t;
+          atomicSub(bin_word(vkey_t(raw, t)), 1u);
         }
+        one_by_one(g * 8 + j, raw, pen);
       }
     }
+    return kept;
   };
   // The stream: batches of U chunks through a buffer resource (a read past
   // the row returns 0 and touches no memory, so every load is issued by every
@@ -177,16 +181,46 @@ __device__ __forceinline__ float value_hist_pass(const SelectArgs &a, int row, c
   };
   uint32_t kb_n = tid < NG ? kbyte[tid] : 0u;
   uint32_t sb_n = dense_pen && tid < NG ? sbyte[tid] : 0u;
+  // A batch's kept elements are appended as raw score and id at slots that
+  // one add per wave and batch reserves (a wave scan of the lanes' counts
+  // places them).
   auto batch = [&](int i, const uint4 *cw) {  // batch i: chunks tid + (i U + u) NT
+    uint32_t km[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = tid + (i * U + u) * NT;
+      km[u] = 0u;
       if (__ballot(g < NG) == 0ull) continue;  // (past the row for the whole wave)
       const uint32_t kb = kb_n, sb = sb_n;
       const int gn = min(g + NT, NG - 1);
       kb_n = kbyte[gn];
       sb_n = dense_pen ? sbyte[gn] : 0u;
-      chunk(g, cw[u], kb, sb, g < NG);
+      km[u] = chunk(g, cw[u], kb, sb, g < NG);
+    }
+    if (keep) {
+      int n = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) n += __popc(km[u]);
+      const int incl = wave_incl_scan_i32(n);
+      const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+      if (tot > 0) {
+        int first = 0;
+        if (lane == kWave - 1) first = atomicAdd(&sh.n_coll, tot);
+        int o = __builtin_amdgcn_readlane(first, kWave - 1) + incl - n;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int g = tid + (i * U + u) * NT;
+          const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+#pragma unroll 1
+          for (uint32_t m = km[u]; m; m &= m - 1u, ++o) {
+            const int j = __ffs(m) - 1;
+            if (o < a.ccap) {
+              ckey[o] = ((uint64_t)((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 32) | (uint32_t)(g * 8 + j);
+              cval[o] = -1.0f;
+            }
+          }
+        }
+      }
     }
   };
   const int nbat = (NG + NT * U - 1) / (NT * U);
@@ -218,11 +252,13 @@ __device__ __forceinline__ float value_hist_pass(const SelectArgs &a, int row, c
     }
   }
   __syncthreads();
-  // value bins -> mass histogram (bin 0: below klo, nothing)
+  // value bins -> mass histogram (bin 0: below klo, nothing; the near-zero
+  // keys' words: elements counted one by one)
   for (int b = 1 + tid; b < kVBins; b += NT) {
     const uint32_t n = vb[b] + vb[kVStride + b];
-    if (n == 0u) continue;
-    const uint32_t bits = __float_as_uint(mass_of<TOPK>(final_y(vkey_value(klo + (uint32_t)b - 1u)), t_y, c));
+    const uint32_t kb = klo + (uint32_t)b - 1u;
+    if (n == 0u || kb == kKeyZoneNeg || kb == kKeyZonePos) continue;
+    const uint32_t bits = __float_as_uint(mass_of<TOPK>(final_y(vkey_value(kb)), t_y, c));
     atomicAdd(&hist[mass_bin(bits, shift, base, nb)],
               (uint64_t)n * ((1ull << 40) | (bits & lowmask)));
   }
@@ -238,8 +274,11 @@ __device__ __forceinline__ float value_hist_pass(const SelectArgs &a, int row, c
       }
     }
   }
-  const float vmx = kmx >= kKeyLowFinite ? final_y(vkey_value(kmx)) : -INFINITY;
-  return fmaxf(lmx, vmx);
+  // The largest key stands for its value unless it is a near-zero key: then
+  // every element of the lane lies at or below that key's range, and those
+  // in it went one by one.
+  const bool kval = kmx >= kKeyLowFinite && kmx != kKeyZoneNeg && kmx != kKeyZonePos;
+  return fmaxf(lmx, kval ? final_y(vkey_value(kmx)) : -INFINITY);
 }
 
 // ---------------------------------------------------------------------------

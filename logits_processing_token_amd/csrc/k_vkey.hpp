@@ -1,6 +1,6 @@
 // k_vkey.hpp -- 16-bit value keys of bf16 scores, shared by the kernels that
 // count a bf16 row into one histogram bin per value (k_vres, and the streamed
-// histogram pass of k_full).
+// histogram pass of k_full), and the removal of killed elements from a chunk.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,11 +30,37 @@ __device__ __forceinline__ float vkey_value(uint32_t k) {
                                      : 0x8000u | (kKeyZoneNeg - k + kZoneMag);
   return __uint_as_float(u << 16);
 }
+// vkey without a select: the pattern in the low 16 bits of hw (the bits
+// above are ignored); t: the clamped magnitude (0 on the near-zero keys).
+__device__ __forceinline__ uint32_t vkey_t(uint32_t hw, uint32_t &t) {
+  const uint32_t m = hw & 0x7FFFu;
+  t = m > kZoneMag ? m - kZoneMag : 0u;
+  return (t ^ (0u - ((hw >> 15) & 1u))) + 0x8000u;  // 0x8000 + t, or 0x7FFF - t
+}
 // Key of the largest bf16 value not above y (y not NaN; -0 counts as +0).
 __device__ __forceinline__ uint32_t vkey_floor(float y) {
   uint32_t u = __float_as_uint(y + 0.0f);
   if ((u & 0x80000000u) && (u & 0xFFFFu)) u += 0x10000u;  // negative: away from zero
   return vkey(u >> 16);
+}
+
+// Removed elements of a chunk (kill bit j for element j) become -inf: for
+// word q, bits 2q and 2q + 1 are shifted to the sign bit of each half and
+// spread over it (two packed shifts, written out so that the compiler keeps
+// them rather than a compare and select per half).
+__device__ __forceinline__ uint4 vkill(uint4 c, uint32_t kb, uint32_t ninf) {
+  const uint32_t kbp = (kb & 0xFFu) | ((kb & 0xFEu) << 15);  // bits 2q | bits 2q + 1 << 16
+  uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m;
+    asm("v_pk_lshlrev_b16 %0, %1, %2 op_sel_hi:[0,1]\n\t"
+        "v_pk_ashrrev_i16 %0, 15, %0 op_sel_hi:[0,1]"
+        : "=&v"(m)
+        : "n"(15 - 2 * q), "v"(kbp));
+    w[q] = (m & ninf) | (~m & w[q]);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 }  // namespace tsel

@@ -105,25 +105,6 @@ __device__ __forceinline__ uint32_t vaddr2(uint32_t w, u16x2 t, const VMapP &m) 
   return a;
 }
 
-// Removed elements of a chunk (kill bit j for element j) become -inf: for
-// word q, bits 2q and 2q + 1 are shifted to the sign bit of each half and
-// spread over it (two packed shifts, written out so that the compiler keeps
-// them rather than a compare and select per half).
-__device__ __forceinline__ uint4 vkill(uint4 c, uint32_t kb, uint32_t ninf) {
-  const uint32_t kbp = (kb & 0xFFu) | ((kb & 0xFEu) << 15);  // bits 2q | bits 2q + 1 << 16
-  uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t m;
-    asm("v_pk_lshlrev_b16 %0, %1, %2 op_sel_hi:[0,1]\n\t"
-        "v_pk_ashrrev_i16 %0, 15, %0 op_sel_hi:[0,1]"
-        : "=&v"(m)
-        : "n"(15 - 2 * q), "v"(kbp));
-    w[q] = (m & ninf) | (~m & w[q]);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // A constant in a scalar register (a literal cannot be an operand of the
 // three-operand bit operations).
 __device__ __forceinline__ uint32_t sconst(uint32_t v) {
