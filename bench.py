@@ -145,17 +145,20 @@ PROFILED = {
     "C1": (("k_greedy",), "k_greedy_c1_traffic.txt", SELECT_COMMON + (CSRC + "k_greedy.hip",)),
     "C1v": (("k_verify_part", "k_verify_merge"), "k_verify_c1_traffic.txt",
             COMMON + (CSRC + "k_verify.hip",)),
-    "C2": (("k_topk",), "k_topk_c2_traffic.txt", SELECT_COMMON + (CSRC + "k_full.hip",)),
+    "C2": (("k_topk",), "k_topk_c2_traffic.txt",
+           SELECT_COMMON + (CSRC + "k_full.hip", CSRC + "k_vkey.hpp")),
     "C3": (("k_vres",), "k_vres_b256_v128256_traffic.txt",
-           SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp")),
+           SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp", CSRC + "k_vkey.hpp")),
     "C4": (("k_verify_part", "k_verify_merge"), "k_verify_c4_traffic.txt",
            COMMON + (CSRC + "k_verify.hip",)),
-    "C5": (("k_topk",), "k_topk_c5_traffic.txt", SELECT_COMMON + (CSRC + "k_full.hip",)),
+    "C5": (("k_topk",), "k_topk_c5_traffic.txt",
+           SELECT_COMMON + (CSRC + "k_full.hip", CSRC + "k_vkey.hpp")),
     "F1": (("k_vres",), "k_vres_logprob_c3_traffic.txt",
-           SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp")),
-    "F2": (("k_beam_rows", "k_beam_merge_wave"), "k_beam_c3_traffic.txt", COMMON + (CSRC + "k_beam.hip",)),
+           SELECT_COMMON + (CSRC + "k_vres.hip", CSRC + "k_res_common.hpp", CSRC + "k_vkey.hpp")),
+    "F2": (("k_beam_rows", "k_beam_merge_wave"), "k_beam_c3_traffic.txt",
+           COMMON + (CSRC + "k_beam.hip", CSRC + "k_vkey.hpp")),
     "F3": (("k_full", "k_vsel_expand", "k_vsel_match"), "k_vsel_c4_traffic.txt",
-           SELECT_COMMON + (CSRC + "k_full.hip", CSRC + "k_vsel.hip")),
+           SELECT_COMMON + (CSRC + "k_full.hip", CSRC + "k_vsel.hip", CSRC + "k_vkey.hpp")),
 }
 
 
