@@ -333,6 +333,24 @@ def test_many_distinct_seen_ids():
     _assert_select(w)
 
 
+@pytest.mark.parametrize("rep", [1.4, 0.8])
+def test_many_distinct_seen_ids_streamed_bf16(rep):
+    """A bf16 row past the registers (V = 151936: the streamed full path,
+    which counts each score into a bin per bf16 value) with more distinct
+    history ids than the on-chip list holds: the stream penalizes them
+    itself, each penalized score first taking its value count back; with
+    removed ids, a temperature and top_p."""
+    B, V, H = 3, 151936, 12000
+    g = np.random.default_rng(5)
+    w = synth.random_select(13, B, V, H, dtype="bf16", sigma=3.0,
+                            settings=dict(repetition_penalty=rep, do_sample=True, top_p=0.9,
+                                          temperature=0.7, bad_words_ids=[5, 77, 150000],
+                                          suppress_tokens=[9]))
+    for b in range(B):
+        w.history[b] = g.permutation(V)[:H]
+    _assert_select(w)
+
+
 # ---------------------------------------------------------------------------
 # The named workloads.
 
