@@ -38,7 +38,7 @@ constexpr int kBinBelow = 50;
 constexpr int kBinAbove = 16;
 constexpr int kGatherCap = 256;           // elements of one mass sub-bin ordered on chip
 constexpr float kRefSlack = 2.0f;           // reference = first-chunk max + this (nats)
-constexpr int kKeepBelow = 13;              // binades under the reference whose elements the
+constexpr int kKeepBelow = 11;              // binades under the reference whose elements the
                                             // streamed histogram pass keeps on chip
 
 // Value-bin resident kernel (bf16 rows): one bin per bf16 value.
