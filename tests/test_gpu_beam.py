@@ -101,6 +101,9 @@ def _workload(seed, P, nb, V, dtype, settings, hist_len=24, scale=2.0, hot_hist=
     ("f32", 32000, 4, [2]),
     ("bf16", 50272, 1, []),
     ("f32", 50272, 8, [5, 6, 7]),
+    ("bf16", 50257, 4, [3]),   # (a row tail past the 16-byte chunks)
+    ("f32", 50257, 2, []),
+    ("bf16", 7, 2, []),        # (a row shorter than one chunk)
 ])
 def test_beam_random(dtype, V, nb, eos):
     w = _workload(2000 + V + nb, 8, nb, V, dtype, dict(eos_token_ids=eos), hot_hist=False)
