@@ -648,7 +648,15 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
           const int q0 = part * nk / parts, q1 = (part + 1) * nk / parts;
           const uint64_t kj = cand[j];
           uint32_t c = 0u;
-          for (int q = q0; q < q1; ++q) c += cand[q] > kj ? 1u : 0u;
+          int q = q0;
+          for (; q + 8 <= q1; q += 8) {  // (eight reads in flight)
+            uint64_t t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) t[u] = cand[q + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c += t[u] > kj ? 1u : 0u;
+          }
+          for (; q < q1; ++q) c += cand[q] > kj ? 1u : 0u;
           if (c) atomicAdd(&rk[j], c);
         }
         __syncthreads();
