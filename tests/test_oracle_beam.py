@@ -9,9 +9,10 @@ and a score never goes below it; at the start only the first beam counts.
 Scores x = ln w with integer w make the log-softmax ln(w / sum(w)) up to a
 few binary32 roundings (5e-7 here).  (Because a candidate's score never goes
 below the smallest finite value, removing an id with that value or with
--inf gives the same candidate scores; the pins see the clamp.)  Equal scores go by flattened index
-(beam * V + id), the reading the survey fixes.  Each pin is shown to fail
-on a copy of the oracle with a planted mistake.
+-inf gives the same candidate scores; the pins see the clamp.)  Equal
+scores go by flattened index (beam * V + id), the plainest reading of the
+paragraph, which names no order among equal scores.  Each pin is shown to
+fail on a copy of the oracle with a planted mistake.
 """
 import os
 import shutil
