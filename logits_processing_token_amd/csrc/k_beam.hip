@@ -440,10 +440,10 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
     return bf16 ? ((j & 1) ? __uint_as_float(c[j >> 1] & 0xFFFF0000u) : __uint_as_float(c[j >> 1] << 16))
                 : __uint_as_float(c[j]);
   };
-  // ---- from the sample, in one exchange: M0, the largest logit of the
-  // first chunks and the row tail (the log-softmax's provisional shift),
-  // and each wave's largest logit among its sample ids that are neither
-  // removed nor seen ----
+  // ---- from the sample: M0, the largest logit of the first chunks and
+  // the row tail (the log-softmax's provisional shift), and the largest
+  // logit among the sample ids that are neither removed nor seen of each of
+  // NW groups of lanes ----
   float m0 = -INFINITY, me = -INFINITY;
   if (tid < NGs) {
     // (a lane's epc ids lie in one word of each mask)
@@ -458,12 +458,18 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   for (int v = NGs * epc + tid; v < V; v += kBT)  // (the row tail)
     m0 = fmaxf(m0, bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(rowp)[v] << 16)
                         : reinterpret_cast<const float *>(rowp)[v]);
+  float *lme = reinterpret_cast<float *>(cand);  // (free until the selection)
+  lme[tid] = me;
   {
-    const float wm = wave_max_f32_uni(m0), we = wave_max_f32_uni(me);
-    if (lane == 0) {
-      wmax_s[0][tid / kWave] = wm;
-      wmax_s[1][tid / kWave] = we;
-    }
+    const float wm = wave_max_f32_uni(m0);
+    if (lane == 0) wmax_s[0][tid / kWave] = wm;
+  }
+  lds_barrier();
+  {
+    // group w: the lanes t with t mod NW = w, whose chunks spread over the
+    // sample (so that ids in order of their logits do not crowd one group)
+    const float ge = wave_max_f32_uni(lme[tid / kWave + NW * lane]);
+    if (lane == 0) wmax_s[1][tid / kWave] = ge;
   }
   lds_barrier();
   float M0 = -INFINITY;
@@ -475,14 +481,14 @@ __global__ __launch_bounds__(kBT, 1) void k_beam_rows(BeamArgs a) {
   // enough that even its plain score is lower (checked once the log-softmax
   // is known) cannot be among the row's best K: the sum pass keeps the ids
   // at or above xf less a small slack, on chip.  For K up to the number of
-  // waves, xf is the K-th largest of the waves' maxima (each held by an id
-  // of its own wave); else the K-th largest of the sample itself. ----
+  // groups, xf is the K-th largest of the groups' maxima (each held by an id
+  // of its own group); else the K-th largest of the sample itself. ----
   bool bounded = false;
   float xthr = INFINITY, xf = -INFINITY;
   if (forced < 0) {
     if (K <= NW) {
       const float wv = lane < NW ? wmax_s[1][lane] : -INFINITY;
-      int rank = 0;  // (equal maxima ranked by wave)
+      int rank = 0;  // (equal maxima ranked by group)
 #pragma unroll
       for (int q = 0; q < NW; ++q) {
         const float o = wmax_s[1][q];

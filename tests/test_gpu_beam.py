@@ -246,6 +246,22 @@ def test_beam_long_kept_list(dtype, shift):
     _check(w)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_beam_logits_in_id_order(dtype):
+    """Rows whose logits fall as the id rises (as in vocabularies ordered by
+    frequency): the row's best ids all lie in the sample's first lanes."""
+    w = _workload(77, 4, 4, 32000, dtype,
+                  dict(eos_token_ids=[2], repetition_penalty=1.2, bad_words_ids=[1]),
+                  hist_len=30, hot_hist=False)
+    x = w["x"]
+    if dtype == "bf16":
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+        w["x"] = synth.bf16_bits(-np.sort(-xf, axis=1))
+    else:
+        w["x"] = np.ascontiguousarray(-np.sort(-x, axis=1))
+    _check(w)
+
+
 def test_beam_large_vocab():
     """The 151,936-id bf16 vocabulary, 8 prompts x 4 beams, with the penalty
     and an n-gram ban on histories of 256 ids."""
