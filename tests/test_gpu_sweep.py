@@ -4,7 +4,9 @@ history (repeats, planted n-grams), the processors of "Transmuter.Generation
 (transmuter v2.0.0)" in their module-doc order, and the warpers (greedy,
 temperature, top_k, top_p), and compares token ids and processed rows with
 the oracle as the named parity tests do.  Lengths are mixed too, so that the
-forced, begin-suppress and minimum-length rules fire on some rows."""
+forced, begin-suppress and minimum-length rules fire on some rows.  Beam
+steps and verification with selection get sweeps of their own, checked by
+their parity tests' helpers."""
 import os
 import sys
 
@@ -91,3 +93,31 @@ def _beam_case(seed):
 def test_beam_sweep(seed):
     from test_gpu_beam import _check
     _check(_beam_case(seed), first_step=seed % 5 == 0)
+
+
+def _verify_select_case(seed):
+    from test_gpu_verify_select import _workload
+    g = np.random.default_rng(9800 + seed)
+    V = int(g.choice([97, 4099, 32000, 151936]))
+    dtype = "bf16" if g.random() < 0.6 else "f32"
+    k = int(g.choice([1, 3, 8]))
+    s = {}
+    if g.random() < 0.7:
+        s["repetition_penalty"] = float(g.choice([1.3, 0.8, 1.1]))
+    if g.random() < 0.4:
+        s["no_repeat_ngram_size"] = int(g.choice([2, 3]))
+    if g.random() < 0.5:
+        s["suppress_tokens"] = [int(v) for v in g.choice(V, size=min(V, 5), replace=False)]
+    if g.random() < 0.7:
+        s["do_sample"] = True
+        s["temperature"] = float(g.choice([1.0, 0.7]))
+        s["top_k"] = int(g.choice([0, 0, 5, 64]))
+        s["top_p"] = float(g.choice([1.0, 0.9]))
+    return _workload(seed + 900, 3, k, V, dtype, s, hist_len=int(g.choice([8, 200])),
+                     p_match=float(g.choice([0.5, 0.9])))
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_verify_select_sweep(seed):
+    from test_gpu_verify_select import _check
+    _check(_verify_select_case(seed))
