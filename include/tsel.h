@@ -315,7 +315,7 @@ size_t tsel_verify_select_workspace_size(const tsel_params *params, int32_t k);
  * a batch that is not a multiple of num_beams, or NULL required pointers;
  * TSEL_ERR_WORKSPACE for a missing or small workspace; TSEL_ERR_UNSUPPORTED
  * for num_beams > 64, num_beams * V >= 2^32, or V beyond the on-chip masks
- * of this path (V > 409,600).
+ * and lists of this path (V > 344,064).
  */
 tsel_status tsel_beam_step(const void *logits, const int32_t *history, const int32_t *lens,
                            const tsel_params *params, int32_t num_beams,

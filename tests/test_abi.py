@@ -195,6 +195,10 @@ def test_beam_step_rejects_before_any_gpu_call():
     assert call(_params(batch=8, renormalize_logits=True), 4) == tsel.TSEL_ERR_INVALID_ARG
     assert call(_params(batch=8, output_logprobs=True), 4) == tsel.TSEL_ERR_INVALID_ARG
     assert call(_params(batch=8, vocab=409632, row_stride=409632), 4) == tsel.TSEL_ERR_UNSUPPORTED
+    # the largest vocabulary the beam rows' LDS holds, and one past it
+    assert call(_params(batch=8, vocab=344064, row_stride=344064), 4,
+                wsp=None, nbytes=0) == tsel.TSEL_ERR_WORKSPACE
+    assert call(_params(batch=8, vocab=344065, row_stride=344072), 4) == tsel.TSEL_ERR_UNSUPPORTED
     assert call(p, 4, logits=None) == tsel.TSEL_ERR_INVALID_ARG
     assert call(p, 4, wsp=None, nbytes=0) == tsel.TSEL_ERR_WORKSPACE
     assert call(p, 4, nbytes=need - 1) == tsel.TSEL_ERR_WORKSPACE

@@ -262,6 +262,18 @@ def test_beam_logits_in_id_order(dtype):
     _check(w)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_beam_largest_vocabulary(dtype):
+    """The largest vocabulary whose masks and lists the beam rows hold on
+    chip (V = 344064), with removals near its end."""
+    V = 344064
+    w = _workload(88, 1, 2, V, dtype,
+                  dict(eos_token_ids=[V - 1], repetition_penalty=1.1,
+                       bad_words_ids=[V - 2, 5], suppress_tokens=[V - 3]),
+                  hist_len=50, hot_hist=False)
+    _check(w)
+
+
 def test_beam_large_vocab():
     """The 151,936-id bf16 vocabulary, 8 prompts x 4 beams, with the penalty
     and an n-gram ban on histories of 256 ids."""
