@@ -314,12 +314,13 @@ __device__ __forceinline__ int full_core(const SelectArgs &a, int row, const Lds
   bool kept = false;  // the collect buffer holds every element of bins >= keep_bin
   for (int attempt = 0; attempt < 2; ++attempt) {
     const float c = ref * kLog2e;
-    const bool keep = VF && keep1 && attempt == 0;
+    const bool vpass = VF && attempt == 0 && a.vbins != 0;  // (the value bins fit on chip)
+    const bool keep = vpass && keep1;
     for (int i = tid; i < nb; i += NT) hist[i] = 0ull;
     if (tid == 0) sh.n_coll = 0;
     __syncthreads();
     float lmx = -INFINITY;
-    if (VF && attempt == 0) {
+    if (vpass) {
       uint32_t *vb = reinterpret_cast<uint32_t *>(s.area + 8 * (size_t)nb + 12 * (size_t)a.ccap +
                                                   12 * (size_t)kGatherCap);
       lmx = value_hist_pass<TOPK>(a, row, s, sh, t_y, c, keep, keep_bin, hist, ckey, cval, vb);

@@ -64,7 +64,7 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   // so that the value array stays 16-byte aligned
   size_t lcap = (size_t)std::min<int64_t>(std::max<int64_t>(p->hist_stride, 0), V) + 8;
   lcap = std::min<size_t>((lcap + 3) & ~size_t(3), kMaxList);
-  int32_t nb = 0, ccap = 0, mant = 0, tcap = 0;
+  int32_t nb = 0, ccap = 0, mant = 0, tcap = 0, vb = 0;
   size_t area = 0;
   if (kind == SelectKernel::kTopK) {
     tcap = 2048;
@@ -85,19 +85,24 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
       area = need();
     }
   } else if (kind == SelectKernel::kFull) {
-    mant = 6;
-    ccap = 4096;
-    // bf16 rows: two copies of the value bins of the streamed histogram pass
-    const size_t vbins = p->dtype == TSEL_BF16 ? 2 * 4 * (size_t)tsel::kVStride : 0;
-    auto need = [&]() {
-      nb = (tsel::kBinBelow + tsel::kBinAbove) << mant;
-      // collected (key, mass) pairs, then room to order one sub-bin
-      return 8 * (size_t)nb + 12 * (size_t)ccap + 12 * (size_t)tsel::kGatherCap + vbins;
-    };
-    area = need();
-    while ((mant > 3 || ccap > 256) && fixed + area + 8 * lcap > budget) {
-      if (mant > 3) --mant; else ccap /= 2;
+    // bf16 rows: two copies of the value bins of the streamed histogram pass,
+    // when they fit beside the rest (else that pass counts by mass)
+    for (int with = p->dtype == TSEL_BF16 ? 1 : 0; with >= 0; --with) {
+      mant = 6;
+      ccap = 4096;
+      const size_t vbins = with ? 2 * 4 * (size_t)tsel::kVStride : 0;
+      auto need = [&]() {
+        nb = (tsel::kBinBelow + tsel::kBinAbove) << mant;
+        // collected (key, mass) pairs, then room to order one sub-bin
+        return 8 * (size_t)nb + 12 * (size_t)ccap + 12 * (size_t)tsel::kGatherCap + vbins;
+      };
       area = need();
+      while ((mant > 3 || ccap > 256) && fixed + area + 8 * lcap > budget) {
+        if (mant > 3) --mant; else ccap /= 2;
+        area = need();
+      }
+      vb = with;
+      if (fixed + area + min_list <= budget) break;
     }
   }
   if (fixed + area + min_list > budget) return false;
@@ -109,6 +114,7 @@ bool plan_layout(const tsel_params *p, SelectKernel kind, tsel::SelectArgs *a,
   a->ccap = ccap;
   a->bin_mant = mant;
   a->tcap = tcap;
+  a->vbins = vb;
   a->off_smask = (uint32_t)mask_bytes;
   a->off_list_id = (uint32_t)base;
   a->off_list_val = (uint32_t)(base + 4 * lcap);
@@ -148,6 +154,7 @@ bool plan_vres(const tsel_params *p, int res, tsel::SelectArgs *a, size_t *lds_b
   a->ccap = 0;
   a->bin_mant = 0;
   a->tcap = 0;
+  a->vbins = 0;
   a->off_kmask = (uint32_t)off;
   off += kmask_bytes;
   a->off_smask = (uint32_t)off;

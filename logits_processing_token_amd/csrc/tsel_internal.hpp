@@ -91,6 +91,7 @@ struct SelectArgs {
   int32_t nb, ccap;         // full path: histogram bins, collect capacity
   int32_t bin_mant;         // full path: mantissa bits per bin
   int32_t tcap;             // top_k candidate capacity
+  int32_t vbins;            // full path, bf16: the value bins fit on chip (else count by mass)
   uint32_t off_smask, off_list_id, off_list_val, off_lut, off_rhist, off_area;
   uint32_t off_woff;        // resident path: list offset of each thread's mask words
   uint32_t off_kmask;       // kill mask (0 but on the value-bin path)

@@ -351,6 +351,17 @@ def test_many_distinct_seen_ids_streamed_bf16(rep):
     _assert_select(w)
 
 
+@pytest.mark.parametrize("settings", [
+    dict(do_sample=True, top_p=0.9, temperature=0.7, repetition_penalty=1.2),
+    dict(do_sample=True, top_k=50, top_p=0.95),
+])
+def test_largest_bf16_vocabulary_sampling(settings):
+    """bf16 rows of 524,288 ids, sampled: the full path's on-chip layout has
+    no room left for the value bins, so its histogram pass counts by mass."""
+    w = synth.random_select(21, 2, 524288, 300, dtype="bf16", sigma=3.0, settings=settings)
+    _assert_select(w)
+
+
 # ---------------------------------------------------------------------------
 # The named workloads.
 
